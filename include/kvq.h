@@ -1,0 +1,161 @@
+/*
+ * kvq.h — paged K8/V4 KV cache and long-context decode attention on MI355X (gfx950).
+ *
+ * Two calls make up the library: kvq_append (quantize new tokens' K/V into cache pages)
+ * and kvq_decode_attn (softmax(Q K^T * scale) V over the paged cache through a page table).
+ * The rest of this header is the byte format those calls share and small host-side helpers.
+ *
+ * Sources.  The KV dtype "rk8v4" (K stored in 8 bits, V in 4 bits) is the engine's
+ * --kv-dtype flag in the forum post "3090 单卡跑 Qwen3.8-27B：NInfer 上机实测（180K 上下文 /
+ * C2 并发 / 4bit KV）", section 一、部署, launch-flag table: it lets a 184,320-token pool serve
+ * two concurrent requests.  The same post and the blog page "標籤: vLLM" (section 重點說明,
+ * part 2 "C++/CUDA 層的 kernel fusion 與 KV cache 策略") describe a KV cache managed in
+ * segments of the context rather than one buffer, and a decode kernel tuned for one long
+ * request.  None of the pages fixes the scale granularity or rounding of rk8v4; this library
+ * defines it (below) and does not claim byte compatibility with any other engine.
+ *
+ * Conventions for every call:
+ *   - All array arguments are device pointers to memory the caller owns (e.g. torch tensors).
+ *     The library allocates nothing, keeps no state between calls, never synchronizes, and
+ *     enqueues its kernels on `stream` (a hipStream_t passed as void*; NULL = default stream).
+ *   - Calls are asynchronous and stream-ordered: kvq_append followed by kvq_decode_attn on
+ *     the same stream makes the appended tokens visible to the attention.
+ *   - Every scalar argument is validated on the host before any HIP call; a bad argument
+ *     returns a negative KVQ_ERR_* code and enqueues nothing.  Contents of device arrays
+ *     (slot numbers, page ids, sequence lengths) cannot be checked on the host; how the
+ *     kernels treat out-of-range values is stated per call.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes ---------------------------------------------------------------------- */
+#define KVQ_OK               0
+#define KVQ_ERR_ARG         (-1)  /* NULL pointer where one is required, or a size <= 0 / inconsistent */
+#define KVQ_ERR_UNSUPPORTED (-2)  /* head_dim, page_size or rows-per-KV-head outside what is built   */
+#define KVQ_ERR_WORKSPACE   (-3)  /* workspace NULL or smaller than kvq_decode_workspace_bytes()      */
+#define KVQ_ERR_HIP         (-4)  /* a HIP launch reported an error (hipGetLastError)                 */
+
+/* ---- supported shapes ------------------------------------------------------------------ */
+/* head_dim D in {64, 128, 256}; page_size P a power of two in [16, 256];
+ * rows per KV head (GQA group size G = n_q_heads / num_kv_heads, times n_rows) <= 32;
+ * n_rows (query rows per sequence: 1 for plain decode, 1 + drafts for an MTP verify step) in [1, 4]. */
+#define KVQ_TILE_TOKENS     16
+#define KVQ_MAX_ROWS_PER_KV 32
+#define KVQ_MAX_N_ROWS      4
+
+/* ---- quantization (defined by this library; the pages give only "K8/V4") ---------------
+ * Per token and KV head, with inputs in fp32:
+ *   K row (D values):  a = max_d |k_d|;  s = fp16_rne(a / 127.0f)   (IEEE fp32 divide, then
+ *                      round-to-nearest-even to fp16, saturating at 65504);
+ *                      code_d = clamp(rint_half_even(k_d / (float)s), -127, 127) as int8
+ *                      (fp32 IEEE divide); if s == 0 every code is 0.
+ *   V row: the same per group of 32 contiguous dims with 7 in place of 127, codes in [-7, 7]
+ *          stored as 4-bit two's complement; one fp16 scale per group (D/32 per token).
+ *   Dequantized values are code * scale (exact in fp32).  Non-finite inputs are undefined.
+ *
+ * ---- page format ----------------------------------------------------------------------
+ * The pool is num_pages pages; page p holds num_kv_heads blocks.  The block of (page p,
+ * KV head h) starts at byte (p * num_kv_heads + h) * kvq_block_bytes(P, D) and holds the
+ * P token slots of that page for that head in four sections:
+ *
+ *   K codes   P*D bytes     at 0
+ *   K scales  P fp16        at P*D
+ *   V codes   P*D/2 bytes   at P*D + 2*P
+ *   V scales  P*D/32 fp16   at P*D + 2*P + P*D/2
+ *
+ * so block_bytes = P * (D + 2 + D/2 + D/16): 25,728 B for P=64, D=256.
+ * Slots are grouped in tiles of 16 (slot s -> tile s/16, t = s%16).  Within a tile the codes
+ * are laid out so that one 16-byte load per lane of a 64-lane wave delivers matrix-core
+ * operands directly (see kvq_decode_attn):
+ *
+ *   K code (t, d):  byte  16*D*tile + 256*(d/16) + 16*t + d%16            (int8)
+ *   K scale (s):    fp16 index s
+ *   V code (t, d):  with j = d/32 (scale group), lane = 16*(t/4) + d%16, r = t%4,
+ *                   w = min(D/32, 4):
+ *                   byte  8*D*tile + 256*w*(j/w) + 4*w*lane + 4*(j%w) + r,
+ *                   low nibble if (d/16) is even, high nibble if odd  (4-bit two's complement)
+ *   V scale (s, j): fp16 index s*(D/32) + j
+ *
+ * Every byte of a token's codes belongs to that token alone, so appends of different
+ * tokens never write the same byte.
+ */
+size_t kvq_block_bytes(int32_t page_size, int32_t head_dim);
+
+/* ---- kvq_append ------------------------------------------------------------------------
+ * Quantizes n_tok new tokens and writes each into its cache slot.
+ *   pool          device, num_pages * num_kv_heads * kvq_block_bytes(page_size, head_dim) bytes,
+ *                 16-byte aligned; written in place (only the bytes of the target slots).
+ *   k, v          device fp32 [n_tok][num_kv_heads][head_dim], contiguous.
+ *   slot_mapping  device int32 [n_tok]; slot = page * page_size + offset.  A slot < 0 or
+ *                 >= num_pages * page_size is skipped (no write), so -1 can mark padding.
+ *                 Two tokens with the same slot in one call race; the result is undefined.
+ *   n_tok         >= 0 (0 enqueues nothing and returns KVQ_OK).
+ * Returns KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED or KVQ_ERR_HIP.
+ */
+int kvq_append(void* pool, int32_t num_pages, int32_t page_size, int32_t num_kv_heads,
+               int32_t head_dim, const float* k, const float* v, const int32_t* slot_mapping,
+               int32_t n_tok, void* stream);
+
+/* ---- kvq_decode_attn -------------------------------------------------------------------
+ * For each sequence b, query row i (0..n_rows-1) and query head hq, with KV head
+ * h = hq / (n_q_heads / num_kv_heads) (contiguous GQA groups) and L = seq_lens[b]:
+ *   z_t = softmax_scale * sum_d q[b][i][hq][d] * K^[t][d]         for t = 0 .. L - n_rows + i
+ *   out[b][i][hq][:] = sum_t softmax(z)_t * V^[t][:],   lse[b][i][hq] = ln sum_t exp(z_t)
+ * where K^, V^ are the dequantized cache entries of logical token t of sequence b, found at
+ * page page_table[b][t / page_size], slot t % page_size.  n_rows > 1 is an MTP verify step:
+ * row i sees the cache up to and including the i-th of the last n_rows tokens (causal mask),
+ * so the last row sees all L tokens.  (Multi-token-prediction with 3 draft tokens is the
+ * engine's --spec mtp --draft-tokens 3 in the forum post's launch-flag table.)
+ *
+ *   pool, num_pages, page_size, num_kv_heads, head_dim   as for kvq_append (read only).
+ *   q             device fp16 bits [n_seq][n_rows][n_q_heads][head_dim].
+ *   page_table    device int32 [n_seq][max_pages_per_seq], logical -> physical page.  Only the
+ *                 first ceil(L / page_size) entries of a row are read; an entry outside
+ *                 [0, num_pages) is clamped into range (wrong values, never a fault).
+ *   seq_lens      device int32 [n_seq]: tokens seen by the last row.  Must satisfy
+ *                 n_rows <= L <= max_seq_len; tokens beyond max_seq_len are not attended, and a
+ *                 row that sees no token gets out = 0 and lse = -inf.
+ *   max_seq_len   host-side upper bound on seq_lens; sizes the grid and the workspace.
+ *   softmax_scale <= 0 selects 1/sqrt(head_dim).
+ *   num_splits    0 = choose automatically (kvq_decode_num_splits); otherwise the number of
+ *                 pieces each (sequence, KV head) context is cut into, clamped to the number of
+ *                 32-token blocks.  The result does not depend on it beyond fp32 rounding.
+ *   out           device fp32 [n_seq][n_rows][n_q_heads][head_dim].
+ *   lse           device fp32 [n_seq][n_rows][n_q_heads], or NULL.
+ *   workspace     device scratch of at least kvq_decode_workspace_bytes(...) bytes, 16-byte
+ *                 aligned; contents on entry are ignored, on exit unspecified.  Two calls in
+ *                 flight at once must not share it.
+ * Returns KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE or KVQ_ERR_HIP.
+ */
+int kvq_decode_attn(const void* pool, int32_t num_pages, int32_t page_size,
+                    int32_t num_kv_heads, int32_t head_dim, const uint16_t* q,
+                    const int32_t* page_table, const int32_t* seq_lens, int32_t n_seq,
+                    int32_t n_rows, int32_t n_q_heads, int32_t max_pages_per_seq,
+                    int32_t max_seq_len, float softmax_scale, int32_t num_splits, float* out,
+                    float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Number of context pieces kvq_decode_attn uses per (sequence, KV head) for these shapes
+ * (num_splits_request as in kvq_decode_attn), or a negative KVQ_ERR_* code.  Host only. */
+int32_t kvq_decode_num_splits(int32_t n_seq, int32_t num_kv_heads, int32_t max_seq_len,
+                              int32_t num_splits_request);
+
+/* Workspace bytes kvq_decode_attn needs for these shapes (0 on invalid shapes).  Host only. */
+size_t kvq_decode_workspace_bytes(int32_t n_seq, int32_t n_rows, int32_t n_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
+                                  int32_t num_splits_request);
+
+/* Static description of a return code. */
+const char* kvq_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,332 @@
+/*
+ * kvq_oracle.c — the plain CPU oracle for the paged K8/V4 cache and its decode attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg may load this library.  It shares no code with the HIP library: the byte format, the
+ * quantizer, the fp16 conversion and the attention are written here again from their
+ * definitions, slowly and in the order the definitions state them.
+ *
+ * What it computes (the definition; the GPU's split-KV flash-decoding reaches the same value
+ * up to fp32 rounding):
+ *   - quantization of each new token's K row to int8 with one fp16 scale, and of its V row to
+ *     int4 with one fp16 scale per 32 dims (the engine's "rk8v4"/K8-V4 KV dtype: forum post
+ *     "3090 单卡跑 Qwen3.8-27B：NInfer 上机实测（180K 上下文 / C2 并发 / 4bit KV）", section
+ *     一、部署, launch-flag table; the pages leave the scale granularity open, the library
+ *     header fixes it and this file follows that definition);
+ *   - the page format of that header (the KV cache kept in fixed-size pieces of the context,
+ *     blog page "標籤: vLLM", section 重點說明 part 2 on segmented KV);
+ *   - exact attention in fp64 over the dequantized entries, token by token in logical order
+ *     through the page table, with the causal mask of an MTP verify step (same forum post,
+ *     --spec mtp --draft-tokens 3).
+ *
+ * Build: gcc -O2 -std=c11 -fopenmp -ffp-contract=off -shared -fPIC (no fast-math: the quantizer
+ * relies on IEEE fp32 division and round-half-to-even).
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------------------------------------------------------- IEEE binary16 ---------- */
+
+/* Value of an IEEE 754 binary16 bit pattern: subnormals are f * 2^-24, normals are
+ * (1024 + f) * 2^(e - 25) for biased exponent e in 1..30. */
+double kvq_oracle_fp16_to_double(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 31;
+  int f = h & 1023;
+  double v;
+  if (e == 0)
+    v = ldexp((double)f, -24);
+  else if (e == 31)
+    v = f ? NAN : INFINITY;
+  else
+    v = ldexp(1024.0 + (double)f, e - 25);
+  return sign ? -v : v;
+}
+
+/* Round x to the nearest binary16 value, ties to even (IEEE default rounding).  The spacing
+ * of binary16 values near |x| is 2^(E-10) with E = max(floor(log2|x|), -14); rounding |x| to a
+ * multiple of that spacing is the definition of round-to-nearest.  Magnitudes that round to
+ * 65520 or above overflow to infinity. */
+uint16_t kvq_oracle_fp16_from_double(double x) {
+  if (isnan(x)) return 0x7E00;
+  uint16_t sign = signbit(x) ? 0x8000 : 0;
+  double a = fabs(x);
+  if (a == 0.0) return sign;
+  int E;
+  frexp(a, &E);           /* a = m * 2^E, m in [0.5, 1)  ->  floor(log2 a) = E - 1 */
+  int e = E - 1;
+  if (e < -14) e = -14;   /* below the normal range the spacing stays 2^-24 */
+  double quantum = ldexp(1.0, e - 10);
+  double n = nearbyint(a / quantum); /* exact quotient (power-of-two scaling); ties to even */
+  double r = n * quantum;
+  if (r >= 65520.0) return sign | 0x7C00;
+  if (r < ldexp(1.0, -14)) return sign | (uint16_t)n; /* subnormal: field = r / 2^-24 */
+  int Er;
+  frexp(r, &Er);
+  int ebits = (Er - 1) + 15;
+  int mbits = (int)(ldexp(r, -(Er - 1)) * 1024.0 - 1024.0);
+  return sign | (uint16_t)(ebits << 10) | (uint16_t)mbits;
+}
+
+/* ---------------------------------------------------------------- quantizer -------------- */
+
+/* One scale group: absmax -> scale = fp16_rne(absmax / qmax) (fp32 IEEE divide, saturated to
+ * the largest finite fp16) -> code = clamp(rint_half_even(x / scale), -qmax, qmax) with the
+ * divide in fp32 and the stored fp16 scale, all codes 0 when the scale is 0. */
+void kvq_oracle_quantize_group(const float* x, int n, int qmax, int8_t* codes,
+                               uint16_t* scale_bits) {
+  float a = 0.0f;
+  for (int i = 0; i < n; ++i) {
+    float m = fabsf(x[i]);
+    if (m > a) a = m;
+  }
+  float s32 = a / (float)qmax;
+  uint16_t sb = kvq_oracle_fp16_from_double((double)s32);
+  if ((sb & 0x7FFF) == 0x7C00) sb = (uint16_t)((sb & 0x8000) | 0x7BFF);
+  *scale_bits = sb;
+  float s = (float)kvq_oracle_fp16_to_double(sb);
+  for (int i = 0; i < n; ++i) {
+    if (s == 0.0f) {
+      codes[i] = 0;
+      continue;
+    }
+    float y = x[i] / s;
+    float c = nearbyintf(y);
+    if (c > (float)qmax) c = (float)qmax;
+    if (c < (float)-qmax) c = (float)-qmax;
+    codes[i] = (int8_t)c;
+  }
+}
+
+/* ---------------------------------------------------------------- page format ------------ */
+
+size_t kvq_oracle_block_bytes(int P, int D) { return (size_t)P * (size_t)(D + 2 + D / 2 + D / 16); }
+
+static size_t k_code_offset(int D, int s, int d) {
+  int tile = s / 16, t = s % 16;
+  return (size_t)16 * D * tile + (size_t)256 * (d / 16) + (size_t)16 * t + (size_t)(d % 16);
+}
+static size_t k_scale_offset(int P, int D, int s) { return (size_t)P * D + (size_t)2 * s; }
+static size_t v_code_offset(int P, int D, int s, int d, int* high_nibble) {
+  int tile = s / 16, t = s % 16;
+  int j = d / 32;
+  int lane = 16 * (t / 4) + d % 16;
+  int r = t % 4;
+  int w = D / 32 < 4 ? D / 32 : 4;
+  *high_nibble = (d / 16) % 2;
+  return (size_t)P * D + (size_t)2 * P + (size_t)8 * D * tile + (size_t)256 * w * (j / w) +
+         (size_t)4 * w * lane + (size_t)4 * (j % w) + (size_t)r;
+}
+static size_t v_scale_offset(int P, int D, int s, int j) {
+  return (size_t)P * D + (size_t)2 * P + (size_t)P * D / 2 + (size_t)2 * ((size_t)s * (D / 32) + j);
+}
+
+/* Byte offset of a quantity within its block, exposed so tests can check the format's
+ * bijectivity: what = 0 K code, 1 K scale, 2 V code (returns nibble in *aux), 3 V scale. */
+long long kvq_oracle_format_offset(int what, int P, int D, int s, int d, int* aux) {
+  *aux = 0;
+  switch (what) {
+    case 0: return (long long)k_code_offset(D, s, d);
+    case 1: return (long long)k_scale_offset(P, D, s);
+    case 2: return (long long)v_code_offset(P, D, s, d, aux);
+    case 3: return (long long)v_scale_offset(P, D, s, d);
+  }
+  return -1;
+}
+
+static uint8_t* block_of(uint8_t* pool, int Hkv, int P, int D, int page, int h) {
+  return pool + ((size_t)page * Hkv + h) * kvq_oracle_block_bytes(P, D);
+}
+
+/* Quantize n_tok tokens and write them into their slots (slot < 0 or beyond the pool: skip). */
+void kvq_oracle_append(uint8_t* pool, int num_pages, int P, int Hkv, int D, const float* k,
+                       const float* v, const int32_t* slots, int n_tok) {
+  int8_t* codes = (int8_t*)malloc((size_t)D);
+  for (int n = 0; n < n_tok; ++n) {
+    long long slot = slots[n];
+    if (slot < 0 || slot >= (long long)num_pages * P) continue;
+    int page = (int)(slot / P), s = (int)(slot % P);
+    for (int h = 0; h < Hkv; ++h) {
+      uint8_t* blk = block_of(pool, Hkv, P, D, page, h);
+      const float* krow = k + ((size_t)n * Hkv + h) * D;
+      const float* vrow = v + ((size_t)n * Hkv + h) * D;
+      uint16_t sb;
+      kvq_oracle_quantize_group(krow, D, 127, codes, &sb);
+      for (int d = 0; d < D; ++d) blk[k_code_offset(D, s, d)] = (uint8_t)codes[d];
+      size_t so = k_scale_offset(P, D, s);
+      blk[so] = (uint8_t)(sb & 0xFF);
+      blk[so + 1] = (uint8_t)(sb >> 8);
+      for (int j = 0; j < D / 32; ++j) {
+        kvq_oracle_quantize_group(vrow + 32 * j, 32, 7, codes + 32 * j, &sb);
+        size_t vo = v_scale_offset(P, D, s, j);
+        blk[vo] = (uint8_t)(sb & 0xFF);
+        blk[vo + 1] = (uint8_t)(sb >> 8);
+      }
+      for (int d = 0; d < D; ++d) {
+        int hi;
+        size_t o = v_code_offset(P, D, s, d, &hi);
+        uint8_t nib = (uint8_t)(codes[d] & 0x0F);
+        blk[o] = hi ? (uint8_t)((blk[o] & 0x0F) | (nib << 4)) : (uint8_t)((blk[o] & 0xF0) | nib);
+      }
+    }
+  }
+  free(codes);
+}
+
+/* Read back one slot of one head: codes and fp16 scale bits (kc[D], ks[1], vc[D], vs[D/32]). */
+void kvq_oracle_read_slot(const uint8_t* pool, int P, int Hkv, int D, int page, int s, int h,
+                          int8_t* kc, uint16_t* ks, int8_t* vc, uint16_t* vs) {
+  const uint8_t* blk = pool + ((size_t)page * Hkv + h) * kvq_oracle_block_bytes(P, D);
+  for (int d = 0; d < D; ++d) kc[d] = (int8_t)blk[k_code_offset(D, s, d)];
+  size_t so = k_scale_offset(P, D, s);
+  *ks = (uint16_t)(blk[so] | (blk[so + 1] << 8));
+  for (int d = 0; d < D; ++d) {
+    int hi;
+    size_t o = v_code_offset(P, D, s, d, &hi);
+    int nib = hi ? (blk[o] >> 4) & 0xF : blk[o] & 0xF;
+    vc[d] = (int8_t)(nib >= 8 ? nib - 16 : nib); /* 4-bit two's complement */
+  }
+  for (int j = 0; j < D / 32; ++j) {
+    size_t vo = v_scale_offset(P, D, s, j);
+    vs[j] = (uint16_t)(blk[vo] | (blk[vo + 1] << 8));
+  }
+}
+
+/* ---------------------------------------------------------------- attention -------------- */
+
+/* Dequantized K and V of logical token t of sequence b, head h (page-table entries clamped
+ * into [0, num_pages) as the library header specifies). */
+static void token_kv(const uint8_t* pool, int num_pages, int P, int Hkv, int D,
+                     const int32_t* pt_row, int t, int h, double* kd, double* vd, int8_t* kc,
+                     int8_t* vc, uint16_t* vs) {
+  int page = pt_row[t / P];
+  if (page < 0) page = 0;
+  if (page >= num_pages) page = num_pages - 1;
+  uint16_t ks;
+  kvq_oracle_read_slot(pool, P, Hkv, D, page, t % P, h, kc, &ks, vc, vs);
+  double sk = kvq_oracle_fp16_to_double(ks);
+  for (int d = 0; d < D; ++d) kd[d] = (double)kc[d] * sk;
+  for (int d = 0; d < D; ++d) vd[d] = (double)vc[d] * kvq_oracle_fp16_to_double(vs[d / 32]);
+}
+
+/* Softmax weights of one output row (sequence b, query row i, query head hq): w[t] for
+ * t < L (0 where masked).  Returns the number of attended tokens; *m_out and *sum_out get the
+ * max logit and sum of exp(z - max) for the log-sum-exp. */
+static int row_weights(const uint8_t* pool, int num_pages, int P, int Hkv, int D,
+                       const uint16_t* q, const int32_t* page_table, const int32_t* seq_lens,
+                       int R, int Hq, int max_pages, double scale, int b, int i, int hq,
+                       double* w, double* m_out, double* sum_out) {
+  int G = Hq / Hkv;
+  int h = hq / G;
+  int L = seq_lens[b];
+  int last = L - R + i; /* causal mask: row i sees tokens 0 .. L - R + i */
+  int n = last + 1;
+  if (n <= 0) {
+    *m_out = -INFINITY;
+    *sum_out = 0.0;
+    return 0;
+  }
+  double* qd = (double*)malloc(sizeof(double) * D);
+  double* kd = (double*)malloc(sizeof(double) * D);
+  double* vd = (double*)malloc(sizeof(double) * D);
+  int8_t* kc = (int8_t*)malloc((size_t)D);
+  int8_t* vc = (int8_t*)malloc((size_t)D);
+  uint16_t* vs = (uint16_t*)malloc(sizeof(uint16_t) * (D / 32));
+  const uint16_t* qrow = q + (((size_t)b * R + i) * Hq + hq) * D;
+  for (int d = 0; d < D; ++d) qd[d] = kvq_oracle_fp16_to_double(qrow[d]);
+  const int32_t* pt_row = page_table + (size_t)b * max_pages;
+  double m = -INFINITY;
+  for (int t = 0; t < n; ++t) {
+    token_kv(pool, num_pages, P, Hkv, D, pt_row, t, h, kd, vd, kc, vc, vs);
+    double dot = 0.0;
+    for (int d = 0; d < D; ++d) dot += qd[d] * kd[d];
+    w[t] = scale * dot; /* logit z_t, replaced by its weight below */
+    if (w[t] > m) m = w[t];
+  }
+  double sum = 0.0;
+  for (int t = 0; t < n; ++t) {
+    w[t] = exp(w[t] - m);
+    sum += w[t];
+  }
+  for (int t = 0; t < n; ++t) w[t] /= sum;
+  *m_out = m;
+  *sum_out = sum;
+  free(qd); free(kd); free(vd); free(kc); free(vc); free(vs);
+  return n;
+}
+
+/* Attention outputs for a list of (b, i, hq) triples (sel, n_sel of them), or for every
+ * output in [b][i][hq] order when sel is NULL.  out: [count][D] fp64, lse: [count] fp64. */
+void kvq_oracle_decode_attn(const uint8_t* pool, int num_pages, int P, int Hkv, int D,
+                            const uint16_t* q, const int32_t* page_table,
+                            const int32_t* seq_lens, int n_seq, int R, int Hq, int max_pages,
+                            double scale, const int32_t* sel, int n_sel, double* out,
+                            double* lse) {
+  if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+  int count = sel ? n_sel : n_seq * R * Hq;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int o = 0; o < count; ++o) {
+    int b, i, hq;
+    if (sel) {
+      b = sel[3 * o];
+      i = sel[3 * o + 1];
+      hq = sel[3 * o + 2];
+    } else {
+      b = o / (R * Hq);
+      i = (o / Hq) % R;
+      hq = o % Hq;
+    }
+    int L = seq_lens[b];
+    double* w = (double*)malloc(sizeof(double) * (L > 0 ? (size_t)L : 1));
+    double m, sum;
+    int n = row_weights(pool, num_pages, P, Hkv, D, q, page_table, seq_lens, R, Hq, max_pages,
+                        scale, b, i, hq, w, &m, &sum);
+    double* o_row = out + (size_t)o * D;
+    for (int d = 0; d < D; ++d) o_row[d] = 0.0;
+    if (n > 0) {
+      double* kd = (double*)malloc(sizeof(double) * D);
+      double* vd = (double*)malloc(sizeof(double) * D);
+      int8_t* kc = (int8_t*)malloc((size_t)D);
+      int8_t* vc = (int8_t*)malloc((size_t)D);
+      uint16_t* vs = (uint16_t*)malloc(sizeof(uint16_t) * (D / 32));
+      const int32_t* pt_row = page_table + (size_t)b * max_pages;
+      int h = hq / (Hq / Hkv);
+      for (int t = 0; t < n; ++t) {
+        token_kv(pool, num_pages, P, Hkv, D, pt_row, t, h, kd, vd, kc, vc, vs);
+        for (int d = 0; d < D; ++d) o_row[d] += w[t] * vd[d];
+      }
+      free(kd); free(vd); free(kc); free(vc); free(vs);
+      lse[o] = m + log(sum);
+    } else {
+      lse[o] = -INFINITY;
+    }
+    free(w);
+  }
+}
+
+/* Softmax weights of one output row, w[0..L-1] (0 where masked). Returns attended count. */
+int kvq_oracle_attn_weights(const uint8_t* pool, int num_pages, int P, int Hkv, int D,
+                            const uint16_t* q, const int32_t* page_table,
+                            const int32_t* seq_lens, int R, int Hq, int max_pages, double scale,
+                            int b, int i, int hq, double* w) {
+  if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+  int L = seq_lens[b];
+  for (int t = 0; t < L; ++t) w[t] = 0.0;
+  double m, sum;
+  return row_weights(pool, num_pages, P, Hkv, D, q, page_table, seq_lens, R, Hq, max_pages,
+                     scale, b, i, hq, w, &m, &sum);
+}
+
+int kvq_oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

@@ -1,0 +1,200 @@
+"""A compact battery of the oracle pins, runnable against any compiled oracle variant.
+
+``run(o)`` returns the names of the checks that fail for oracle ``o``.  The real oracle must
+fail none; each mutant in ``test_oracle_mutations.py`` must fail at least one.  The references
+(numpy float16, argmin codes, hand-worked fixtures, pure-Python brute force, closed forms) never
+come from the oracle under test.
+"""
+from __future__ import annotations
+
+import functools
+import math
+import os
+
+import numpy as np
+
+from long_context_decode_flash_amd import workloads as W
+from tests import brute
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+BRUTE_CASES = [
+    dict(n_seq=1, seq_lens=(37,), num_kv_heads=1, n_q_heads=4, head_dim=64, page_size=16,
+         n_rows=1),
+    dict(n_seq=2, seq_lens=(45, 20), num_kv_heads=2, n_q_heads=6, head_dim=64, page_size=16,
+         n_rows=4),
+    dict(n_seq=1, seq_lens=(33,), num_kv_heads=1, n_q_heads=2, head_dim=128, page_size=32,
+         n_rows=2, k_outliers=True),
+]
+
+
+def _case(i):
+    c = BRUTE_CASES[i]
+    return W.custom(**c, seed=sum(c["seq_lens"]))
+
+
+@functools.lru_cache(maxsize=None)
+def _brute_ref(i):
+    inp = _case(i)
+    wl = inp.wl
+    n, L, H, D = wl.n_seq, wl.seq_len, wl.num_kv_heads, wl.head_dim
+    kc = np.zeros((n, L, H, D), np.int8)
+    vc = np.zeros((n, L, H, D), np.int8)
+    ks = np.zeros((n, L, H), np.uint16)
+    vs = np.zeros((n, L, H, D // 32), np.uint16)
+    for b in range(n):
+        for t in range(int(inp.seq_lens[b])):
+            for h in range(H):
+                kc[b, t, h], ks[b, t, h], vc[b, t, h], vs[b, t, h] = brute.quantize_token_np(
+                    inp.k[b, t, h], inp.v[b, t, h])
+    return brute.attention_brute(inp.q_bits, kc, ks, vc, vs, inp.seq_lens, wl.n_rows,
+                                 wl.n_q_heads, H, 1.0 / math.sqrt(D))
+
+
+def _golden_lines(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                yield line
+
+
+def check_fp16(o):
+    for bits in range(0, 1 << 16, 7):
+        ref = float(np.uint16(bits).view(np.float16))
+        got = o.fp16_to_double(bits)
+        if not (math.isnan(ref) and math.isnan(got)) and got != ref:
+            return False
+    rng = np.random.default_rng(4)
+    xs = (rng.standard_normal(500) * 10.0 ** rng.integers(-9, 6, 500)).astype(np.float32)
+    ties = [np.float32((float(np.uint16(b).view(np.float16)) +
+                        float(np.uint16(b + 1).view(np.float16))) / 2)
+            for b in list(range(1, 0x400, 61)) + list(range(0x400, 0x7BFF, 1499))]
+    with np.errstate(over="ignore"):
+        return all(o.fp16_from_double(float(x)) == brute.fp16_bits_np(x)
+                   for x in list(xs) + ties)
+
+
+def check_quantizer_golden(o):
+    for line in _golden_lines("quantizer_cases.txt"):
+        qmax, vals, sb, codes = [p.strip() for p in line.split(";")]
+        vals = [float(v) for v in vals.split()]
+        codes = [int(c) for c in codes.split()]
+        x = np.zeros(32, np.float32)
+        x[:len(vals)] = vals
+        c, s = o.quantize_group(x, int(qmax))
+        if s != int(sb, 16) or list(c[:len(codes)]) != codes:
+            return False
+    return True
+
+
+def check_quantizer_argmin(o):
+    rng = np.random.default_rng(9)
+    for qmax, n in ((127, 64), (7, 32)):
+        for _ in range(10):
+            x = rng.standard_normal(n).astype(np.float32)
+            c, sb = o.quantize_group(x, qmax)
+            if sb != brute.fp16_bits_np(np.float32(np.max(np.abs(x))) / np.float32(qmax)):
+                return False
+            s = brute.fp16_value_np(sb)
+            for xi, ci in zip(x, c):
+                q = float(xi) / s
+                if abs(q - math.floor(q) - 0.5) < 1e-6 * max(1.0, abs(q)):
+                    continue
+                if int(ci) != brute.argmin_code(float(xi), s, qmax):
+                    return False
+    return True
+
+
+def check_format_golden(o):
+    for line in _golden_lines("format_offsets.txt"):
+        lhs, rhs = line.split("->")
+        what, P, D, s, idx = (int(x) for x in lhs.split())
+        if o.format_offset(what, P, D, s, idx) != tuple(int(x) for x in rhs.split()):
+            return False
+    return True
+
+
+def _fill(o, inp):
+    wl = inp.wl
+    pool = o.new_pool(wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim)
+    k, v, slots = inp.all_tokens()
+    o.append(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim, k, v, slots)
+    return pool
+
+
+def _attend(o, inp, pool, scale=0.0):
+    wl = inp.wl
+    return o.decode_attn(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
+                         inp.q_bits, inp.page_table, inp.seq_lens, wl.n_rows, wl.n_q_heads,
+                         softmax_scale=scale)
+
+
+def check_brute_force(o):
+    for i in range(len(BRUTE_CASES)):
+        inp = _case(i)
+        out, lse = _attend(o, inp, _fill(o, inp))
+        out_b, lse_b = _brute_ref(i)
+        if not (np.allclose(out, out_b, rtol=0, atol=1e-12) and
+                np.allclose(lse, lse_b, rtol=0, atol=1e-11)):
+            return False
+    return True
+
+
+def check_closed_forms(o):
+    # zero query -> uniform mean, lse = ln L
+    inp = W.custom(n_seq=1, seq_lens=(40,), num_kv_heads=1, n_q_heads=2, head_dim=64,
+                   page_size=16, n_rows=1, seed=23)
+    inp.q_bits[:] = 0
+    out, lse = _attend(o, inp, _fill(o, inp))
+    if not abs(lse[0, 0, 0] - math.log(40)) < 1e-12:
+        return False
+    kc_vs = [brute.quantize_token_np(inp.k[0, t, 0], inp.v[0, t, 0]) for t in range(40)]
+    mean = np.mean([c[2].astype(float) * np.repeat([brute.fp16_value_np(x) for x in c[3]], 32)
+                    for c in kc_vs], 0)
+    if not np.allclose(out[0, 0, 0], mean, rtol=0, atol=1e-13):
+        return False
+    # weights sum to 1 under the causal mask
+    inp = W.custom(n_seq=1, seq_lens=(70,), num_kv_heads=2, n_q_heads=4, head_dim=64,
+                   page_size=16, n_rows=4, seed=26)
+    pool = _fill(o, inp)
+    for i in range(4):
+        w, n = o.attn_weights(pool, inp.wl.pool_pages, 16, 2, 64, inp.q_bits, inp.page_table,
+                              inp.seq_lens, 4, 4, 0, i, 3)
+        if n != 67 + i or abs(w.sum() - 1.0) > 1e-12:
+            return False
+    return True
+
+
+def check_large_logits(o):
+    """Two tokens with logits in the thousands: the blend is the sigmoid closed form and the
+    log-sum-exp is max + log1p(exp(-gap)); a softmax without its max shift overflows."""
+    inp = W.custom(n_seq=1, seq_lens=(2,), num_kv_heads=1, n_q_heads=1, head_dim=64,
+                   page_size=16, n_rows=1, seed=24)
+    scale = 900.0
+    out, lse = _attend(o, inp, _fill(o, inp), scale=scale)
+    kv = [brute.quantize_token_np(inp.k[0, t, 0], inp.v[0, t, 0]) for t in range(2)]
+    q = inp.q_bits[0, 0, 0].view(np.float16).astype(float)
+    z = [scale * (q @ (c[0].astype(float) * brute.fp16_value_np(c[1]))) for c in kv]
+    v = [c[2].astype(float) * np.repeat([brute.fp16_value_np(x) for x in c[3]], 32) for c in kv]
+    gap = z[1] - z[0]
+    sig = 1.0 / (1.0 + math.exp(gap)) if gap < 700 else 0.0
+    if not np.allclose(out[0, 0, 0], sig * v[0] + (1 - sig) * v[1], rtol=0, atol=1e-12):
+        return False
+    return abs(lse[0, 0, 0] - (max(z) + math.log1p(math.exp(-abs(gap))))) < 1e-9 * abs(max(z))
+
+
+CHECKS = [check_fp16, check_quantizer_golden, check_quantizer_argmin, check_format_golden,
+          check_brute_force, check_closed_forms, check_large_logits]
+
+
+def run(o):
+    failed = []
+    for chk in CHECKS:
+        try:
+            ok = chk(o)
+        except Exception:  # a crash inside a check counts as a caught mistake
+            ok = False
+        if not ok:
+            failed.append(chk.__name__)
+    return failed

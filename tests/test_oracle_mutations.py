@@ -1,0 +1,58 @@
+"""Plausible mistakes planted in copies of the CPU oracle (on the CPU) must be caught by the pins.
+
+Each mutant is the oracle source with one text substitution (a dropped term, a wrong sign,
+index, bound or rounding), compiled with gcc into a temporary directory and run through the pin
+battery.  The unmodified oracle must pass the same battery.
+"""
+import os
+
+import pytest
+
+import oracle
+from tests import pin_battery
+
+MUTATIONS = {
+    "scale_divisor": ("float s32 = a / (float)qmax;", "float s32 = a / (float)(qmax + 1);"),
+    "truncate_not_round": ("float c = nearbyintf(y);", "float c = truncf(y);"),
+    "no_clamp": ("if (c > (float)qmax) c = (float)qmax;", ""),
+    "unrounded_scale": ("float s = (float)kvq_oracle_fp16_to_double(sb);", "float s = s32;"),
+    "fp16_ties_away": ("double n = nearbyint(a / quantum);", "double n = round(a / quantum);"),
+    "fp16_subnormal_floor": ("if (e < -14) e = -14;", "if (e < -15) e = -15;"),
+    "v_group_stride": ("vrow + 32 * j", "vrow + 16 * j"),
+    "v_nibble_unsigned": ("(int8_t)(nib >= 8 ? nib - 16 : nib)", "(int8_t)(nib)"),
+    "k_scale_dropped": ("kd[d] = (double)kc[d] * sk;", "kd[d] = (double)kc[d];"),
+    "v_scale_group": ("kvq_oracle_fp16_to_double(vs[d / 32])", "kvq_oracle_fp16_to_double(vs[d / 64])"),
+    "mask_off_by_one": ("int last = L - R + i;", "int last = L - R + i - 1;"),
+    "gqa_map_logits": ("int h = hq / G;", "int h = hq % Hkv;"),
+    "gqa_map_values": ("int h = hq / (Hq / Hkv);", "int h = hq % Hkv;"),
+    "exp_sign": ("w[t] = exp(w[t] - m);", "w[t] = exp(m - w[t]);"),
+    "lse_drops_max": ("lse[o] = m + log(sum);", "lse[o] = log(sum);"),
+    "default_scale": ("if (scale <= 0.0) scale = 1.0 / sqrt((double)D);\n  int count",
+                      "if (scale <= 0.0) scale = 1.0 / (double)D;\n  int count"),
+    "wrong_slot": ("kvq_oracle_read_slot(pool, P, Hkv, D, page, t % P, h, kc, &ks, vc, vs);",
+                   "kvq_oracle_read_slot(pool, P, Hkv, D, page, (t + 1) % P, h, kc, &ks, vc, vs);"),
+    "k_tokens_swapped": ("(size_t)16 * t + (size_t)(d % 16)", "(size_t)16 * (t ^ 1) + (size_t)(d % 16)"),
+    "v_lane_transposed": ("int lane = 16 * (t / 4) + d % 16;\n  int r = t % 4;",
+                          "int lane = 16 * (t % 4) + d % 16;\n  int r = t / 4;"),
+    "wrong_query_row": ("q + (((size_t)b * R + i) * Hq + hq) * D",
+                        "q + (((size_t)b * R + (R - 1)) * Hq + hq) * D"),
+    "no_normalize": ("for (int t = 0; t < n; ++t) w[t] /= sum;", ""),
+    "no_running_max": ("if (w[t] > m) m = w[t];", "m = 0.0;"),
+}
+
+
+def test_unmodified_oracle_passes_the_battery():
+    assert pin_battery.run(oracle.default()) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTATIONS[name]
+    src = open(oracle.SOURCE).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique or missing"
+    path = os.path.join(tmp_path, "mutant.c")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    lib = oracle.build(force=True, source=path, out=os.path.join(tmp_path, "libmutant.so"))
+    failed = pin_battery.run(oracle.Oracle(lib))
+    assert failed, f"mutation {name} slipped past every pin"
