@@ -1,0 +1,170 @@
+// kvq_api.hip — the C ABI of include/kvq.h: argument validation (all on the host, before any
+// HIP call), split planning, workspace sizing and the launches.
+#include "kvq.h"
+
+#include <math.h>
+
+#include "kvq_internal.h"
+
+namespace {
+
+bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
+bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
+
+// Waves the decode grid aims for: 256 CUs x 4 SIMDs x 2.
+constexpr long long kTargetWaves = 2048;
+// A split covers at least this many 32-token blocks, so the per-wave prologue (query operands)
+// and the partial it writes stay small next to the bytes it streams.
+constexpr long long kMinBlocksPerSplit = 4;
+
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+struct Plan {
+  int splits;
+  int blocks_per_split;
+};
+
+int plan_splits(int n_seq, int num_kv_heads, int max_seq_len, int request, Plan* plan) {
+  if (n_seq <= 0 || num_kv_heads <= 0 || max_seq_len <= 0 || request < 0) return KVQ_ERR_ARG;
+  const long long nblk = ceil_div(max_seq_len, kvq::kBlock);
+  const long long units = (long long)n_seq * num_kv_heads;
+  long long s;
+  if (request > 0) {
+    s = request;
+  } else {
+    s = ceil_div(kTargetWaves, units);
+    s = s < ceil_div(nblk, kMinBlocksPerSplit) ? s : ceil_div(nblk, kMinBlocksPerSplit);
+  }
+  if (s < 1) s = 1;
+  if (s > nblk) s = nblk;
+  const long long bps = ceil_div(nblk, s);
+  s = ceil_div(nblk, bps);  // drop splits that would start past the last block
+  if (units * s > (1LL << 30)) return KVQ_ERR_ARG;
+  plan->splits = (int)s;
+  plan->blocks_per_split = (int)bps;
+  return KVQ_OK;
+}
+
+size_t workspace_for(long long units, int splits, int rows, int head_dim) {
+  const size_t acc = (size_t)units * splits * rows * head_dim * sizeof(float);
+  const size_t ml = (size_t)units * splits * rows * 2 * sizeof(float);
+  return acc + ml;
+}
+
+int pool_args_ok(const void* pool, int32_t num_pages, int32_t page_size, int32_t num_kv_heads,
+                 int32_t head_dim) {
+  if (!pool || num_pages <= 0 || num_kv_heads <= 0 || page_size <= 0) return KVQ_ERR_ARG;
+  if (!head_dim_ok(head_dim) || !pow2_in(page_size, 16, 256)) return KVQ_ERR_UNSUPPORTED;
+  if (((uintptr_t)pool & 15) != 0) return KVQ_ERR_ARG;
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kvq_block_bytes(int32_t page_size, int32_t head_dim) {
+  if (!head_dim_ok(head_dim) || !pow2_in(page_size, 16, 256)) return 0;
+  return kvq::block_bytes(page_size, head_dim);
+}
+
+const char* kvq_strerror(int code) {
+  switch (code) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_ARG: return "invalid argument (NULL pointer, non-positive or inconsistent size)";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported shape (head_dim, page_size or rows per KV head)";
+    case KVQ_ERR_WORKSPACE: return "workspace missing or smaller than kvq_decode_workspace_bytes()";
+    case KVQ_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown kvq error code";
+}
+
+int32_t kvq_decode_num_splits(int32_t n_seq, int32_t num_kv_heads, int32_t max_seq_len,
+                              int32_t num_splits_request) {
+  Plan p;
+  const int rc = plan_splits(n_seq, num_kv_heads, max_seq_len, num_splits_request, &p);
+  return rc == KVQ_OK ? p.splits : rc;
+}
+
+size_t kvq_decode_workspace_bytes(int32_t n_seq, int32_t n_rows, int32_t n_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
+                                  int32_t num_splits_request) {
+  if (n_rows <= 0 || n_q_heads <= 0 || num_kv_heads <= 0 || n_q_heads % num_kv_heads != 0 ||
+      !head_dim_ok(head_dim))
+    return 0;
+  Plan p;
+  if (plan_splits(n_seq, num_kv_heads, max_seq_len, num_splits_request, &p) != KVQ_OK) return 0;
+  const int rows = (n_q_heads / num_kv_heads) * n_rows;
+  return workspace_for((long long)n_seq * num_kv_heads, p.splits, rows, head_dim);
+}
+
+int kvq_append(void* pool, int32_t num_pages, int32_t page_size, int32_t num_kv_heads,
+               int32_t head_dim, const float* k, const float* v, const int32_t* slot_mapping,
+               int32_t n_tok, void* stream) {
+  int rc = pool_args_ok(pool, num_pages, page_size, num_kv_heads, head_dim);
+  if (rc != KVQ_OK) return rc;
+  if (n_tok < 0) return KVQ_ERR_ARG;
+  if (n_tok == 0) return KVQ_OK;
+  if (!k || !v || !slot_mapping) return KVQ_ERR_ARG;
+  if ((long long)n_tok * num_kv_heads > (1LL << 33)) return KVQ_ERR_ARG;
+  kvq::AppendArgs a{(uint8_t*)pool, num_pages, page_size, num_kv_heads, k, v, slot_mapping, n_tok};
+  (void)hipGetLastError();  // start from a clean error state
+  return kvq::launch_append(head_dim, a, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+int kvq_decode_attn(const void* pool, int32_t num_pages, int32_t page_size,
+                    int32_t num_kv_heads, int32_t head_dim, const uint16_t* q,
+                    const int32_t* page_table, const int32_t* seq_lens, int32_t n_seq,
+                    int32_t n_rows, int32_t n_q_heads, int32_t max_pages_per_seq,
+                    int32_t max_seq_len, float softmax_scale, int32_t num_splits, float* out,
+                    float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = pool_args_ok(pool, num_pages, page_size, num_kv_heads, head_dim);
+  if (rc != KVQ_OK) return rc;
+  if (!q || !page_table || !seq_lens || !out) return KVQ_ERR_ARG;
+  if (n_seq <= 0 || n_q_heads <= 0 || max_pages_per_seq <= 0 || max_seq_len <= 0 ||
+      num_splits < 0)
+    return KVQ_ERR_ARG;
+  if (n_rows < 1 || n_rows > KVQ_MAX_N_ROWS) return KVQ_ERR_UNSUPPORTED;
+  if (n_q_heads % num_kv_heads != 0) return KVQ_ERR_ARG;
+  const int group = n_q_heads / num_kv_heads;
+  if ((long long)group * n_rows > KVQ_MAX_ROWS_PER_KV) return KVQ_ERR_UNSUPPORTED;
+  if ((long long)max_seq_len > (long long)max_pages_per_seq * page_size) return KVQ_ERR_ARG;
+  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return KVQ_ERR_ARG;
+  if (((uintptr_t)q & 15) != 0) return KVQ_ERR_ARG;
+  Plan plan;
+  rc = plan_splits(n_seq, num_kv_heads, max_seq_len, num_splits, &plan);
+  if (rc != KVQ_OK) return rc;
+  const int rows = group * n_rows;
+  const long long units = (long long)n_seq * num_kv_heads;
+  const size_t need = workspace_for(units, plan.splits, rows, head_dim);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15) != 0)
+    return KVQ_ERR_WORKSPACE;
+  const double scale = softmax_scale > 0.0f ? (double)softmax_scale : 1.0 / sqrt((double)head_dim);
+
+  kvq::DecodeArgs a;
+  a.pool = (const uint8_t*)pool;
+  a.num_pages = num_pages;
+  a.page_size = page_size;
+  a.num_kv_heads = num_kv_heads;
+  a.q = q;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.n_seq = n_seq;
+  a.n_rows = n_rows;
+  a.n_q_heads = n_q_heads;
+  a.group = group;
+  a.rows = rows;
+  a.max_pages = max_pages_per_seq;
+  a.max_seq_len = max_seq_len;
+  a.splits = plan.splits;
+  a.blocks_per_split = plan.blocks_per_split;
+  a.scale_log2 = (float)(scale * 1.4426950408889634074);
+  a.ws_acc = (float*)workspace;
+  a.ws_ml = (float2*)((char*)workspace + (size_t)units * plan.splits * rows * head_dim * sizeof(float));
+  a.out = out;
+  a.lse = lse;
+  (void)hipGetLastError();
+  return kvq::launch_decode(head_dim, a, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+}  // extern "C"

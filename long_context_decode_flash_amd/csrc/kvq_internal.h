@@ -1,0 +1,54 @@
+// kvq_internal.h — shared declarations of the HIP library (device code for gfx950 only).
+//
+// The page format is the one stated in include/kvq.h; the helpers here are the library's own
+// implementation of it (the CPU oracle has a separate one).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvq {
+
+constexpr int kTile = 16;        // tokens per tile
+constexpr int kBlock = 32;       // tokens per decode step of one wave (two tiles)
+constexpr int kWave = 64;
+
+__host__ __device__ constexpr size_t block_bytes(int P, int D) {
+  return (size_t)P * (size_t)(D + 2 + D / 2 + D / 16);
+}
+__host__ __device__ constexpr size_t k_scales_at(int P, int D) { return (size_t)P * D; }
+__host__ __device__ constexpr size_t v_codes_at(int P, int D) { return (size_t)P * D + 2 * (size_t)P; }
+__host__ __device__ constexpr size_t v_scales_at(int P, int D) {
+  return (size_t)P * D + 2 * (size_t)P + (size_t)P * D / 2;
+}
+
+struct AppendArgs {
+  uint8_t* pool;
+  int num_pages, page_size, num_kv_heads;
+  const float* k;
+  const float* v;
+  const int32_t* slots;
+  int n_tok;
+};
+
+struct DecodeArgs {
+  const uint8_t* pool;
+  int num_pages, page_size, num_kv_heads;
+  const uint16_t* q;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  int n_seq, n_rows, n_q_heads, group, rows;  // rows = group * n_rows (query rows per KV head)
+  int max_pages, max_seq_len;
+  int splits, blocks_per_split;
+  float scale_log2;  // softmax_scale * log2(e)
+  float* ws_acc;     // [units][splits][rows][D]
+  float2* ws_ml;     // [units][splits][rows] (running max in log2 units, sum of exp2)
+  float* out;
+  float* lse;
+};
+
+hipError_t launch_append(int head_dim, const AppendArgs& a, hipStream_t stream);
+hipError_t launch_decode(int head_dim, const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace kvq

@@ -1,0 +1,180 @@
+"""Python binding of ``libkvq.so`` (include/kvq.h): argument marshalling only.
+
+Every step of the path runs in the library's HIP kernels; torch provides device memory and the
+stream.  There is no fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
+
+KVQ_OK = 0
+KVQ_ERR_ARG = -1
+KVQ_ERR_UNSUPPORTED = -2
+KVQ_ERR_WORKSPACE = -3
+KVQ_ERR_HIP = -4
+
+_lock = threading.Lock()
+_lib = None
+
+
+class KVQError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {strerror(code)} (code {code})")
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -m long_context_decode_flash_amd.build` "
+                "(hipcc, gfx950). There is no CPU fallback.")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        I = ctypes.c_int32
+        L.kvq_block_bytes.argtypes = [I, I]
+        L.kvq_block_bytes.restype = ctypes.c_size_t
+        L.kvq_strerror.argtypes = [ctypes.c_int]
+        L.kvq_strerror.restype = ctypes.c_char_p
+        L.kvq_decode_num_splits.argtypes = [I, I, I, I]
+        L.kvq_decode_num_splits.restype = I
+        L.kvq_decode_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+        L.kvq_decode_workspace_bytes.restype = ctypes.c_size_t
+        L.kvq_append.argtypes = [P, I, I, I, I, P, P, P, I, P]
+        L.kvq_append.restype = ctypes.c_int
+        L.kvq_decode_attn.argtypes = [P, I, I, I, I, P, P, P, I, I, I, I, I, ctypes.c_float, I,
+                                      P, P, P, ctypes.c_size_t, P]
+        L.kvq_decode_attn.restype = ctypes.c_int
+        _lib = L
+        return L
+
+
+def strerror(code: int) -> str:
+    return lib().kvq_strerror(int(code)).decode()
+
+
+def block_bytes(page_size: int, head_dim: int) -> int:
+    return int(lib().kvq_block_bytes(page_size, head_dim))
+
+
+def pool_bytes(num_pages: int, page_size: int, num_kv_heads: int, head_dim: int) -> int:
+    return num_pages * num_kv_heads * block_bytes(page_size, head_dim)
+
+
+def decode_num_splits(n_seq: int, num_kv_heads: int, max_seq_len: int,
+                      num_splits: int = 0) -> int:
+    r = int(lib().kvq_decode_num_splits(n_seq, num_kv_heads, max_seq_len, num_splits))
+    if r < 0:
+        raise KVQError(r, "kvq_decode_num_splits")
+    return r
+
+
+def decode_workspace_bytes(n_seq: int, n_rows: int, n_q_heads: int, num_kv_heads: int,
+                           head_dim: int, max_seq_len: int, num_splits: int = 0) -> int:
+    return int(lib().kvq_decode_workspace_bytes(n_seq, n_rows, n_q_heads, num_kv_heads,
+                                                 head_dim, max_seq_len, num_splits))
+
+
+def _stream_ptr(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype | None = None) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+@dataclass
+class PagedCache:
+    """A caller-owned pool tensor (uint8, on the GPU) and its geometry."""
+    pool: torch.Tensor
+    num_pages: int
+    page_size: int
+    num_kv_heads: int
+    head_dim: int
+
+    @staticmethod
+    def allocate(num_pages: int, page_size: int, num_kv_heads: int, head_dim: int,
+                 device="cuda") -> "PagedCache":
+        n = pool_bytes(num_pages, page_size, num_kv_heads, head_dim)
+        if n == 0:
+            raise KVQError(KVQ_ERR_UNSUPPORTED, "PagedCache.allocate")
+        pool = torch.zeros(n, dtype=torch.uint8, device=device)
+        return PagedCache(pool, num_pages, page_size, num_kv_heads, head_dim)
+
+    def append(self, k, v, slot_mapping, stream=None) -> None:
+        append(self, k, v, slot_mapping, stream=stream)
+
+    def decode_attn(self, q, page_table, seq_lens, max_seq_len: int, **kw):
+        return decode_attn(self, q, page_table, seq_lens, max_seq_len, **kw)
+
+
+def append(cache: PagedCache, k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+           stream=None) -> None:
+    """kvq_append: quantize k, v (fp32 [n_tok][Hkv][D]) into their slots of ``cache``."""
+    n_tok = slot_mapping.numel()
+    shape = (n_tok, cache.num_kv_heads, cache.head_dim)
+    if tuple(k.shape) != shape or tuple(v.shape) != shape:
+        raise ValueError(f"k and v must be {shape}")
+    rc = lib().kvq_append(
+        _dev(cache.pool, "pool", torch.uint8), cache.num_pages, cache.page_size,
+        cache.num_kv_heads, cache.head_dim, _dev(k, "k", torch.float32),
+        _dev(v, "v", torch.float32), _dev(slot_mapping, "slot_mapping", torch.int32), n_tok,
+        _stream_ptr(stream))
+    if rc != KVQ_OK:
+        raise KVQError(rc, "kvq_append")
+
+
+def decode_attn(cache: PagedCache, q: torch.Tensor, page_table: torch.Tensor,
+                seq_lens: torch.Tensor, max_seq_len: int, *, softmax_scale: float = 0.0,
+                num_splits: int = 0, out: torch.Tensor | None = None, want_lse: bool = True,
+                lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                stream=None):
+    """kvq_decode_attn. q: fp16 [n_seq][n_rows][Hq][D]; page_table: int32 [n_seq][max_pages];
+    seq_lens: int32 [n_seq]. Returns (out fp32 [n_seq][n_rows][Hq][D], lse or None)."""
+    if q.dim() != 4 or q.shape[3] != cache.head_dim:
+        raise ValueError("q must be [n_seq][n_rows][n_q_heads][head_dim]")
+    n_seq, n_rows, n_q_heads, D = (int(x) for x in q.shape)
+    if page_table.dim() != 2 or page_table.shape[0] != n_seq:
+        raise ValueError("page_table must be [n_seq][max_pages_per_seq]")
+    if seq_lens.numel() != n_seq:
+        raise ValueError("seq_lens must have n_seq entries")
+    dev = q.device
+    if out is None:
+        out = torch.empty((n_seq, n_rows, n_q_heads, D), dtype=torch.float32, device=dev)
+    if want_lse and lse is None:
+        lse = torch.empty((n_seq, n_rows, n_q_heads), dtype=torch.float32, device=dev)
+    need = decode_workspace_bytes(n_seq, n_rows, n_q_heads, cache.num_kv_heads, D, max_seq_len,
+                                  num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    rc = lib().kvq_decode_attn(
+        _dev(cache.pool, "pool", torch.uint8), cache.num_pages, cache.page_size,
+        cache.num_kv_heads, D, _dev(q, "q", torch.float16),
+        _dev(page_table, "page_table", torch.int32), _dev(seq_lens, "seq_lens", torch.int32),
+        n_seq, n_rows, n_q_heads, int(page_table.shape[1]), int(max_seq_len),
+        float(softmax_scale), int(num_splits), _dev(out, "out", torch.float32),
+        _dev(lse, "lse", torch.float32) if lse is not None else None,
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream_ptr(stream))
+    if rc != KVQ_OK:
+        raise KVQError(rc, "kvq_decode_attn")
+    return out, lse

@@ -1,0 +1,105 @@
+"""Shared plumbing of the GPU parity tests: run a workload through the HIP library (via the
+C ABI binding) and through the CPU oracle, from the same seeded inputs."""
+from __future__ import annotations
+
+import functools
+import sys
+
+import numpy as np
+
+import oracle
+from long_context_decode_flash_amd import workloads as W
+
+TOL_ABS = 2e-3  # attention max-abs bound against the fp64 oracle
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def kvq():
+    from long_context_decode_flash_amd import kvq as _k
+    return _k
+
+
+def to_dev(a: np.ndarray):
+    torch = torch_mod()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def gpu_cache(inp: W.Inputs):
+    wl = inp.wl
+    return kvq().PagedCache.allocate(wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim)
+
+
+def gpu_append(cache, k, v, slots):
+    torch = torch_mod()
+    kvq().append(cache, to_dev(k), to_dev(v), to_dev(slots.astype(np.int32)))
+    torch.cuda.synchronize()
+
+
+def gpu_fill(inp: W.Inputs, cache=None, split_step=True):
+    """Fill a pool on the GPU: the cached context, then the step's appended tokens."""
+    cache = cache or gpu_cache(inp)
+    if split_step and inp.wl.n_new and np.all(inp.seq_lens == inp.wl.seq_len):
+        gpu_append(cache, *inp.prefill())
+        gpu_append(cache, *inp.step_tokens())
+    else:
+        gpu_append(cache, *inp.all_tokens())
+    return cache
+
+
+def gpu_decode(inp: W.Inputs, cache, num_splits=0, max_seq_len=None, page_table=None,
+               softmax_scale=0.0):
+    torch = torch_mod()
+    wl = inp.wl
+    q = to_dev(inp.q_bits).view(torch.float16)
+    pt = to_dev(inp.page_table if page_table is None else page_table)
+    sl = to_dev(inp.seq_lens)
+    msl = int(max_seq_len or max(int(inp.seq_lens.max()), 1))
+    out, lse = kvq().decode_attn(cache, q, pt, sl, msl, num_splits=num_splits,
+                                 softmax_scale=softmax_scale)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
+def oracle_fill(inp: W.Inputs):
+    wl = inp.wl
+    pool = oracle.new_pool(wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim)
+    if wl.n_new and np.all(inp.seq_lens == wl.seq_len):
+        oracle.append(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
+                      *inp.prefill())
+        oracle.append(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
+                      *inp.step_tokens())
+    else:
+        oracle.append(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
+                      *inp.all_tokens())
+    return pool
+
+
+def oracle_decode(inp: W.Inputs, pool, select=None, softmax_scale=0.0):
+    wl = inp.wl
+    return oracle.decode_attn(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
+                              inp.q_bits, inp.page_table, inp.seq_lens, wl.n_rows,
+                              wl.n_q_heads, softmax_scale=softmax_scale, select=select)
+
+
+@functools.lru_cache(maxsize=2)
+def full_workload(name: str):
+    """(inputs, oracle pool) of a full-size workload, cached across tests."""
+    inp = W.generate(W.WORKLOADS[name])
+    return inp, oracle_fill(inp)
+
+
+def report(tag, got, ref):
+    err = np.abs(got - ref)
+    mx = float(np.max(err)) if err.size else 0.0
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    say(f"{tag}: max_abs={mx:.3e} max|ref|={scale:.3e} rel={mx / max(scale, 1e-30):.3e}")
+    return mx

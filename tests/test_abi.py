@@ -1,0 +1,153 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/kvq.h declares, and its
+host-side logic (sizes, split planning, argument validation) behaves as documented.  No call
+here reaches a kernel launch: every invalid call returns before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from long_context_decode_flash_amd import build as B
+from long_context_decode_flash_amd import kvq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kvq.LIB_PATH):
+        B.build()
+    return kvq.lib()
+
+
+def declared_functions():
+    names = []
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", h)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^\s*[A-Za-z_][\w \*]*?\b(kvq_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"kvq_append", "kvq_decode_attn"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", kvq.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (kvq_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_block_bytes(lib):
+    assert kvq.block_bytes(64, 256) == 25728
+    assert kvq.block_bytes(16, 64) == 1632
+    assert kvq.block_bytes(32, 128) == 32 * (128 + 2 + 64 + 8)
+    for bad in ((64, 96), (48, 256), (8, 64), (512, 64), (0, 64)):
+        assert kvq.block_bytes(*bad) == 0
+
+
+def test_split_plan(lib):
+    # headline: 2 sequences x 4 KV heads x 92,160 tokens
+    s = kvq.decode_num_splits(2, 4, 92160)
+    nblk = 92160 // 32
+    bps = -(-nblk // s)
+    assert s * bps >= nblk and (s - 1) * bps < nblk
+    assert 1024 <= 8 * s <= 2048
+    # explicit requests are clamped to the number of 32-token blocks
+    assert kvq.decode_num_splits(1, 1, 100, 3) == 2  # 4 blocks, 2 per split
+    assert kvq.decode_num_splits(1, 1, 100, 1000) == 4
+    assert kvq.decode_num_splits(1, 1, 1, 0) == 1
+    # every planned split starts inside the context
+    for n_seq, hkv, L, req in ((1, 4, 262144, 0), (1, 1, 512, 0), (3, 2, 1001, 7), (1, 4, 8192, 0)):
+        s = kvq.decode_num_splits(n_seq, hkv, L, req)
+        nblk = -(-L // 32)
+        bps = -(-nblk // s)
+        assert (s - 1) * bps < nblk <= s * bps
+    with pytest.raises(kvq.KVQError):
+        kvq.decode_num_splits(0, 4, 100)
+    with pytest.raises(kvq.KVQError):
+        kvq.decode_num_splits(1, 4, 100, -1)
+
+
+def test_workspace_size(lib):
+    s = kvq.decode_num_splits(2, 4, 92160)
+    assert kvq.decode_workspace_bytes(2, 1, 24, 4, 256, 92160) == 2 * 4 * s * 6 * (256 + 2) * 4
+    assert kvq.decode_workspace_bytes(2, 1, 24, 5, 256, 92160) == 0  # heads not divisible
+    assert kvq.decode_workspace_bytes(2, 1, 24, 4, 100, 92160) == 0
+
+
+P = ctypes.c_void_p
+FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: validation fails first
+
+
+def append_rc(lib, pool=FAKE, num_pages=4, page_size=16, hkv=1, d=64, k=FAKE, v=FAKE,
+              slots=FAKE, n_tok=1):
+    return lib.kvq_append(pool, num_pages, page_size, hkv, d, k, v, slots, n_tok, None)
+
+
+def test_append_validation(lib):
+    assert append_rc(lib, pool=None) == kvq.KVQ_ERR_ARG
+    assert append_rc(lib, num_pages=0) == kvq.KVQ_ERR_ARG
+    assert append_rc(lib, hkv=0) == kvq.KVQ_ERR_ARG
+    assert append_rc(lib, d=96) == kvq.KVQ_ERR_UNSUPPORTED
+    assert append_rc(lib, page_size=24) == kvq.KVQ_ERR_UNSUPPORTED
+    assert append_rc(lib, page_size=512) == kvq.KVQ_ERR_UNSUPPORTED
+    assert append_rc(lib, n_tok=-1) == kvq.KVQ_ERR_ARG
+    assert append_rc(lib, k=None) == kvq.KVQ_ERR_ARG
+    assert append_rc(lib, slots=None) == kvq.KVQ_ERR_ARG
+    assert append_rc(lib, pool=ctypes.c_void_p(0x100004)) == kvq.KVQ_ERR_ARG  # misaligned
+    assert append_rc(lib, n_tok=0) == kvq.KVQ_OK  # nothing to do, nothing enqueued
+
+
+def decode_rc(lib, **kw):
+    a = dict(pool=FAKE, num_pages=8, page_size=16, hkv=2, d=64, q=FAKE, pt=FAKE, sl=FAKE,
+             n_seq=1, n_rows=1, hq=4, max_pages=8, max_seq_len=100, scale=0.0, splits=0,
+             out=FAKE, lse=None, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return lib.kvq_decode_attn(a["pool"], a["num_pages"], a["page_size"], a["hkv"], a["d"],
+                               a["q"], a["pt"], a["sl"], a["n_seq"], a["n_rows"], a["hq"],
+                               a["max_pages"], a["max_seq_len"], a["scale"], a["splits"],
+                               a["out"], a["lse"], a["ws"], a["ws_bytes"], None)
+
+
+def test_decode_validation(lib):
+    E = kvq
+    assert decode_rc(lib, pool=None) == E.KVQ_ERR_ARG
+    assert decode_rc(lib, q=None) == E.KVQ_ERR_ARG
+    assert decode_rc(lib, pt=None) == E.KVQ_ERR_ARG
+    assert decode_rc(lib, sl=None) == E.KVQ_ERR_ARG
+    assert decode_rc(lib, out=None) == E.KVQ_ERR_ARG
+    assert decode_rc(lib, d=32) == E.KVQ_ERR_UNSUPPORTED
+    assert decode_rc(lib, page_size=17) == E.KVQ_ERR_UNSUPPORTED
+    assert decode_rc(lib, n_rows=0) == E.KVQ_ERR_UNSUPPORTED
+    assert decode_rc(lib, n_rows=5) == E.KVQ_ERR_UNSUPPORTED
+    assert decode_rc(lib, hq=5) == E.KVQ_ERR_ARG                  # not a multiple of hkv
+    assert decode_rc(lib, hq=2 * 33) == E.KVQ_ERR_UNSUPPORTED      # 33 rows per KV head
+    assert decode_rc(lib, hq=2 * 9, n_rows=4) == E.KVQ_ERR_UNSUPPORTED
+    assert decode_rc(lib, max_seq_len=129) == E.KVQ_ERR_ARG       # beyond the page table
+    assert decode_rc(lib, max_seq_len=0) == E.KVQ_ERR_ARG
+    assert decode_rc(lib, n_seq=0) == E.KVQ_ERR_ARG
+    assert decode_rc(lib, splits=-1) == E.KVQ_ERR_ARG
+    assert decode_rc(lib, scale=float("nan")) == E.KVQ_ERR_ARG
+    assert decode_rc(lib, scale=float("inf")) == E.KVQ_ERR_ARG
+    assert decode_rc(lib, ws=None) == E.KVQ_ERR_WORKSPACE
+    need = kvq.decode_workspace_bytes(1, 1, 4, 2, 64, 100)
+    assert decode_rc(lib, ws_bytes=need - 1) == E.KVQ_ERR_WORKSPACE
+    assert decode_rc(lib, q=ctypes.c_void_p(0x100002)) == E.KVQ_ERR_ARG
+
+
+def test_strerror(lib):
+    for code in (0, -1, -2, -3, -4, 7):
+        assert isinstance(kvq.strerror(code), str) and kvq.strerror(code)
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(kvq, "_lib", None)
+    monkeypatch.setattr(kvq, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        kvq.lib()

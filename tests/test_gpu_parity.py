@@ -1,0 +1,234 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same seeded inputs.
+
+Bar: pool bytes (codes and scales) bit-exact; attention max-abs <= 2e-3 against the fp64
+oracle, element by element at sizes the oracle finishes in seconds and on sampled output rows
+at the full workload sizes in the launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+
+from long_context_decode_flash_amd import workloads as W
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------ append ---------------
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_append_pool_bytes_bit_exact_full_size(name):
+    H.say(f"[append bit-exact] {name}")
+    inp, pool_ref = H.full_workload(name)
+    cache = H.gpu_fill(inp)
+    pool = cache.pool.cpu().numpy()
+    diff = np.flatnonzero(pool != pool_ref)
+    H.say(f"  pool {pool.size} B, differing bytes {diff.size}")
+    assert diff.size == 0, f"first differing byte at {diff[:8]}"
+
+
+def test_append_edge_rows_bit_exact():
+    """Zero rows, tiny (subnormal-scale) rows, huge (saturating) rows, exact ties, padding
+    slots (-1) and slots past the pool in one call."""
+    H.say("[append edge rows]")
+    rng = np.random.default_rng(77)
+    for P, D, Hkv in ((16, 64, 2), (64, 256, 1), (32, 128, 3)):
+        pages = 6
+        n = 12
+        k = rng.standard_normal((n, Hkv, D)).astype(np.float32)
+        v = rng.standard_normal((n, Hkv, D)).astype(np.float32)
+        k[0] = 0.0
+        v[0] = 0.0
+        k[1] *= np.float32(1e-6)
+        v[1] *= np.float32(1e-7)
+        k[2] *= np.float32(1e7)
+        v[2] *= np.float32(1e6)
+        k[3] = (np.arange(D) % 17 - 8 + 0.5).astype(np.float32)  # halves: ties under scale 1
+        k[3, :, 0] = 127.0
+        v[4, :, :] = np.float32(3.5)
+        v[4, :, ::32] = np.float32(7.0)
+        slots = rng.choice(pages * P, n, replace=False).astype(np.int32)
+        slots[5] = -1
+        slots[6] = pages * P + 3
+        inp_pool = H.oracle.new_pool(pages, P, Hkv, D)
+        H.oracle.append(inp_pool, pages, P, Hkv, D, k, v, slots)
+        cache = H.kvq().PagedCache.allocate(pages, P, Hkv, D)
+        H.gpu_append(cache, k, v, slots)
+        got = cache.pool.cpu().numpy()
+        assert np.array_equal(got, inp_pool), (P, D, Hkv, np.flatnonzero(got != inp_pool)[:8])
+
+
+# ------------------------------------------------------------------ decode, small --------
+
+SMALL = [
+    W.WORKLOADS["tiny_512"],
+    W.scaled(W.WORKLOADS["ctx8k"], 1000),
+    W.scaled(W.WORKLOADS["ctx64k_outlier"], 777),
+    W.scaled(W.WORKLOADS["ctx184k_c2"], 611),
+    W.scaled(W.WORKLOADS["ctx256k_mtp"], 1003),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+def test_decode_small_every_output(wl):
+    """Every output element at sizes spanning several tiles and a ragged tail."""
+    H.say(f"[decode small] {wl.name} L={wl.seq_len}")
+    inp = W.generate(wl)
+    cache = H.gpu_fill(inp)
+    pool_ref = H.oracle_fill(inp)
+    assert np.array_equal(cache.pool.cpu().numpy(), pool_ref)
+    out, lse = H.gpu_decode(inp, cache)
+    out_r, lse_r = H.oracle_decode(inp, pool_ref)
+    mx = H.report("  out", out, out_r)
+    H.report("  lse", lse, lse_r)
+    assert mx <= H.TOL_ABS
+    np.testing.assert_allclose(lse, lse_r, rtol=0, atol=1e-4)
+
+
+@pytest.mark.parametrize("case", [
+    dict(n_seq=1, seq_lens=(1,), n_rows=1),
+    dict(n_seq=1, seq_lens=(4,), n_rows=4),
+    dict(n_seq=1, seq_lens=(32,), n_rows=1),
+    dict(n_seq=1, seq_lens=(33,), n_rows=2),
+    dict(n_seq=1, seq_lens=(16,), n_rows=1),
+    dict(n_seq=3, seq_lens=(1, 200, 47), n_rows=1),
+    dict(n_seq=2, seq_lens=(2, 129), n_rows=4),   # rows 0-1 of seq 0 see no token
+], ids=lambda c: "L" + "-".join(map(str, c["seq_lens"])) + f"_R{c['n_rows']}")
+def test_decode_edge_lengths(case):
+    H.say(f"[decode edge] {case}")
+    inp = W.custom(num_kv_heads=2, n_q_heads=6, head_dim=64, page_size=16, seed=5, **case)
+    cache = H.gpu_fill(inp)
+    out, lse = H.gpu_decode(inp, cache)
+    out_r, lse_r = H.oracle_decode(inp, H.oracle_fill(inp))
+    assert H.report("  out", out, out_r) <= H.TOL_ABS
+    finite = np.isfinite(lse_r)
+    assert np.array_equal(np.isfinite(lse), finite)
+    assert np.all(out[~finite] == 0)
+    np.testing.assert_allclose(lse[finite], lse_r[finite], rtol=0, atol=1e-4)
+
+
+@pytest.mark.parametrize("shape", [
+    dict(head_dim=64, page_size=16, num_kv_heads=1, n_q_heads=1, n_rows=1),
+    dict(head_dim=128, page_size=32, num_kv_heads=2, n_q_heads=16, n_rows=2),
+    dict(head_dim=256, page_size=256, num_kv_heads=1, n_q_heads=8, n_rows=4),   # 32 rows
+    dict(head_dim=128, page_size=128, num_kv_heads=4, n_q_heads=4, n_rows=3),
+    dict(head_dim=256, page_size=16, num_kv_heads=2, n_q_heads=32, n_rows=1),
+], ids=lambda s: "D{head_dim}_P{page_size}_G{g}_R{n_rows}".format(
+    g=s["n_q_heads"] // s["num_kv_heads"], **s))
+def test_decode_shapes(shape):
+    H.say(f"[decode shapes] {shape}")
+    inp = W.custom(n_seq=2, seq_lens=(531, 300), seed=9, **shape)
+    cache = H.gpu_fill(inp)
+    out, lse = H.gpu_decode(inp, cache)
+    out_r, lse_r = H.oracle_decode(inp, H.oracle_fill(inp))
+    assert H.report("  out", out, out_r) <= H.TOL_ABS
+    np.testing.assert_allclose(lse, lse_r, rtol=0, atol=1e-4)
+
+
+@pytest.mark.parametrize("wl", SMALL[1:], ids=lambda w: w.name)
+def test_decode_peaked_attention(wl):
+    """Queries scaled by 8: attention concentrates on a few tokens, outputs are O(1)."""
+    wl = W.scaled(wl, wl.seq_len, name=wl.name + "_peaked", q_scale=8.0)
+    H.say(f"[decode peaked] {wl.name}")
+    inp = W.generate(wl)
+    cache = H.gpu_fill(inp)
+    out, lse = H.gpu_decode(inp, cache)
+    out_r, lse_r = H.oracle_decode(inp, H.oracle_fill(inp))
+    assert H.report("  out", out, out_r) <= H.TOL_ABS
+    np.testing.assert_allclose(lse, lse_r, rtol=1e-6, atol=1e-4)
+
+
+def test_decode_split_count_invariance():
+    wl = W.scaled(W.WORKLOADS["ctx184k_c2"], 3001)
+    H.say(f"[split invariance] {wl.name}")
+    inp = W.generate(wl)
+    cache = H.gpu_fill(inp)
+    base, lbase = H.gpu_decode(inp, cache, num_splits=1)
+    for s in (2, 7, 0, 94):
+        out, lse = H.gpu_decode(inp, cache, num_splits=s)
+        assert H.report(f"  splits={s}", out, base) <= 1e-5
+        np.testing.assert_allclose(lse, lbase, rtol=0, atol=1e-5)
+
+
+def test_decode_page_permutation_bit_identical():
+    wl = W.scaled(W.WORKLOADS["ctx184k_c2"], 2000)
+    H.say(f"[page permutation] {wl.name}")
+    inp = W.generate(wl)
+    out_a, lse_a = H.gpu_decode(inp, H.gpu_fill(inp))
+    perm = np.random.default_rng(3).permutation(wl.pool_pages).astype(np.int32)
+    inp.page_table = perm[inp.page_table]
+    out_b, lse_b = H.gpu_decode(inp, H.gpu_fill(inp))
+    assert np.array_equal(out_a, out_b) and np.array_equal(lse_a, lse_b)
+
+
+def test_decode_mtp_rows_equal_single_row_decodes():
+    wl = W.scaled(W.WORKLOADS["ctx256k_mtp"], 1500)
+    H.say(f"[mtp rows] {wl.name}")
+    inp = W.generate(wl)
+    cache = H.gpu_fill(inp)
+    L, R = wl.seq_len, wl.n_rows
+    out, lse = H.gpu_decode(inp, cache, num_splits=5, max_seq_len=L)
+    for i in range(R):
+        one = W.generate(wl)
+        one.wl = W.scaled(wl, L, n_rows=1, n_new=0)
+        one.q_bits = np.ascontiguousarray(inp.q_bits[:, i:i + 1])
+        one.seq_lens = np.array([L - R + 1 + i], np.int32)
+        one.page_table = inp.page_table
+        o1, l1 = H.gpu_decode(one, cache, num_splits=5, max_seq_len=L)
+        assert H.report(f"  row {i}", o1[0, 0], out[0, i]) <= 1e-6
+        np.testing.assert_allclose(l1[0, 0], lse[0, i], rtol=0, atol=1e-6)
+
+
+def test_decode_batch_equals_each_sequence_alone():
+    inp = W.custom(n_seq=2, seq_lens=(700, 450), num_kv_heads=2, n_q_heads=12, head_dim=256,
+                   page_size=64, n_rows=1, seed=12)
+    H.say("[batch vs alone]")
+    cache = H.gpu_fill(inp)
+    out, lse = H.gpu_decode(inp, cache, num_splits=6, max_seq_len=700)
+    for b in range(2):
+        one = W.custom(n_seq=2, seq_lens=(700, 450), num_kv_heads=2, n_q_heads=12,
+                       head_dim=256, page_size=64, n_rows=1, seed=12)
+        one.wl = W.scaled(inp.wl, 700, n_seq=1)
+        one.q_bits = np.ascontiguousarray(inp.q_bits[b:b + 1])
+        one.page_table = np.ascontiguousarray(inp.page_table[b:b + 1])
+        one.seq_lens = inp.seq_lens[b:b + 1].copy()
+        o1, l1 = H.gpu_decode(one, cache, num_splits=6, max_seq_len=700)
+        assert np.array_equal(o1[0], out[b]) and np.array_equal(l1[0], lse[b])
+
+
+# ------------------------------------------------------------------ decode, full size ----
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_decode_full_size_sampled_rows(name):
+    """Full-size workloads, the automatic split plan (what the benchmark times), sampled rows
+    computed one by one by the oracle."""
+    H.say(f"[decode full] {name}")
+    inp, pool_ref = H.full_workload(name)
+    wl = inp.wl
+    cache = H.gpu_fill(inp)
+    out, lse = H.gpu_decode(inp, cache)
+    rng = np.random.default_rng(wl.seed)
+    sel = {(0, 0, 0), (wl.n_seq - 1, wl.n_rows - 1, wl.n_q_heads - 1)}
+    want = min(8, wl.n_seq * wl.n_rows * wl.n_q_heads)
+    while len(sel) < want:
+        sel.add((int(rng.integers(wl.n_seq)), int(rng.integers(wl.n_rows)),
+                 int(rng.integers(wl.n_q_heads))))
+    sel = sorted(sel)
+    out_r, lse_r = H.oracle_decode(inp, pool_ref, select=sel)
+    got = np.stack([out[b, i, hq] for b, i, hq in sel])
+    got_l = np.array([lse[b, i, hq] for b, i, hq in sel])
+    assert H.report("  out", got, out_r) <= H.TOL_ABS
+    np.testing.assert_allclose(got_l, lse_r, rtol=0, atol=1e-4)
+    assert np.all(np.isfinite(out))
+
+
+def test_decode_rejects_small_workspace():
+    import torch
+    H.say("[workspace check]")
+    inp = W.custom(n_seq=1, seq_lens=(100,), seed=2)
+    cache = H.gpu_fill(inp)
+    kvq = H.kvq()
+    q = H.to_dev(inp.q_bits).view(torch.float16)
+    with pytest.raises(kvq.KVQError) as e:
+        kvq.decode_attn(cache, q, H.to_dev(inp.page_table), H.to_dev(inp.seq_lens), 100,
+                        workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    assert e.value.code == kvq.KVQ_ERR_WORKSPACE
