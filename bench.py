@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged K8/V4 decode step on one MI355X.
+
+A step is one pass of the whole hot path over one batch: ``kvq_append`` of the step's new
+tokens (quantize + paged write) followed by ``kvq_decode_attn`` (split-KV attention + merge)
+for every sequence, query head and query row.  The default workload is the 184,320-token KV
+pool shared by two 92,160-token sequences (4 KV heads, 24 query heads, head_dim 256, page 64,
+interleaved random page tables), the shape of the forum post "3090 单卡跑 Qwen3.8-27B：NInfer
+上机实测（180K 上下文 / C2 并发 / 4bit KV）" (一、部署, launch-flag table: 184,320-token pool,
+concurrency 2, rk8v4 KV).
+
+Cold cache: the pool is replicated into ``--copies`` copies (default 8, 2.4 GB at the default
+workload) and step k uses copy k mod copies, so no pool byte is still in the 256 MB Infinity
+Cache or the L2s when it is read again.  Inputs are resident in HBM before the timed region.
+
+Prints one JSON line (rank 0, N = 1).  Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth, 8 TB/s
+PMC_FILE = os.path.join(ROOT, "profiles", "decode_ctx184k_c2_pmc.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    """Hash of the HIP sources: counters taken on other code are not reported as traffic."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "long_context_decode_flash_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def token_bytes(head_dim: int) -> int:
+    """Stored bytes per token per KV head: K codes + K scale + V codes + V scales."""
+    return head_dim + 2 + head_dim // 2 + 2 * (head_dim // 32)
+
+
+def decode_algorithmic_bytes(wl, seq_lens) -> int:
+    """Bytes the method itself must move per decode call: every cached K/V byte of every
+    attended token once, the queries, the page-table entries used, the outputs (+ lse)."""
+    D = wl.head_dim
+    kv = sum(int(L) for L in seq_lens) * wl.num_kv_heads * token_bytes(D)
+    q = wl.n_seq * wl.n_rows * wl.n_q_heads * D * 2
+    pt = sum(-(-int(L) // wl.page_size) for L in seq_lens) * 4
+    out = wl.n_seq * wl.n_rows * wl.n_q_heads * (D + 1) * 4
+    return kv + q + pt + out
+
+
+def append_algorithmic_bytes(wl) -> int:
+    n = wl.n_seq * wl.n_new
+    return n * wl.num_kv_heads * (2 * wl.head_dim * 4 + token_bytes(wl.head_dim)) + n * 4
+
+
+def cpu_baseline(wl, inp):
+    """The oracle, as it is, on one full step of the workload on the host cores."""
+    import oracle
+    pool = oracle.new_pool(wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim)
+    t0 = time.perf_counter()
+    oracle.append(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
+                  *inp.prefill())
+    log(f"[cpu] oracle prefill {time.perf_counter() - t0:.1f}s (not timed)")
+    t0 = time.perf_counter()
+    oracle.append(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
+                  *inp.step_tokens())
+    oracle.decode_attn(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
+                       inp.q_bits, inp.page_table, inp.seq_lens, wl.n_rows, wl.n_q_heads)
+    dt = time.perf_counter() - t0
+    return dt, oracle.num_threads()
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=None, help="name in workloads.WORKLOADS")
+    ap.add_argument("--copies", type=int, default=8, help="pool copies rotated for a cold cache")
+    ap.add_argument("--splits", type=int, default=0, help="0 = automatic split plan")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path: the decode shards by KV head or sequence with no exchange, see "
+              "DESIGN.md.", file=sys.stderr)
+        return 2
+
+    import torch
+    from long_context_decode_flash_amd import kvq
+    from long_context_decode_flash_amd import workloads as W
+
+    name = args.workload or W.HEADLINE
+    wl = W.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    log(f"[bench] workload {name}: generating inputs")
+    inp = W.generate(wl)
+    D = wl.head_dim
+
+    def dev_t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    caches = [kvq.PagedCache.allocate(wl.pool_pages, wl.page_size, wl.num_kv_heads, D, dev)]
+    k_pre, v_pre, s_pre = inp.prefill()
+    kvq.append(caches[0], dev_t(k_pre), dev_t(v_pre), dev_t(s_pre))
+    del k_pre, v_pre
+    for _ in range(args.copies - 1):
+        c = kvq.PagedCache.allocate(wl.pool_pages, wl.page_size, wl.num_kv_heads, D, dev)
+        c.pool.copy_(caches[0].pool)
+        caches.append(c)
+    k_new, v_new, s_new = (dev_t(x) for x in inp.step_tokens())
+    q = dev_t(inp.q_bits).view(torch.float16)
+    pt = dev_t(inp.page_table)
+    sl = dev_t(inp.seq_lens)
+    msl = int(wl.seq_len)
+    splits = kvq.decode_num_splits(wl.n_seq, wl.num_kv_heads, msl, args.splits)
+    ws = torch.zeros(kvq.decode_workspace_bytes(wl.n_seq, wl.n_rows, wl.n_q_heads,
+                                                wl.num_kv_heads, D, msl, args.splits),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((wl.n_seq, wl.n_rows, wl.n_q_heads, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((wl.n_seq, wl.n_rows, wl.n_q_heads), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+    log(f"[bench] pool {caches[0].pool.numel() / 1e6:.1f} MB x {len(caches)} copies, "
+        f"splits {splits}")
+
+    calls = []
+    for c in caches:
+        app = kvq.prepare_append(c, k_new, v_new, s_new, stream=stream) if wl.n_new else None
+        dec = kvq.prepare_decode_attn(c, q, pt, sl, msl, out, lse, ws,
+                                      num_splits=args.splits, stream=stream)
+        calls.append((app, dec))
+
+    def step(i):
+        app, dec = calls[i % len(calls)]
+        if app:
+            app()
+        dec()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} steps done; timing {args.steps} steps")
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        app, dec = calls[i % len(calls)]
+        ev[i][0].record(stream)
+        if app:
+            app()
+        ev[i][1].record(stream)
+        dec()
+        ev[i][2].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    append_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    decode_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    log(f"[bench] {args.steps} steps in {total_ms:.2f} ms (wall {wall * 1e3:.1f} ms); "
+        f"decode call median {np.median(decode_ms) * 1e3:.1f} us, "
+        f"p90 {np.percentile(decode_ms, 90) * 1e3:.1f} us; append {append_ms * 1e3:.1f} us")
+
+    dec_bytes = decode_algorithmic_bytes(wl, inp.seq_lens)
+    step_bytes = dec_bytes + (append_algorithmic_bytes(wl) if wl.n_new else 0)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    dec_mean_s = float(np.mean(decode_ms)) * 1e-3
+    achieved = dec_bytes / dec_mean_s / 1e9
+
+    traffic = None
+    if os.path.exists(PMC_FILE):
+        with open(PMC_FILE) as f:
+            pmc = json.load(f)
+        if pmc.get("source_hash") == source_hash() and pmc.get("workload") == name:
+            traffic = pmc.get("hbm_bytes_per_launch")
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {args.copy_probe_mib} MiB device copy x3")
+
+    res = {
+        "metric": "decode-attn HBM GB/s (% of MI355X peak) + steps/s at 184K ctx, K8/V4 paged KV",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "steps_per_s": round(1e3 / ms_per_step, 1),
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": name, "n_seq": wl.n_seq, "seq_len": wl.seq_len,
+            "kv_heads": wl.num_kv_heads, "q_heads": wl.n_q_heads, "head_dim": D,
+            "page_size": wl.page_size, "pool_pages": wl.pool_pages,
+            "page_order": wl.page_order, "query_rows": wl.n_rows, "new_tokens_per_seq": wl.n_new,
+            "kv_format": "K int8/token scale, V int4/32-dim scale", "splits": splits,
+            "pool_copies": len(caches), "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "kvq_decode_attn (split-KV partial kernel + LSE merge kernel)",
+            "algorithmic_bytes_per_launch": dec_bytes,
+            "launch_us_mean": round(dec_mean_s * 1e6, 2),
+            "launch_us_median": round(float(np.median(decode_ms)) * 1e3, 2),
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline: oracle on one full step")
+        dt, cores = cpu_baseline(wl, inp)
+        res["cpu_baseline"] = {
+            "value": round(step_bytes / dt / 1e9, 4),
+            "unit": "GB/s",
+            "cores": cores,
+            "kind": "oracle",
+            "sample": f"one full step of {name} (append of {wl.n_seq * wl.n_new} tokens + "
+                      f"attention of all {wl.n_seq * wl.n_rows * wl.n_q_heads} output rows over "
+                      f"{wl.seq_len} tokens each), fp64, {dt:.2f} s",
+            "s_per_step": round(dt, 3),
+        }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

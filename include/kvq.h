@@ -125,13 +125,17 @@ int kvq_append(void* pool, int32_t num_pages, int32_t page_size, int32_t num_kv_
  *   max_seq_len   host-side upper bound on seq_lens; sizes the grid and the workspace.
  *   softmax_scale <= 0 selects 1/sqrt(head_dim).
  *   num_splits    0 = choose automatically (kvq_decode_num_splits); otherwise the number of
- *                 pieces each (sequence, KV head) context is cut into, clamped to the number of
- *                 32-token blocks.  The result does not depend on it beyond fp32 rounding.
+ *                 pieces each (sequence, KV head) context is cut into (one workgroup each),
+ *                 clamped to the number of 32-token blocks and to 128.  The result does not depend on it
+ *                 beyond fp32 rounding.
  *   out           device fp32 [n_seq][n_rows][n_q_heads][head_dim].
  *   lse           device fp32 [n_seq][n_rows][n_q_heads], or NULL.
  *   workspace     device scratch of at least kvq_decode_workspace_bytes(...) bytes, 16-byte
- *                 aligned; contents on entry are ignored, on exit unspecified.  Two calls in
- *                 flight at once must not share it.
+ *                 aligned, zero-filled before its first use (e.g. allocated with torch.zeros).
+ *                 Its first bytes hold one arrival counter per (sequence, KV head) with which
+ *                 the last workgroup to finish detects that it must merge the pieces; every
+ *                 call leaves those counters at zero again, so one zero-fill serves any number
+ *                 of calls of any shape.  Two calls in flight at once must not share it.
  * Returns KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE or KVQ_ERR_HIP.
  */
 int kvq_decode_attn(const void* pool, int32_t num_pages, int32_t page_size,

@@ -11,11 +11,10 @@ namespace {
 bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
 bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
 
-// Waves the decode grid aims for: 256 CUs x 4 SIMDs x 2.
-constexpr long long kTargetWaves = 2048;
-// A split covers at least this many 32-token blocks, so the per-wave prologue (query operands)
-// and the partial it writes stay small next to the bytes it streams.
-constexpr long long kMinBlocksPerSplit = 4;
+// Workgroups (4 waves each) the decode grid aims for: one per CU of the 256.
+constexpr long long kTargetGroups = 256;
+// A split covers at least one 32-token block per wave of its workgroup.
+constexpr long long kMinBlocksPerSplit = kvq::kWavesPerGroup;
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
@@ -32,11 +31,13 @@ int plan_splits(int n_seq, int num_kv_heads, int max_seq_len, int request, Plan*
   if (request > 0) {
     s = request;
   } else {
-    s = ceil_div(kTargetWaves, units);
-    s = s < ceil_div(nblk, kMinBlocksPerSplit) ? s : ceil_div(nblk, kMinBlocksPerSplit);
+    s = ceil_div(kTargetGroups, units);
+    const long long cap = ceil_div(nblk, kMinBlocksPerSplit);
+    s = s < cap ? s : cap;
   }
   if (s < 1) s = 1;
   if (s > nblk) s = nblk;
+  if (s > kvq::kMaxSplits) s = kvq::kMaxSplits;
   const long long bps = ceil_div(nblk, s);
   s = ceil_div(nblk, bps);  // drop splits that would start past the last block
   if (units * s > (1LL << 30)) return KVQ_ERR_ARG;
@@ -45,10 +46,14 @@ int plan_splits(int n_seq, int num_kv_heads, int max_seq_len, int request, Plan*
   return KVQ_OK;
 }
 
+// Workspace: [arrival counters, units x 4 B, padded to 256 B][partial numerators
+// units x splits x rows x D fp32][partial (max, sum) units x splits x rows x 2 fp32].
+size_t counters_bytes(long long units) { return (size_t)ceil_div(units * 4, 256) * 256; }
+
 size_t workspace_for(long long units, int splits, int rows, int head_dim) {
   const size_t acc = (size_t)units * splits * rows * head_dim * sizeof(float);
   const size_t ml = (size_t)units * splits * rows * 2 * sizeof(float);
-  return acc + ml;
+  return counters_bytes(units) + acc + ml;
 }
 
 int pool_args_ok(const void* pool, int32_t num_pages, int32_t page_size, int32_t num_kv_heads,
@@ -159,8 +164,9 @@ int kvq_decode_attn(const void* pool, int32_t num_pages, int32_t page_size,
   a.splits = plan.splits;
   a.blocks_per_split = plan.blocks_per_split;
   a.scale_log2 = (float)(scale * 1.4426950408889634074);
-  a.ws_acc = (float*)workspace;
-  a.ws_ml = (float2*)((char*)workspace + (size_t)units * plan.splits * rows * head_dim * sizeof(float));
+  a.ws_count = (unsigned*)workspace;
+  a.ws_acc = (float*)((char*)workspace + counters_bytes(units));
+  a.ws_ml = (float2*)((char*)a.ws_acc + (size_t)units * plan.splits * rows * head_dim * sizeof(float));
   a.out = out;
   a.lse = lse;
   (void)hipGetLastError();

@@ -13,6 +13,8 @@ namespace kvq {
 constexpr int kTile = 16;        // tokens per tile
 constexpr int kBlock = 32;       // tokens per decode step of one wave (two tiles)
 constexpr int kWave = 64;
+constexpr int kWavesPerGroup = 4;  // waves of one decode workgroup
+constexpr int kMaxSplits = 128;    // workgroups per (sequence, KV head) at most
 
 __host__ __device__ constexpr size_t block_bytes(int P, int D) {
   return (size_t)P * (size_t)(D + 2 + D / 2 + D / 16);
@@ -40,9 +42,10 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   int n_seq, n_rows, n_q_heads, group, rows;  // rows = group * n_rows (query rows per KV head)
   int max_pages, max_seq_len;
-  int splits, blocks_per_split;
+  int splits, blocks_per_split;  // workgroups per (sequence, KV head), 32-token blocks each
   float scale_log2;  // softmax_scale * log2(e)
-  float* ws_acc;     // [units][splits][rows][D]
+  unsigned* ws_count;  // [units] arrival counters: zero on entry, left zero on exit
+  float* ws_acc;     // [units][splits][rows][D] partial numerators
   float2* ws_ml;     // [units][splits][rows] (running max in log2 units, sum of exp2)
   float* out;
   float* lse;

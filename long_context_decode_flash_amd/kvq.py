@@ -166,7 +166,7 @@ def decode_attn(cache: PagedCache, q: torch.Tensor, page_table: torch.Tensor,
     need = decode_workspace_bytes(n_seq, n_rows, n_q_heads, cache.num_kv_heads, D, max_seq_len,
                                   num_splits)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
     rc = lib().kvq_decode_attn(
         _dev(cache.pool, "pool", torch.uint8), cache.num_pages, cache.page_size,
         cache.num_kv_heads, D, _dev(q, "q", torch.float16),
@@ -178,3 +178,48 @@ def decode_attn(cache: PagedCache, q: torch.Tensor, page_table: torch.Tensor,
     if rc != KVQ_OK:
         raise KVQError(rc, "kvq_decode_attn")
     return out, lse
+
+
+def prepare_append(cache: PagedCache, k: torch.Tensor, v: torch.Tensor,
+                   slot_mapping: torch.Tensor, stream=None):
+    """Marshal the arguments of one kvq_append once; the returned callable re-issues it.
+    For loops where the per-call Python checks would cost more than the kernel."""
+    n_tok = slot_mapping.numel()
+    shape = (n_tok, cache.num_kv_heads, cache.head_dim)
+    if tuple(k.shape) != shape or tuple(v.shape) != shape:
+        raise ValueError(f"k and v must be {shape}")
+    args = (_dev(cache.pool, "pool", torch.uint8), cache.num_pages, cache.page_size,
+            cache.num_kv_heads, cache.head_dim, _dev(k, "k", torch.float32),
+            _dev(v, "v", torch.float32), _dev(slot_mapping, "slot_mapping", torch.int32), n_tok,
+            _stream_ptr(stream))
+    fn = lib().kvq_append
+
+    def call():
+        rc = fn(*args)
+        if rc != KVQ_OK:
+            raise KVQError(rc, "kvq_append")
+    return call
+
+
+def prepare_decode_attn(cache: PagedCache, q: torch.Tensor, page_table: torch.Tensor,
+                        seq_lens: torch.Tensor, max_seq_len: int, out: torch.Tensor,
+                        lse: torch.Tensor | None, workspace: torch.Tensor, *,
+                        softmax_scale: float = 0.0, num_splits: int = 0, stream=None):
+    """Marshal the arguments of one kvq_decode_attn once; the returned callable re-issues it."""
+    n_seq, n_rows, n_q_heads, D = (int(x) for x in q.shape)
+    if D != cache.head_dim or tuple(out.shape) != (n_seq, n_rows, n_q_heads, D):
+        raise ValueError("q / out shapes do not match the cache")
+    args = (_dev(cache.pool, "pool", torch.uint8), cache.num_pages, cache.page_size,
+            cache.num_kv_heads, D, _dev(q, "q", torch.float16),
+            _dev(page_table, "page_table", torch.int32), _dev(seq_lens, "seq_lens", torch.int32),
+            n_seq, n_rows, n_q_heads, int(page_table.shape[1]), int(max_seq_len),
+            float(softmax_scale), int(num_splits), _dev(out, "out", torch.float32),
+            _dev(lse, "lse", torch.float32) if lse is not None else None,
+            _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream_ptr(stream))
+    fn = lib().kvq_decode_attn
+
+    def call():
+        rc = fn(*args)
+        if rc != KVQ_OK:
+            raise KVQError(rc, "kvq_decode_attn")
+    return call
