@@ -151,6 +151,7 @@ int kvq_decode_attn(const void* pool, int32_t num_pages, int32_t page_size,
   a.num_pages = num_pages;
   a.page_size = page_size;
   a.num_kv_heads = num_kv_heads;
+  a.log2_page = __builtin_ctz((unsigned)page_size);
   a.q = q;
   a.page_table = page_table;
   a.seq_lens = seq_lens;

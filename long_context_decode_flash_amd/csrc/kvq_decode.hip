@@ -1,5 +1,5 @@
-// kvq_decode.hip — split-KV decode attention over the paged K8/V4 cache, and the merge of the
-// splits by log-sum-exp.
+// kvq_decode.hip — split-KV decode attention over the paged K8/V4 cache with the log-sum-exp
+// merge of the pieces in the same launch.
 //
 // The pages describe a decode kernel tuned for one long request over a KV cache handled in
 // pieces of the context, loading only the current piece on chip (blog page "標籤: vLLM",
@@ -7,19 +7,22 @@
 // "3090 单卡跑 Qwen3.8-27B：NInfer 上机实测（180K 上下文 / C2 并发 / 4bit KV）", 二、测评 and the
 // replies on 4-bit vs fp16 KV).  The split-KV scheme here is this library's MI355X design:
 //
-//   * one 64-lane wave owns one split (a run of 32-token blocks) of one (sequence, KV head);
-//     the grid has units * splits waves so that a single long sequence fills the 256 CUs;
-//   * K codes arrive with one 16-byte load per lane in exactly the layout of the A operand of
-//     v_mfma_f32_16x16x32_f16 (tokens on M, dims on K), Q^T is the B operand (query rows of
-//     the GQA group x MTP rows on N), so QK^T is 8 MFMAs per 16 tokens for D = 256;
-//   * the 16x16 logit tile comes out with each lane holding one query row and four tokens,
-//     which is the B-operand layout of the PV product (tokens on K), so P never leaves the
-//     registers; V codes arrive pre-arranged as the A operand (dims on M, tokens on K);
-//   * int8 and int4 codes are widened to fp16 with exact integer bit tricks; the V scale
-//     (per token and 32 dims) is folded into P, split into an fp16 high and low part so the
-//     PV product keeps fp32 accuracy;
-//   * online softmax in log2 units with wave shuffles for the row max, one partial
-//     (acc, max, sum) per split in the workspace, then a second kernel merges them.
+//   * one workgroup of 4 waves per piece of a (sequence, KV head) context; each wave streams
+//     32-token blocks through three LDS stage buffers with direct-to-LDS 16-byte loads, so two
+//     blocks are in flight while it computes one;
+//   * Q K^T runs on the int8 matrix cores: the K codes of one 16-byte load per lane are the A
+//     operand of v_mfma_i32_16x16x64_i8 as they sit in the page, and each query row is split
+//     exactly into three int8 digits at a per-row power-of-two scale (B operands, query rows of
+//     the GQA group x MTP rows on N), so the dot products are exact integers;
+//   * the 16x16 logit tile comes out with each lane holding one query row and four tokens, the
+//     B-operand layout of the P V product (tokens on K), so P never leaves the registers; V codes
+//     arrive pre-arranged as the A operand of v_mfma_f32_16x16x32_f16 and are widened with
+//     exact bit tricks; the V scale (per token and 32 dims) is folded into P, split into fp16
+//     high and low parts from one single-rounding multiply so the product keeps fp32 accuracy;
+//   * online softmax in log2 units whose exponent offset only moves in powers of two when a
+//     block needs it, so most blocks rescale nothing;
+//   * the waves merge through LDS; the last workgroup of each (sequence, KV head) to finish
+//     merges the pieces' partials into the output.
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -30,32 +33,12 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_inff();
 
 __device__ inline half2v as_h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
 __device__ inline uint32_t as_u32(half2v h) { return __builtin_bit_cast(uint32_t, h); }
-
-// Four int8 codes (bytes b0..b3 of x) -> fp16 pairs (c0, c2) and (c1, c3), exact:
-// 0x6400 | u is the fp16 value 1024 + u for u < 1024, and u = c + 128 after flipping the sign bit.
-__device__ inline void i8x4_to_h2x2(uint32_t x, uint32_t& c02, uint32_t& c13) {
-  const uint32_t u = x ^ 0x80808080u;
-  const half2v off = {(_Float16)1152.0f, (_Float16)1152.0f};
-  c02 = as_u32(as_h2((u & 0x00FF00FFu) | 0x64006400u) - off);
-  c13 = as_u32(as_h2(((u >> 8) & 0x00FF00FFu) | 0x64006400u) - off);
-}
-
-// 16 int8 codes of one token (one 16-byte load) -> the two 8-wide MFMA operands.  Element order
-// within each operand is dims [0,2,1,3,4,6,5,7] (+8 for the second); Q is permuted to match.
-__device__ inline void k_operands(const u32x4 raw, half8& lo, half8& hi) {
-  uint32_t a0, a1, b0, b1, c0, c1, d0, d1;
-  i8x4_to_h2x2(raw[0], a0, a1);
-  i8x4_to_h2x2(raw[1], b0, b1);
-  i8x4_to_h2x2(raw[2], c0, c1);
-  i8x4_to_h2x2(raw[3], d0, d1);
-  lo = __builtin_bit_cast(half8, u32x4{a0, a1, b0, b1});
-  hi = __builtin_bit_cast(half8, u32x4{c0, c1, d0, d1});
-}
 
 // One V dword holds, for four tokens r = 0..3 (byte r), the codes of two dims (low nibble: a
 // dim of the even 16-dim block, high nibble: the same dim of the odd block), 4-bit two's
@@ -64,13 +47,14 @@ __device__ inline void i4x8_to_h2x4(uint32_t x, uint32_t& lo02, uint32_t& lo13, 
                                     uint32_t& hi13) {
   const uint32_t u = x ^ 0x88888888u;  // nibble n' = code + 8 in [0, 15]
   const uint32_t u8 = u >> 8;
-  const half2v off_lo = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const half2v off_lo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
   const half2v sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-  const half2v off_hi = {(_Float16)72.0f, (_Float16)72.0f};
-  lo02 = as_u32(as_h2((u & 0x000F000Fu) | 0x64006400u) - off_lo);           // 1024 + n' - 1032
-  lo13 = as_u32(as_h2((u8 & 0x000F000Fu) | 0x64006400u) - off_lo);
-  hi02 = as_u32(as_h2((u & 0x00F000F0u) | 0x64006400u) * sixteenth - off_hi);  // (1024+16n')/16 - 72
-  hi13 = as_u32(as_h2((u8 & 0x00F000F0u) | 0x64006400u) * sixteenth - off_hi);
+  const half2v off_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
+  // 0x6400 | n' is the fp16 value 1024 + n'; 0x6400 | 16 n' is 1024 + 16 n'
+  lo02 = as_u32(as_h2(((u & 0x000F000Fu) | 0x64006400u)) + off_lo);
+  lo13 = as_u32(as_h2((u8 & 0x000F000Fu) | 0x64006400u) + off_lo);
+  hi02 = as_u32(__builtin_elementwise_fma(as_h2((u & 0x00F000F0u) | 0x64006400u), sixteenth, off_hi));
+  hi13 = as_u32(__builtin_elementwise_fma(as_h2((u8 & 0x00F000F0u) | 0x64006400u), sixteenth, off_hi));
 }
 
 // Two fp32 values as fp16 pairs hi + lo with hi + lo = x to about 2^-21 relative.  hi comes from
@@ -84,6 +68,38 @@ __device__ inline void split_hi_lo(float x0, float x1, uint32_t& hi, uint32_t& l
   const float r0 = x0 - (float)h[0];
   const float r1 = x1 - (float)h[1];
   lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+}
+
+// p0 * s0 and p1 * s1 (p fp32, s an fp16 half of sw0 / sw1 selected by SH) as fp16 hi + lo pairs:
+// hi = rne(p * s) and lo = rne(p * s - hi) straight from the exact products (v_fma_mix*), so the
+// two halves always belong together and hi + lo = p * s to about 2^-22.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <int SH>
+__device__ inline void mix_hi_lo(float p0, uint32_t sw0, float p1, uint32_t sw1, uint32_t& hi,
+                                 uint32_t& lo) {
+  uint32_t h = 0, l = 0;
+  if constexpr (SH == 0) {
+    asm volatile("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel:[0,0,0] op_sel_hi:[0,1,0]" : "+v"(h) : "v"(p0), "v"(sw0));
+    asm volatile("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[0,0,0] op_sel_hi:[0,1,0]" : "+v"(h) : "v"(p1), "v"(sw1));
+    asm volatile("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel:[0,0,0] op_sel_hi:[0,1,1]" : "+v"(l) : "v"(p0), "v"(sw0), "v"(h));
+    asm volatile("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,1,1]" : "+v"(l) : "v"(p1), "v"(sw1), "v"(h));
+  } else {
+    asm volatile("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "+v"(h) : "v"(p0), "v"(sw0));
+    asm volatile("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "+v"(h) : "v"(p1), "v"(sw1));
+    asm volatile("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel:[0,1,0] op_sel_hi:[0,1,1]" : "+v"(l) : "v"(p0), "v"(sw0), "v"(h));
+    asm volatile("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,1,1] op_sel_hi:[0,1,1]" : "+v"(l) : "v"(p1), "v"(sw1), "v"(h));
+  }
+  hi = h;
+  lo = l;
+}
+#pragma clang diagnostic pop
+
+__device__ inline void store_agent(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint64_t load_agent(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ inline float h_at(const uint32_t* words, int idx) {
@@ -119,22 +135,28 @@ struct Stage {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// M0 is named as clobbered below: these kernels set it themselves before each direct-to-LDS
-// load and use it for nothing else, so the compiler's warning about reserved registers is moot.
+// M0 is named as clobbered below: these kernels set it themselves before each group of
+// direct-to-LDS loads and use it for nothing else, so the compiler's warning is moot.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ inline void dma16(const uint8_t* src, uint8_t* lds_dst) {
-  // 16 bytes per active lane from src to lds_dst + 16 * lane_id (gfx950 global_load_lds_dwordx4).
-  // Issued as inline asm: the waits for these loads are this file's explicit s_waitcnt vmcnt,
-  // which keep two blocks in flight (the compiler would otherwise drain every load before each
-  // LDS read).  The "memory" clobber keeps LDS reads of the buffer on their side of it.
-  const uint32_t lds = (uint32_t)(uintptr_t)(lds_void*)lds_dst;
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :
-      : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds))
-      : "memory", "m0");
+// N x 16 bytes per active lane: load i moves src + 1024 i + 16 lane to lds_dst + 1024 i + 16 lane
+// (gfx950 global_load_lds_dwordx4; the immediate offset applies to both addresses).  Issued as
+// inline asm: the waits for these loads are this file's explicit s_waitcnt vmcnt, which keep two
+// blocks in flight (the compiler would otherwise drain every load before each LDS read).  The
+// "memory" clobber keeps LDS reads of the buffer on their side of it.
+template <int N>
+__device__ inline void dma16(const uint8_t* src, uint32_t lds) {
+  static_assert(N >= 1 && N <= 4, "immediate offsets up to 3072");
+  if constexpr (N == 1)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+  else if constexpr (N == 2)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off\n\t"
+                 "global_load_lds_dwordx4 %0, off offset:1024" ::"v"(src), "s"(lds) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off\n\t"
+                 "global_load_lds_dwordx4 %0, off offset:1024\n\t"
+                 "global_load_lds_dwordx4 %0, off offset:2048\n\t"
+                 "global_load_lds_dwordx4 %0, off offset:3072" ::"v"(src), "s"(lds) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -144,23 +166,22 @@ __device__ inline void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Issue the loads of one tile (slot0 = first slot of the tile in its page) into LDS.
+// Issue the loads of one tile (slot0 = first slot of the tile in its page) into LDS at byte
+// address dst (wave-uniform).
 template <int D>
-__device__ inline void stage_tile(const uint8_t* base, int P, int slot0, uint8_t* dst, int lane) {
+__device__ inline void stage_tile(const uint8_t* base, int P, int slot0, uint32_t dst, int lane) {
+  static_assert(D == 64 || D == 128 || D == 256, "head_dim");
   const int tip = slot0 / kTile;
-#pragma unroll
-  for (int jj = 0; jj < D / 64; ++jj)
-    dma16(base + (size_t)16 * D * tip + 1024 * jj + 16 * lane, dst + Stage<D>::kK + 1024 * jj);
+  dma16<D / 64>(base + (size_t)16 * D * tip + 16 * lane, dst + Stage<D>::kK);
   const uint8_t* vb = base + v_codes_at(P, D) + (size_t)8 * D * tip;
   if constexpr (D >= 128) {
-#pragma unroll
-    for (int c = 0; c < D / 128; ++c) dma16(vb + 1024 * c + 16 * lane, dst + Stage<D>::kV + 1024 * c);
+    dma16<D / 128>(vb + 16 * lane, dst + Stage<D>::kV);
   } else {
-    if (lane < 32) dma16(vb + 16 * lane, dst + Stage<D>::kV);
+    if (lane < 32) dma16<1>(vb + 16 * lane, dst + Stage<D>::kV);
   }
   if (lane < D / 16)
-    dma16(base + v_scales_at(P, D) + (size_t)2 * slot0 * (D / 32) + 16 * lane, dst + Stage<D>::kVs);
-  if (lane < 2) dma16(base + k_scales_at(P, D) + 2 * slot0 + 16 * lane, dst + Stage<D>::kKs);
+    dma16<1>(base + v_scales_at(P, D) + (size_t)2 * slot0 * (D / 32) + 16 * lane, dst + Stage<D>::kVs);
+  if (lane < 2) dma16<1>(base + k_scales_at(P, D) + 2 * slot0 + 16 * lane, dst + Stage<D>::kKs);
 }
 
 // Read one staged tile into this lane's registers (the lane's share of every section).
@@ -194,42 +215,44 @@ __device__ inline void read_tile(TileRaw<D>& r, const uint8_t* src, int lane) {
 }
 
 // One 32-token block of one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
-// Running state of one wave, per query row (lane's row in each 16-row block nb):
-//   m_run  the largest logit seen (log2 units), -inf before any unmasked token;
-//   base   the exponent offset of l_run and acc: they hold sums of 2^(z - base) * (...);
-//   base = m_run - k, where 2^k is a per-block power of two that keeps p * v_scale near the top of
-//   the fp16 range, so the fp16 high and low parts of P both stay normal numbers.
+// Running state of one wave, per query row (the lane's row in each 16-row block nb):
+//   base   integer exponent offset (or -inf before any unmasked token): l_run and acc hold
+//          sums of 2^(z - base) * (1, v);  it only moves up, in whole powers of two, when a block's
+//          largest logit and V scale would push p * v_scale past 2^15 (fp16 headroom), so most
+//          blocks rescale nothing and every rescale is exact.
 template <int D, int NB, bool MASK>
 __device__ __attribute__((always_inline)) inline void process_block(
-    const TileRaw<D> (&raw)[2], int blk, const half8 (&qop)[NB][D / 32], const int (&last_tok)[NB],
-    float scale_log2, int g, floatx4 (&acc)[NB][D / 16], float (&m_run)[NB], float (&base)[NB],
+    const TileRaw<D> (&raw)[2], int blk, const i32x4 (&qd)[NB][3][D / 64], const float (&cz)[NB],
+    const int (&last_tok)[NB], int g, floatx4 (&acc)[NB][D / 16], float (&base)[NB],
     float (&l_run)[NB]) {
   constexpr int DB = D / 16;
   constexpr int NG = D / 32;
-  // ---- logits: lane gets row (16nb + m16) and tokens 4g..4g+3 of each tile ----
-  floatx4 s[2][NB];
+  // ---- S^T = K Q^T on the int8 matrix cores, three digit planes of Q ----
+  i32x4 sd[2][NB][3];
 #pragma unroll
-  for (int tau = 0; tau < 2; ++tau) {
+  for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) s[tau][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int jj = 0; jj < D / 64; ++jj) {
-      half8 klo, khi;
-      k_operands(raw[tau].k[jj], klo, khi);
+      for (int pc = 0; pc < 3; ++pc) sd[tau][nb][pc] = i32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        s[tau][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(klo, qop[nb][2 * jj], s[tau][nb], 0, 0, 0);
-        s[tau][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(khi, qop[nb][2 * jj + 1], s[tau][nb], 0, 0, 0);
-      }
+  for (int jj = 0; jj < D / 64; ++jj)
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      const i32x4 ka = __builtin_bit_cast(i32x4, raw[tau].k[jj]);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int pc = 0; pc < 3; ++pc)
+          sd[tau][nb][pc] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka, qd[nb][pc][jj], sd[tau][nb][pc], 0, 0, 0);
     }
-  }
   float ks[2][4];
 #pragma unroll
   for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ks[tau][e] = h_at(raw[tau].ks, e) * scale_log2;
+    for (int e = 0; e < 4; ++e) ks[tau][e] = h_at(raw[tau].ks, e);
 
-  // ---- exponent of the block's largest V scale: k = 29 - e5 keeps p' * scale < 2^15 ----
+  // ---- exponent of the block's largest V scale (positive fp16: bit order is value order) ----
   typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
   u16x2 vmax = {0, 0};
 #pragma unroll
@@ -237,13 +260,15 @@ __device__ __attribute__((always_inline)) inline void process_block(
 #pragma unroll
     for (int c = 0; c < TileRaw<D>::kVsWords; ++c)
       vmax = __builtin_elementwise_max(vmax, __builtin_bit_cast(u16x2, raw[tau].vs[c]));
-  int smax = max((int)vmax[0], (int)vmax[1]);  // positive fp16: bit order is value order
+  int smax = max((int)vmax[0], (int)vmax[1]);
   smax = max(smax, __shfl_xor(smax, 16, kWave));
   smax = max(smax, __shfl_xor(smax, 32, kWave));
-  const float kshift = (float)(29 - ((smax >> 10) & 31));
+  const float e5 = (float)((smax >> 10) & 31);  // scales < 2^(e5 - 14)
 
-  // ---- online softmax in log2 units ----
+  // ---- logits and the online softmax (log2 units) ----
   float pexp[NB][2][4];
+  bool rescale = false;
+  float alpha[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     float z[2][4];
@@ -252,7 +277,9 @@ __device__ __attribute__((always_inline)) inline void process_block(
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float zz = s[tau][nb][e] * ks[tau][e];
+        const int hm = (sd[tau][nb][0][e] << 8) + sd[tau][nb][1][e];  // |.| < 2^30: exact
+        const float sc = __builtin_fmaf((float)hm, 256.0f, (float)sd[tau][nb][2][e]);
+        float zz = sc * (ks[tau][e] * cz[nb]);
         if (MASK) {
           const int t = blk * kBlock + kTile * tau + 4 * g + e;
           zz = (t <= last_tok[nb]) ? zz : kNegInf;
@@ -262,23 +289,34 @@ __device__ __attribute__((always_inline)) inline void process_block(
       }
     bm = fmaxf(bm, __shfl_xor(bm, 16, kWave));
     bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
-    const float m_new = fmaxf(m_run[nb], bm);
-    // empty so far: keep the state at zero (alpha = 0 scales nothing, every p is 0)
-    const float b_new = (m_new == kNegInf) ? 0.0f : m_new - kshift;
-    const float alpha = __builtin_amdgcn_exp2f(base[nb] - b_new);
-    m_run[nb] = m_new;
-    base[nb] = (m_new == kNegInf) ? kNegInf : b_new;
+    // p * v_scale < 2^(bm - base + e5 - 14) must stay below 2^15
+    const float need = bm + (e5 - 29.0f);
+    float b_new = base[nb];
+    alpha[nb] = 1.0f;
+    if (need > b_new) {
+      b_new = __builtin_ceilf(need) + 2.0f;  // two powers of two of headroom for later blocks
+      if (base[nb] != kNegInf) {
+        alpha[nb] = __builtin_ldexpf(1.0f, (int)(base[nb] - b_new));
+        rescale = true;
+      }
+      base[nb] = b_new;
+    }
+    const float b_use = (b_new == kNegInf) ? 0.0f : b_new;
     float lsum = 0.0f;
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        pexp[nb][tau][e] = __builtin_amdgcn_exp2f(z[tau][e] - b_new);
+        pexp[nb][tau][e] = __builtin_amdgcn_exp2f(z[tau][e] - b_use);
         lsum += pexp[nb][tau][e];
       }
-    l_run[nb] = l_run[nb] * alpha + lsum;
+    l_run[nb] = l_run[nb] * alpha[nb] + lsum;
+  }
+  if (__any(rescale)) {  // rare: a larger logit or V scale than this wave has seen
 #pragma unroll
-    for (int db = 0; db < DB; ++db) acc[nb][db] *= alpha;
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[nb][db] *= alpha[nb];
   }
 
   // ---- O^T += V^T P^T, one 32-dim scale group at a time ----
@@ -291,20 +329,34 @@ __device__ __attribute__((always_inline)) inline void process_block(
     const half8 vhi = __builtin_bit_cast(half8, u32x4{h02[0], h13[0], h02[1], h13[1]});
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      // token order of the operand: (tau0: 0,2,1,3), (tau1: 0,2,1,3)
-      float px[2][4];
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          px[tau][e] = pexp[nb][tau][e] * h_at(raw[tau].vs, e * NG + j);
-          if (MASK) px[tau][e] = (pexp[nb][tau][e] == 0.0f) ? 0.0f : px[tau][e];  // junk scale of a masked slot
-        }
+      // token order of the operand: (tau0: 0,2,1,3), (tau1: 0,2,1,3); the scale of token e, group
+      // j is fp16 half (j & 1) of word (e * NG + j) / 2
       uint32_t hw[4], lw[4];
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
-        split_hi_lo(px[tau][0], px[tau][2], hw[2 * tau], lw[2 * tau]);
-        split_hi_lo(px[tau][1], px[tau][3], hw[2 * tau + 1], lw[2 * tau + 1]);
+        if (MASK) {  // a masked slot's scale may be junk: multiply in fp32 and select
+          float px[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            px[e] = pexp[nb][tau][e] * h_at(raw[tau].vs, e * NG + j);
+            px[e] = (pexp[nb][tau][e] == 0.0f) ? 0.0f : px[e];
+          }
+          split_hi_lo(px[0], px[2], hw[2 * tau], lw[2 * tau]);
+          split_hi_lo(px[1], px[3], hw[2 * tau + 1], lw[2 * tau + 1]);
+        } else {
+          const uint32_t* vs = raw[tau].vs;
+          if (j & 1) {  // resolved at compile time once the group loop is unrolled
+            mix_hi_lo<1>(pexp[nb][tau][0], vs[(0 * NG + j) / 2], pexp[nb][tau][2], vs[(2 * NG + j) / 2],
+                         hw[2 * tau], lw[2 * tau]);
+            mix_hi_lo<1>(pexp[nb][tau][1], vs[(1 * NG + j) / 2], pexp[nb][tau][3], vs[(3 * NG + j) / 2],
+                         hw[2 * tau + 1], lw[2 * tau + 1]);
+          } else {
+            mix_hi_lo<0>(pexp[nb][tau][0], vs[(0 * NG + j) / 2], pexp[nb][tau][2], vs[(2 * NG + j) / 2],
+                         hw[2 * tau], lw[2 * tau]);
+            mix_hi_lo<0>(pexp[nb][tau][1], vs[(1 * NG + j) / 2], pexp[nb][tau][3], vs[(3 * NG + j) / 2],
+                         hw[2 * tau + 1], lw[2 * tau + 1]);
+          }
+        }
       }
       const half8 phi = __builtin_bit_cast(half8, u32x4{hw[0], hw[1], hw[2], hw[3]});
       const half8 plo = __builtin_bit_cast(half8, u32x4{lw[0], lw[1], lw[2], lw[3]});
@@ -322,7 +374,6 @@ __device__ __attribute__((always_inline)) inline void process_block(
 // partial; the last workgroup of a unit to finish merges the unit's partials into the output.
 template <int D, int NB>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
-  constexpr int KK = D / 32;
   constexpr int DB = D / 16;
   constexpr int ROWS = 16 * NB;
   constexpr int LDS_STRIDE = D + 4;  // floats; padding spreads the 16 rows over banks
@@ -362,8 +413,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const uint8_t* pool_h = a.pool + (size_t)h * bb;
   const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
 
-  // ---- Q^T operands (B of QK^T): lane holds query row 16*nb + m16, dims of lane group g ----
-  half8 qop[NB][KK];
+  // ---- Q^T as three int8 digit planes (B of QK^T): lane holds query row 16*nb + m16 and the
+  // 16 dims 16*(4*jj + g) .. +15 of each 64-dim step jj.  q * 2^F = h*2^16 + m*2^8 + l with
+  // |q * 2^F| < 2^22 for the row's largest |q|; exact for every element within 2^12 of it.
+  i32x4 qd[NB][3][D / 64];
+  float cz[NB];  // 2^-F * softmax_scale * log2(e)
   int last_tok[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -373,37 +427,76 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int hq = h * a.group + (real ? n % a.group : 0);
     last_tok[nb] = min(real ? L - a.n_rows + i : L - 1, Lc - 1);  // padding rows: q = 0
     const uint16_t* qrow = a.q + (((size_t)b * a.n_rows + i) * a.n_q_heads + hq) * D;
+    float qf[D / 64][16];
+    float amax = 0.0f;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const int dim0 = 16 * (4 * (kk / 2) + g) + 8 * (kk % 2);
-      u32x4 q8 = real ? *(const u32x4*)(qrow + dim0) : u32x4{0, 0, 0, 0};
-      // dims [0..7] -> operand order [0,2,1,3,4,6,5,7]: swap halves 1<->2 and 5<->6
-      const uint32_t p0 = (q8[0] & 0xFFFFu) | (q8[1] << 16);
-      const uint32_t p1 = (q8[0] >> 16) | (q8[1] & 0xFFFF0000u);
-      const uint32_t p2 = (q8[2] & 0xFFFFu) | (q8[3] << 16);
-      const uint32_t p3 = (q8[2] >> 16) | (q8[3] & 0xFFFF0000u);
-      qop[nb][kk] = __builtin_bit_cast(half8, u32x4{p0, p1, p2, p3});
+    for (int jj = 0; jj < D / 64; ++jj) {
+      const int dim0 = 16 * (4 * jj + g);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const u32x4 w8 = real ? *(const u32x4*)(qrow + dim0 + 8 * hf) : u32x4{0, 0, 0, 0};
+        const half8 h8 = __builtin_bit_cast(half8, w8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          qf[jj][8 * hf + e] = (float)h8[e];
+          amax = fmaxf(amax, fabsf(qf[jj][8 * hf + e]));
+        }
+      }
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+    int E = 0;
+    if (amax > 0.0f) (void)__builtin_frexpf(amax, &E);  // amax < 2^E
+    const int F = amax > 0.0f ? 22 - E : 0;
+    cz[nb] = __builtin_ldexpf(a.scale_log2, -F);
+#pragma unroll
+    for (int jj = 0; jj < D / 64; ++jj) {
+      uint32_t wd[3][4];
+#pragma unroll
+      for (int w4 = 0; w4 < 4; ++w4) {
+        uint32_t bh = 0, bmid = 0, bl = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int qi = (int)__builtin_rintf(__builtin_ldexpf(qf[jj][4 * w4 + e], F));
+          const int dl = ((qi + 128) & 255) - 128;
+          const int r1 = (qi - dl) >> 8;
+          const int dm = ((r1 + 128) & 255) - 128;
+          const int dh = (r1 - dm) >> 8;
+          bh |= (uint32_t)(dh & 255) << (8 * e);
+          bmid |= (uint32_t)(dm & 255) << (8 * e);
+          bl |= (uint32_t)(dl & 255) << (8 * e);
+        }
+        wd[0][w4] = bh;
+        wd[1][w4] = bmid;
+        wd[2][w4] = bl;
+      }
+#pragma unroll
+      for (int pc = 0; pc < 3; ++pc)
+        qd[nb][pc][jj] = __builtin_bit_cast(i32x4, u32x4{wd[pc][0], wd[pc][1], wd[pc][2], wd[pc][3]});
     }
   }
   // first token that some row may mask (causal MTP rows, the ragged end, max_seq_len)
   const int mask_from = min(L - a.n_rows + 1, Lc);
 
   floatx4 acc[NB][DB];
-  float m_run[NB], base[NB], l_run[NB];
+  float base[NB], l_run[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[nb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
-    m_run[nb] = kNegInf;
     base[nb] = kNegInf;
     l_run[nb] = 0.0f;
   }
 
-  uint8_t* my_stage = &s_stage[w][0][0];
+  // LDS byte address of this wave's stage buffers (wave-uniform, computed once)
+  const uint32_t my_stage_lds =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)&s_stage[w][0][0]);
+  const uint8_t* my_stage = &s_stage[w][0][0];
+  const int lgP = a.log2_page;
   for (int c0 = g_blk0; c0 < g_blk1; c0 += CHUNK) {
     const int c1 = min(c0 + CHUNK, g_blk1);
-    const int lp0 = (c0 * kBlock) / P;
-    const int lp1 = (c1 * kBlock - 1) / P + 1;
+    const int lp0 = (c0 * kBlock) >> lgP;
+    const int lp1 = ((c1 * kBlock - 1) >> lgP) + 1;
     __syncthreads();  // the previous chunk's page ids are no longer read
     for (int e = threadIdx.x; e < lp1 - lp0; e += blockDim.x)
       s_pt[e] = min(max(pt[lp0 + e], 0), a.num_pages - 1);
@@ -413,13 +506,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int n_my = first < c1 ? (c1 - first + kWavesPerGroup - 1) / kWavesPerGroup : 0;
     auto issue = [&](int k) {
       const int blk = first + kWavesPerGroup * k;
-      uint8_t* dst = my_stage + (k % NSTAGE) * BS;
+      const uint32_t dst = my_stage_lds + (uint32_t)((k % NSTAGE) * BS);
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
         int tok0 = blk * kBlock + kTile * tau;
         if (tok0 >= Lc) tok0 = blk * kBlock;  // tile past the end: stage tile 0 again, all masked
-        const int phys = s_pt[tok0 / P - lp0];
-        stage_tile<D>(pool_h + (size_t)phys * page_stride, P, tok0 % P, dst + tau * Stage<D>::kTileBytes, lane);
+        const int phys = __builtin_amdgcn_readfirstlane(s_pt[(tok0 >> lgP) - lp0]);
+        stage_tile<D>(pool_h + (size_t)phys * page_stride, P, tok0 & (P - 1),
+                      dst + (uint32_t)(tau * Stage<D>::kTileBytes), lane);
       }
     };
     if (n_my > 0) issue(0);
@@ -442,9 +536,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       read_tile<D>(raw[1], src + Stage<D>::kTileBytes, lane);
       const int blk = first + kWavesPerGroup * k;
       if (blk * kBlock + kBlock - 1 >= mask_from)
-        process_block<D, NB, true>(raw, blk, qop, last_tok, a.scale_log2, g, acc, m_run, base, l_run);
+        process_block<D, NB, true>(raw, blk, qd, cz, last_tok, g, acc, base, l_run);
       else
-        process_block<D, NB, false>(raw, blk, qop, last_tok, a.scale_log2, g, acc, m_run, base, l_run);
+        process_block<D, NB, false>(raw, blk, qd, cz, last_tok, g, acc, base, l_run);
     }
   }
   __syncthreads();  // every wave is done with its stage buffers (reused below for the merge)
@@ -496,27 +590,37 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     }
     __syncthreads();
   }
+  // The partial goes out with agent-scope stores (write-through to the level every XCD sees), and
+  // the last workgroup reads the partials back with agent-scope loads; that pairing makes them
+  // visible across XCDs without a cache-wide write-back or invalidate.
   if (w == 0) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int n = 16 * nb + m16;
       if (n < a.rows) {
         const size_t prow = ((size_t)unit * a.splits + split) * a.rows + n;
-        float* dst = a.ws_acc + prow * D + 4 * g;
+        uint64_t* dst = (uint64_t*)(a.ws_acc + prow * D + 4 * g);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) *(floatx4*)(dst + 16 * db) = acc[nb][db];
-        if (g == 0) a.ws_ml[prow] = make_float2(M[nb], l_tot[nb]);
+        for (int db = 0; db < DB; ++db) {
+          const u32x4 bits = __builtin_bit_cast(u32x4, acc[nb][db]);
+          store_agent(dst + 8 * db, bits[0] | ((uint64_t)bits[1] << 32));
+          store_agent(dst + 8 * db + 1, bits[2] | ((uint64_t)bits[3] << 32));
+        }
+        if (g == 0)
+          store_agent((uint64_t*)(a.ws_ml + prow), __builtin_bit_cast(uint32_t, M[nb]) |
+                                                        ((uint64_t)__builtin_bit_cast(uint32_t, l_tot[nb]) << 32));
       }
     }
   }
 
   // ---- the last workgroup of this unit merges every split ----
-  __threadfence();  // release: this workgroup's partial is visible to all XCDs
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's partial stores are complete
   __syncthreads();
-  if (threadIdx.x == 0) s_last = (atomicAdd(&a.ws_count[unit], 1u) == (unsigned)(a.splits - 1));
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(&a.ws_count[unit], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (unsigned)(a.splits - 1);
   __syncthreads();
   if (!s_last) return;
-  __threadfence();  // acquire: every other workgroup's partial
   {
     // (max, sum) of every (split, row) into LDS, then per-row max M, weights 2^(m - M) and the
     // denominator; then the numerators in batches of independent loads.
@@ -527,7 +631,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     float2* s_ml = (float2*)&s_stage[0][0][0];  // [S][R]
     float* s_M = (float*)(s_ml + S * R);          // [R]: 1/den
     floatx4* s_red = (floatx4*)(s_lds + ((S * R * 8 + R * 4 + 15) & ~15));  // [PARTS][4][NQ]
-    for (int e = threadIdx.x; e < S * R; e += blockDim.x) s_ml[e] = a.ws_ml[p0 + e];
+    for (int e = threadIdx.x; e < S * R; e += blockDim.x)
+      s_ml[e] = __builtin_bit_cast(float2, load_agent((const uint64_t*)(a.ws_ml + p0 + e)));
     __syncthreads();
     for (int n = w; n < R; n += kWavesPerGroup) {
       float mx = kNegInf;
@@ -557,18 +662,29 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     for (int n0 = 0; n0 < R; n0 += 4) {
       floatx4 num[4] = {};
       for (int sp0 = part; sp0 < S; sp0 += 8 * PARTS) {
+        // every load is unconditional (indices clamped into range, weight 0 outside), so all 64
+        // of them are in flight at once instead of one round trip each
+        uint64_t v[8][4][2];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int sp = sp0 + u * PARTS;
+        for (int u = 0; u < 8; ++u)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int n = n0 + r;
-            if (sp < S && n < R) {
-              const float wgt = s_ml[sp * R + n].x;
-              num[r] += wgt * *(const floatx4*)(a.ws_acc + (p0 + (size_t)sp * R + n) * D + 4 * q);
-            }
+            const int sp = min(sp0 + u * PARTS, S - 1), n = min(n0 + r, R - 1);
+            const uint64_t* src = (const uint64_t*)(a.ws_acc + (p0 + (size_t)sp * R + n) * D + 4 * q);
+            v[u][r][0] = load_agent(src);
+            v[u][r][1] = load_agent(src + 1);
           }
-        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int sp = sp0 + u * PARTS, n = n0 + r;
+            const float wgt = (sp < S && n < R) ? s_ml[sp * R + n].x : 0.0f;
+            num[r] += wgt * floatx4{__builtin_bit_cast(float, (uint32_t)v[u][r][0]),
+                                    __builtin_bit_cast(float, (uint32_t)(v[u][r][0] >> 32)),
+                                    __builtin_bit_cast(float, (uint32_t)v[u][r][1]),
+                                    __builtin_bit_cast(float, (uint32_t)(v[u][r][1] >> 32))};
+          }
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) s_red[(part * 4 + r) * NQ + q] = num[r];
@@ -586,7 +702,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       __syncthreads();
     }
   }
-  if (threadIdx.x == 0) atomicExch(&a.ws_count[unit], 0u);  // leave the counter zeroed
+  if (threadIdx.x == 0)  // leave the counter zeroed for the next call
+    __hip_atomic_store(&a.ws_count[unit], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int D>

@@ -37,6 +37,7 @@ struct AppendArgs {
 struct DecodeArgs {
   const uint8_t* pool;
   int num_pages, page_size, num_kv_heads;
+  int log2_page;  // page_size = 1 << log2_page
   const uint16_t* q;
   const int32_t* page_table;
   const int32_t* seq_lens;
