@@ -30,7 +30,6 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth, 8 TB/s
-PMC_FILE = os.path.join(ROOT, "profiles", "decode_ctx184k_c2_pmc.json")
 
 
 def log(*a):
@@ -85,6 +84,48 @@ def cpu_baseline(wl, inp):
     return dt, oracle.num_threads()
 
 
+def _counter_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def ingest_pmc(fetch_csv, write_csv, workload, probe_mib, commands):
+    """Per-launch HBM traffic of the decode kernel from two rocprofv3 --pmc runs (FETCH_SIZE,
+    WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for a plain device
+    copy of probe_mib MiB (the largest copyBuffer dispatches of the run)."""
+    probe_kib = probe_mib * 1024.0
+    out = {"workload": workload, "source_hash": source_hash(), "copy_probe_mib": probe_mib,
+           "commands": commands}
+    for key, path in (("fetch", fetch_csv), ("write", write_csv)):
+        rows = _counter_rows(path)
+        dec = [float(r["Counter_Value"]) for r in rows if "decode_kernel" in r["Kernel_Name"]]
+        cps = sorted(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
+        probe = cps[-1]  # the probe copies are the largest copies of the run
+        out[f"{key}_kib_per_dispatch"] = round(sum(dec) / len(dec), 1)
+        out[f"{key}_copy_probe_kib"] = probe
+        out[f"{key}_scale"] = round(probe_kib / probe, 4)
+        out[f"{key}_dispatches"] = len(dec)
+    out["hbm_bytes_per_launch"] = int(1024 * (out["fetch_kib_per_dispatch"] * out["fetch_scale"] +
+                                              out["write_kib_per_dispatch"] * out["write_scale"]))
+    return out
+
+
+def ingest_trace(stats_csv, command):
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run."""
+    rows = _counter_rows(stats_csv)
+    lines = ["# Kernel trace summary", "", "Command:", "", "```", command, "```", "",
+             "| kernel | calls | average us | min us | max us | % of GPU time |",
+             "|---|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        name = r["Name"]
+        short = name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+        lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    return "\n".join(lines) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -96,7 +137,29 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the per-launch HBM traffic of rocprofv3 counter CSVs to profiles/")
+    ap.add_argument("--ingest-trace", metavar="KERNEL_STATS_CSV",
+                    help="write a markdown summary of a rocprofv3 kernel-stats CSV to profiles/")
+    ap.add_argument("--command", default="", help="command line recorded with an ingested profile")
     args = ap.parse_args(argv)
+
+    if args.ingest_pmc or args.ingest_trace:
+        from long_context_decode_flash_amd import workloads as W
+        name = args.workload or W.HEADLINE
+        os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+        if args.ingest_pmc:
+            res = ingest_pmc(*args.ingest_pmc, name, args.copy_probe_mib or 1024,
+                             args.command.split(" ;; ") if args.command else [])
+            path = os.path.join(ROOT, "profiles", f"decode_{name}_pmc.json")
+            with open(path, "w") as f:
+                json.dump(res, f, indent=1)
+        else:
+            path = os.path.join(ROOT, "profiles", f"decode_{name}_kernel_trace.md")
+            with open(path, "w") as f:
+                f.write(ingest_trace(args.ingest_trace, args.command))
+        print(path)
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
@@ -192,8 +255,9 @@ def main(argv=None):
     achieved = dec_bytes / dec_mean_s / 1e9
 
     traffic = None
-    if os.path.exists(PMC_FILE):
-        with open(PMC_FILE) as f:
+    pmc_file = os.path.join(ROOT, "profiles", f"decode_{name}_pmc.json")
+    if os.path.exists(pmc_file):
+        with open(pmc_file) as f:
             pmc = json.load(f)
         if pmc.get("source_hash") == source_hash() and pmc.get("workload") == name:
             traffic = pmc.get("hbm_bytes_per_launch")
@@ -237,7 +301,7 @@ def main(argv=None):
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "kvq_decode_attn (split-KV partial kernel + LSE merge kernel)",
+            "kernel": "decode_kernel (kvq_decode_attn: split-KV attention + fused LSE merge, one launch)",
             "algorithmic_bytes_per_launch": dec_bytes,
             "launch_us_mean": round(dec_mean_s * 1e6, 2),
             "launch_us_median": round(float(np.median(decode_ms)) * 1e3, 2),

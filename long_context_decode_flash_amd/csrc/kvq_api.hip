@@ -61,6 +61,9 @@ int pool_args_ok(const void* pool, int32_t num_pages, int32_t page_size, int32_t
   if (!pool || num_pages <= 0 || num_kv_heads <= 0 || page_size <= 0) return KVQ_ERR_ARG;
   if (!head_dim_ok(head_dim) || !pow2_in(page_size, 16, 256)) return KVQ_ERR_UNSUPPORTED;
   if (((uintptr_t)pool & 15) != 0) return KVQ_ERR_ARG;
+  // one page of all KV heads stays below 4 GiB (the kernels address within it in 32 bits)
+  if ((unsigned long long)num_kv_heads * kvq::block_bytes(page_size, head_dim) >= (1ULL << 32))
+    return KVQ_ERR_UNSUPPORTED;
   return KVQ_OK;
 }
 

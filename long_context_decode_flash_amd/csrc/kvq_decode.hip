@@ -45,29 +45,17 @@ __device__ inline uint32_t as_u32(half2v h) { return __builtin_bit_cast(uint32_t
 // complement.  Returns fp16 pairs (token 0, token 2) and (token 1, token 3) for both dims.
 __device__ inline void i4x8_to_h2x4(uint32_t x, uint32_t& lo02, uint32_t& lo13, uint32_t& hi02,
                                     uint32_t& hi13) {
-  const uint32_t u = x ^ 0x88888888u;  // nibble n' = code + 8 in [0, 15]
-  const uint32_t u8 = u >> 8;
+  // nibble n (two's complement code c) xor 8 = c + 8; 0x6400 | m is the fp16 value 1024 + m, so
+  // (x & 0x000F000F) ^ 0x64086408 is 1024 + c + 8 per half (and the same with 16 (c + 8) for the
+  // high nibbles), one and-xor each
+  const uint32_t x8 = x >> 8;
   const half2v off_lo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
   const half2v sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
   const half2v off_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
-  // 0x6400 | n' is the fp16 value 1024 + n'; 0x6400 | 16 n' is 1024 + 16 n'
-  lo02 = as_u32(as_h2(((u & 0x000F000Fu) | 0x64006400u)) + off_lo);
-  lo13 = as_u32(as_h2((u8 & 0x000F000Fu) | 0x64006400u) + off_lo);
-  hi02 = as_u32(__builtin_elementwise_fma(as_h2((u & 0x00F000F0u) | 0x64006400u), sixteenth, off_hi));
-  hi13 = as_u32(__builtin_elementwise_fma(as_h2((u8 & 0x00F000F0u) | 0x64006400u), sixteenth, off_hi));
-}
-
-// Two fp32 values as fp16 pairs hi + lo with hi + lo = x to about 2^-21 relative.  hi comes from
-// one truncating conversion whose bits feed both the operand and the residual; with an ordinary
-// (half) cast the compiler may compute hi twice in different ways (e.g. once as a fused
-// multiply-convert from the exact product, once from the rounded fp32 product), and near an fp16
-// rounding boundary the two differ by an ulp, which the residual then no longer corrects.
-__device__ inline void split_hi_lo(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  const auto h = __builtin_amdgcn_cvt_pkrtz(x0, x1);
-  hi = __builtin_bit_cast(uint32_t, h);
-  const float r0 = x0 - (float)h[0];
-  const float r1 = x1 - (float)h[1];
-  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+  lo02 = as_u32(as_h2((x & 0x000F000Fu) ^ 0x64086408u) + off_lo);
+  lo13 = as_u32(as_h2((x8 & 0x000F000Fu) ^ 0x64086408u) + off_lo);
+  hi02 = as_u32(__builtin_elementwise_fma(as_h2((x & 0x00F000F0u) ^ 0x64806480u), sixteenth, off_hi));
+  hi13 = as_u32(__builtin_elementwise_fma(as_h2((x8 & 0x00F000F0u) ^ 0x64806480u), sixteenth, off_hi));
 }
 
 // p0 * s0 and p1 * s1 (p fp32, s an fp16 half of sw0 / sw1 selected by SH) as fp16 hi + lo pairs:
@@ -78,17 +66,17 @@ __device__ inline void split_hi_lo(float x0, float x1, uint32_t& hi, uint32_t& l
 template <int SH>
 __device__ inline void mix_hi_lo(float p0, uint32_t sw0, float p1, uint32_t sw1, uint32_t& hi,
                                  uint32_t& lo) {
-  uint32_t h = 0, l = 0;
+  uint32_t h, l;  // the lo-half writes declare the whole register as output; the hi-half writes keep it
   if constexpr (SH == 0) {
-    asm volatile("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel:[0,0,0] op_sel_hi:[0,1,0]" : "+v"(h) : "v"(p0), "v"(sw0));
-    asm volatile("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[0,0,0] op_sel_hi:[0,1,0]" : "+v"(h) : "v"(p1), "v"(sw1));
-    asm volatile("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel:[0,0,0] op_sel_hi:[0,1,1]" : "+v"(l) : "v"(p0), "v"(sw0), "v"(h));
-    asm volatile("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,1,1]" : "+v"(l) : "v"(p1), "v"(sw1), "v"(h));
+    asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel:[0,0,0] op_sel_hi:[0,1,0]" : "=v"(h) : "v"(p0), "v"(sw0));
+    asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[0,0,0] op_sel_hi:[0,1,0]" : "+v"(h) : "v"(p1), "v"(sw1));
+    asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel:[0,0,0] op_sel_hi:[0,1,1]" : "=&v"(l) : "v"(p0), "v"(sw0), "v"(h));
+    asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,1,1]" : "+v"(l) : "v"(p1), "v"(sw1), "v"(h));
   } else {
-    asm volatile("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "+v"(h) : "v"(p0), "v"(sw0));
-    asm volatile("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "+v"(h) : "v"(p1), "v"(sw1));
-    asm volatile("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel:[0,1,0] op_sel_hi:[0,1,1]" : "+v"(l) : "v"(p0), "v"(sw0), "v"(h));
-    asm volatile("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,1,1] op_sel_hi:[0,1,1]" : "+v"(l) : "v"(p1), "v"(sw1), "v"(h));
+    asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(h) : "v"(p0), "v"(sw0));
+    asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "+v"(h) : "v"(p1), "v"(sw1));
+    asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel:[0,1,0] op_sel_hi:[0,1,1]" : "=&v"(l) : "v"(p0), "v"(sw0), "v"(h));
+    asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,1,1] op_sel_hi:[0,1,1]" : "+v"(l) : "v"(p1), "v"(sw1), "v"(h));
   }
   hi = h;
   lo = l;
@@ -105,6 +93,42 @@ __device__ inline uint64_t load_agent(const uint64_t* p) {
 __device__ inline float h_at(const uint32_t* words, int idx) {
   const uint32_t w = words[idx >> 1];
   return (float)__builtin_bit_cast(_Float16, (uint16_t)((idx & 1) ? (w >> 16) : (w & 0xFFFF)));
+}
+
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+// max of x over the four lanes m16, m16 + 16, m16 + 32, m16 + 48 (the lanes of one query row in
+// the 16x16 matrix-core layouts), with the gfx950 cross-row swaps instead of LDS permutes.
+__device__ inline float max_over_rows(float x) {
+  // (max of two lanes' floats that are never NaN: one plain v_max_f32, without the quieting the
+  // compiler adds to fmaxf of values it cannot see)
+  auto mx = [](uint32_t p, uint32_t q) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(p), "v"(q));
+    return r;
+  };
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);  // rows (0,1), (2,3) meet
+  const uint32_t v = __builtin_bit_cast(uint32_t, mx(a[0], a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);  // halves meet
+  return mx(b[0], b[1]);
+}
+
+// Largest of the 128 fp16 halves of x over the wave (as 16-bit patterns, in both halves).
+__device__ inline uint32_t wave_max_u16x2(uint32_t x) {
+  auto mx = [](uint32_t p, uint32_t q) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, p),
+                                                                  __builtin_bit_cast(u16x2, q)));
+  };
+  x = mx(x, __builtin_amdgcn_update_dpp(0u, x, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  x = mx(x, __builtin_amdgcn_update_dpp(0u, x, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  x = mx(x, __builtin_amdgcn_update_dpp(0u, x, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  x = mx(x, __builtin_amdgcn_update_dpp(0u, x, 0x140, 0xF, 0xF, false));  // row_mirror
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = mx(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  x = mx(b[0], b[1]);
+  return mx(x, (x >> 16) | (x << 16));
 }
 
 template <int D>
@@ -129,8 +153,10 @@ struct Stage {
   static constexpr int kKs = 25 * D;
   static constexpr int kTileBytes = 25 * D + 32;
   static constexpr int kBlockBytes = 2 * kTileBytes;
-  // direct-to-LDS loads per block (vmcnt units)
-  static constexpr int kLoads = 2 * (D / 64 + (D >= 128 ? D / 128 : 1) + 2);
+  // direct-to-LDS loads per block (vmcnt units): K codes, V codes, then V and K scales in one
+  // load (they sit back to back in the stage, D/16 lanes of V scales and 2 of K scales)
+  static constexpr int kLoads = 2 * (D / 64 + (D >= 128 ? D / 128 : 1) + 1);
+  static constexpr int kScaleLanes = D / 16 + 2;
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -139,24 +165,35 @@ typedef __attribute__((address_space(3))) void lds_void;
 // direct-to-LDS loads and use it for nothing else, so the compiler's warning is moot.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-// N x 16 bytes per active lane: load i moves src + 1024 i + 16 lane to lds_dst + 1024 i + 16 lane
-// (gfx950 global_load_lds_dwordx4; the immediate offset applies to both addresses).  Issued as
-// inline asm: the waits for these loads are this file's explicit s_waitcnt vmcnt, which keep two
-// blocks in flight (the compiler would otherwise drain every load before each LDS read).  The
-// "memory" clobber keeps LDS reads of the buffer on their side of it.
-template <int N>
-__device__ inline void dma16(const uint8_t* src, uint32_t lds) {
-  static_assert(N >= 1 && N <= 4, "immediate offsets up to 3072");
-  if constexpr (N == 1)
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
-  else if constexpr (N == 2)
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off\n\t"
-                 "global_load_lds_dwordx4 %0, off offset:1024" ::"v"(src), "s"(lds) : "memory", "m0");
-  else
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off\n\t"
-                 "global_load_lds_dwordx4 %0, off offset:1024\n\t"
-                 "global_load_lds_dwordx4 %0, off offset:2048\n\t"
-                 "global_load_lds_dwordx4 %0, off offset:3072" ::"v"(src), "s"(lds) : "memory", "m0");
+// N x 16 bytes per lane: load i moves sbase + voff + 1024 i to LDS lds + 1024 i + 16 lane (gfx950
+// global_load_lds_dwordx4 with a scalar base; the immediate offset applies to both addresses, and
+// the LDS side of a lane is always 16 * lane past M0).  Issued as inline asm: the waits for these
+// loads are this file's explicit s_waitcnt vmcnt, which keep two blocks in flight (the compiler
+// would otherwise drain every load before each LDS read).  The "memory" clobber keeps LDS reads
+// of the buffer on their side of it.  M0 is written one instruction ahead of its first DMA use.
+// With LANES < 64 only lanes 0 .. LANES-1 load (exec is narrowed and restored inside).
+template <int N, int LANES = kWave>
+__device__ inline void dma16(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
+  static_assert(N >= 1 && N <= 4 && (LANES == kWave || N == 1), "shape");
+  if constexpr (LANES < kWave) {
+    uint64_t saved;
+    asm volatile("s_mov_b64 %0, exec\n\ts_bfm_b64 exec, %4, 0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %2, %1\n\ts_mov_b64 exec, %0"
+                 : "=&s"(saved) : "s"(sbase), "v"(voff), "s"(lds), "n"(LANES) : "memory", "m0");
+  } else if constexpr (N == 1) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %0"
+                 ::"s"(sbase), "v"(voff), "s"(lds) : "memory", "m0");
+  } else if constexpr (N == 2) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %0\n\t"
+                 "global_load_lds_dwordx4 %1, %0 offset:1024"
+                 ::"s"(sbase), "v"(voff), "s"(lds) : "memory", "m0");
+  } else {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %0\n\t"
+                 "global_load_lds_dwordx4 %1, %0 offset:1024\n\t"
+                 "global_load_lds_dwordx4 %1, %0 offset:2048\n\t"
+                 "global_load_lds_dwordx4 %1, %0 offset:3072"
+                 ::"s"(sbase), "v"(voff), "s"(lds) : "memory", "m0");
+  }
 }
 #pragma clang diagnostic pop
 
@@ -166,22 +203,34 @@ __device__ inline void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Issue the loads of one tile (slot0 = first slot of the tile in its page) into LDS at byte
-// address dst (wave-uniform).
+// Per-lane byte offsets, within a (page, KV head) block, of the merged scale load of a tile
+// starting at slot 0: lanes below D/16 take 16 bytes each of the V scales, the next two the K
+// scales; a tile at slot0 adds slot0 * scale_step (2 * D/32 or 2 bytes per slot).
+struct ScaleLane {
+  uint32_t off0, step;
+};
+
 template <int D>
-__device__ inline void stage_tile(const uint8_t* base, int P, int slot0, uint32_t dst, int lane) {
+__device__ inline ScaleLane scale_lane(int P, int lane) {
+  if (lane < D / 16) return {(uint32_t)v_scales_at(P, D) + 16u * lane, (uint32_t)(D / 16)};
+  const int kl = min(lane - D / 16, 1);  // lanes past the two K-scale lanes are masked off
+  return {(uint32_t)k_scales_at(P, D) + 16u * kl, 2u};
+}
+
+// Issue the loads of one tile of the (page, KV head) block at pb (slot0 = the tile's first slot
+// in the page) into LDS at byte address dst (wave-uniform).
+template <int D>
+__device__ inline void stage_tile(const uint8_t* pb, int P, int slot0, uint32_t dst, uint32_t lane16,
+                                  ScaleLane sl) {
   static_assert(D == 64 || D == 128 || D == 256, "head_dim");
-  const int tip = slot0 / kTile;
-  dma16<D / 64>(base + (size_t)16 * D * tip + 16 * lane, dst + Stage<D>::kK);
-  const uint8_t* vb = base + v_codes_at(P, D) + (size_t)8 * D * tip;
-  if constexpr (D >= 128) {
-    dma16<D / 128>(vb + 16 * lane, dst + Stage<D>::kV);
-  } else {
-    if (lane < 32) dma16<1>(vb + 16 * lane, dst + Stage<D>::kV);
-  }
-  if (lane < D / 16)
-    dma16<1>(base + v_scales_at(P, D) + (size_t)2 * slot0 * (D / 32) + 16 * lane, dst + Stage<D>::kVs);
-  if (lane < 2) dma16<1>(base + k_scales_at(P, D) + 2 * slot0 + 16 * lane, dst + Stage<D>::kKs);
+  const uint32_t tip = (uint32_t)slot0 >> 4;  // offsets within one block are 32-bit
+  dma16<D / 64>(pb + tip * (16u * D), lane16, dst + Stage<D>::kK);
+  const uint8_t* vb = pb + ((uint32_t)v_codes_at(P, D) + tip * (8u * D));
+  if constexpr (D >= 128)
+    dma16<D / 128>(vb, lane16, dst + Stage<D>::kV);
+  else
+    dma16<1, 32>(vb, lane16, dst + Stage<D>::kV);
+  dma16<1, Stage<D>::kScaleLanes>(pb, sl.off0 + (uint32_t)slot0 * sl.step, dst + Stage<D>::kVs);
 }
 
 // Read one staged tile into this lane's registers (the lane's share of every section).
@@ -220,9 +269,9 @@ __device__ inline void read_tile(TileRaw<D>& r, const uint8_t* src, int lane) {
 //          sums of 2^(z - base) * (1, v);  it only moves up, in whole powers of two, when a block's
 //          largest logit and V scale would push p * v_scale past 2^15 (fp16 headroom), so most
 //          blocks rescale nothing and every rescale is exact.
-template <int D, int NB, bool MASK>
+template <int D, int NB>
 __device__ __attribute__((always_inline)) inline void process_block(
-    const TileRaw<D> (&raw)[2], int blk, const i32x4 (&qd)[NB][3][D / 64], const float (&cz)[NB],
+    TileRaw<D> (&raw)[2], int blk, bool masked, float e5, const i32x4 (&qd)[NB][3][D / 64], const float (&cz)[NB],
     const int (&last_tok)[NB], int g, floatx4 (&acc)[NB][D / 16], float (&base)[NB],
     float (&l_run)[NB]) {
   constexpr int DB = D / 16;
@@ -252,19 +301,6 @@ __device__ __attribute__((always_inline)) inline void process_block(
 #pragma unroll
     for (int e = 0; e < 4; ++e) ks[tau][e] = h_at(raw[tau].ks, e);
 
-  // ---- exponent of the block's largest V scale (positive fp16: bit order is value order) ----
-  typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
-  u16x2 vmax = {0, 0};
-#pragma unroll
-  for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-    for (int c = 0; c < TileRaw<D>::kVsWords; ++c)
-      vmax = __builtin_elementwise_max(vmax, __builtin_bit_cast(u16x2, raw[tau].vs[c]));
-  int smax = max((int)vmax[0], (int)vmax[1]);
-  smax = max(smax, __shfl_xor(smax, 16, kWave));
-  smax = max(smax, __shfl_xor(smax, 32, kWave));
-  const float e5 = (float)((smax >> 10) & 31);  // scales < 2^(e5 - 14)
-
   // ---- logits and the online softmax (log2 units) ----
   float pexp[NB][2][4];
   bool rescale = false;
@@ -279,16 +315,22 @@ __device__ __attribute__((always_inline)) inline void process_block(
       for (int e = 0; e < 4; ++e) {
         const int hm = (sd[tau][nb][0][e] << 8) + sd[tau][nb][1][e];  // |.| < 2^30: exact
         const float sc = __builtin_fmaf((float)hm, 256.0f, (float)sd[tau][nb][2][e]);
-        float zz = sc * (ks[tau][e] * cz[nb]);
-        if (MASK) {
-          const int t = blk * kBlock + kTile * tau + 4 * g + e;
-          zz = (t <= last_tok[nb]) ? zz : kNegInf;
-        }
-        z[tau][e] = zz;
-        bm = fmaxf(bm, zz);
+        z[tau][e] = sc * (ks[tau][e] * cz[nb]);
       }
-    bm = fmaxf(bm, __shfl_xor(bm, 16, kWave));
-    bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
+    if (masked) {  // wave-uniform: only the blocks at the end of a context
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = blk * kBlock + kTile * tau + 4 * g + e;
+          z[tau][e] = (t <= last_tok[nb]) ? z[tau][e] : kNegInf;
+        }
+    }
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bm = fmaxf(bm, z[tau][e]);
+    bm = max_over_rows(bm);
     // p * v_scale < 2^(bm - base + e5 - 14) must stay below 2^15
     const float need = bm + (e5 - 29.0f);
     float b_new = base[nb];
@@ -312,11 +354,13 @@ __device__ __attribute__((always_inline)) inline void process_block(
       }
     l_run[nb] = l_run[nb] * alpha[nb] + lsum;
   }
-  if (__any(rescale)) {  // rare: a larger logit or V scale than this wave has seen
+  if (__builtin_expect(__any(rescale), 0)) {  // rare: a larger logit or V scale than this wave has seen
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) acc[nb][db] *= alpha[nb];
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[nb][db][e] *= alpha[nb];
   }
 
   // ---- O^T += V^T P^T, one 32-dim scale group at a time ----
@@ -334,28 +378,17 @@ __device__ __attribute__((always_inline)) inline void process_block(
       uint32_t hw[4], lw[4];
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
-        if (MASK) {  // a masked slot's scale may be junk: multiply in fp32 and select
-          float px[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            px[e] = pexp[nb][tau][e] * h_at(raw[tau].vs, e * NG + j);
-            px[e] = (pexp[nb][tau][e] == 0.0f) ? 0.0f : px[e];
-          }
-          split_hi_lo(px[0], px[2], hw[2 * tau], lw[2 * tau]);
-          split_hi_lo(px[1], px[3], hw[2 * tau + 1], lw[2 * tau + 1]);
+        const uint32_t* vs = raw[tau].vs;
+        if (j & 1) {  // resolved at compile time once the group loop is unrolled
+          mix_hi_lo<1>(pexp[nb][tau][0], vs[(0 * NG + j) / 2], pexp[nb][tau][2], vs[(2 * NG + j) / 2],
+                       hw[2 * tau], lw[2 * tau]);
+          mix_hi_lo<1>(pexp[nb][tau][1], vs[(1 * NG + j) / 2], pexp[nb][tau][3], vs[(3 * NG + j) / 2],
+                       hw[2 * tau + 1], lw[2 * tau + 1]);
         } else {
-          const uint32_t* vs = raw[tau].vs;
-          if (j & 1) {  // resolved at compile time once the group loop is unrolled
-            mix_hi_lo<1>(pexp[nb][tau][0], vs[(0 * NG + j) / 2], pexp[nb][tau][2], vs[(2 * NG + j) / 2],
-                         hw[2 * tau], lw[2 * tau]);
-            mix_hi_lo<1>(pexp[nb][tau][1], vs[(1 * NG + j) / 2], pexp[nb][tau][3], vs[(3 * NG + j) / 2],
-                         hw[2 * tau + 1], lw[2 * tau + 1]);
-          } else {
-            mix_hi_lo<0>(pexp[nb][tau][0], vs[(0 * NG + j) / 2], pexp[nb][tau][2], vs[(2 * NG + j) / 2],
-                         hw[2 * tau], lw[2 * tau]);
-            mix_hi_lo<0>(pexp[nb][tau][1], vs[(1 * NG + j) / 2], pexp[nb][tau][3], vs[(3 * NG + j) / 2],
-                         hw[2 * tau + 1], lw[2 * tau + 1]);
-          }
+          mix_hi_lo<0>(pexp[nb][tau][0], vs[(0 * NG + j) / 2], pexp[nb][tau][2], vs[(2 * NG + j) / 2],
+                       hw[2 * tau], lw[2 * tau]);
+          mix_hi_lo<0>(pexp[nb][tau][1], vs[(1 * NG + j) / 2], pexp[nb][tau][3], vs[(3 * NG + j) / 2],
+                       hw[2 * tau + 1], lw[2 * tau + 1]);
         }
       }
       const half8 phi = __builtin_bit_cast(half8, u32x4{hw[0], hw[1], hw[2], hw[3]});
@@ -380,8 +413,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   constexpr int NSTAGE = 3;
   constexpr int BS = Stage<D>::kBlockBytes;
   constexpr int NL = Stage<D>::kLoads;
-  constexpr int CHUNK = 128;            // blocks whose page ids sit in LDS at once
-  constexpr int PT_CAP = 2 * CHUNK + 2;
+  constexpr int CHUNK = kWavesPerGroup * 32;  // blocks per chunk: 32 per wave, page ids in lanes
   static_assert(2 * NL <= 63, "vmcnt range");
   // After the main loop the stage buffers hold the wave merge (ROWS x LDS_STRIDE floats) and then
   // the final merge: (max, sum) of kMaxSplits x ROWS, ROWS floats, PARTS x 4 rows x D floats.
@@ -392,7 +424,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[LDS_BYTES];
   typedef uint8_t StageBuf[NSTAGE][BS];
   StageBuf* s_stage = (StageBuf*)s_lds;
-  __shared__ int s_pt[PT_CAP];
   __shared__ float s_m[kWavesPerGroup][ROWS];
   __shared__ float s_l[kWavesPerGroup][ROWS];
   __shared__ int s_last;
@@ -493,52 +524,81 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)&s_stage[w][0][0]);
   const uint8_t* my_stage = &s_stage[w][0][0];
   const int lgP = a.log2_page;
+  const uint32_t lane16 = 16u * lane;
+  const uint32_t page_stride32 = (uint32_t)page_stride;  // < 2^32, checked on the host
+  const ScaleLane sl = scale_lane<D>(P, lane);
   for (int c0 = g_blk0; c0 < g_blk1; c0 += CHUNK) {
     const int c1 = min(c0 + CHUNK, g_blk1);
-    const int lp0 = (c0 * kBlock) >> lgP;
-    const int lp1 = ((c1 * kBlock - 1) >> lgP) + 1;
-    __syncthreads();  // the previous chunk's page ids are no longer read
-    for (int e = threadIdx.x; e < lp1 - lp0; e += blockDim.x)
-      s_pt[e] = min(max(pt[lp0 + e], 0), a.num_pages - 1);
-    __syncthreads();
-
     const int first = c0 + w;
     const int n_my = first < c1 ? (c1 - first + kWavesPerGroup - 1) / kWavesPerGroup : 0;
-    auto issue = [&](int k) {
-      const int blk = first + kWavesPerGroup * k;
-      const uint32_t dst = my_stage_lds + (uint32_t)((k % NSTAGE) * BS);
+    // lane kk < 32 holds the physical page of tile 0 of this wave's kk-th block of the chunk,
+    // lane 32 + kk that of tile 1 (a tile past the end stages tile 0 again, all of it masked)
+    int my_pid;
+    {
+      const int kk = lane & 31;
+      const int blk = first + kWavesPerGroup * kk;
+      int tok0 = blk * kBlock + kTile * (lane >> 5);
+      if (tok0 >= Lc) tok0 = blk * kBlock;
+      my_pid = kk < n_my ? min(max(pt[tok0 >> lgP], 0), a.num_pages - 1) : 0;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // (also orders it before the DMA counting)
+    auto issue = [&](int k, uint32_t dst) {
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
+        const int blk = first + kWavesPerGroup * k;
         int tok0 = blk * kBlock + kTile * tau;
-        if (tok0 >= Lc) tok0 = blk * kBlock;  // tile past the end: stage tile 0 again, all masked
-        const int phys = __builtin_amdgcn_readfirstlane(s_pt[(tok0 >> lgP) - lp0]);
-        stage_tile<D>(pool_h + (size_t)phys * page_stride, P, tok0 & (P - 1),
-                      dst + (uint32_t)(tau * Stage<D>::kTileBytes), lane);
+        if (tok0 >= Lc) tok0 = blk * kBlock;
+        const int phys = __builtin_amdgcn_readlane(my_pid, 32 * tau + k);
+        stage_tile<D>(pool_h + (uint64_t)(uint32_t)phys * page_stride32, P, tok0 & (P - 1),
+                      dst + (uint32_t)(tau * Stage<D>::kTileBytes), lane16, sl);
       }
     };
-    if (n_my > 0) issue(0);
-    if (n_my > 1) issue(1);
+    // stage buffer of block k: k % 3, tracked incrementally
+    uint32_t st_issue = my_stage_lds;
+    auto next_stage = [&](uint32_t x) { return x == my_stage_lds + 2 * BS ? my_stage_lds : x + BS; };
+    if (n_my > 0) issue(0, st_issue);
+    st_issue = next_stage(st_issue);
+    if (n_my > 1) issue(1, st_issue);
+    st_issue = next_stage(st_issue);
+    int st_read = 0;
     for (int k = 0; k < n_my; ++k) {
       if (k + 2 < n_my) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads of the buffer being refilled are done
-        issue(k + 2);
-      }
-      const int ahead = min(n_my - 1 - k, 2);  // blocks issued after this one
-      if (ahead == 2)
+        issue(k + 2, st_issue);
+        st_issue = next_stage(st_issue);
         wait_vmcnt<2 * NL>();
-      else if (ahead == 1)
+      } else if (k + 1 < n_my) {
         wait_vmcnt<NL>();
-      else
+      } else {
         wait_vmcnt<0>();
-      const uint8_t* src = my_stage + (k % NSTAGE) * BS;
+      }
+      const uint8_t* src = my_stage + st_read * BS;
+      st_read = st_read == NSTAGE - 1 ? 0 : st_read + 1;
+      const int blk = first + kWavesPerGroup * k;
+      const bool masked = blk * kBlock + kBlock - 1 >= mask_from;
+      if (masked && lane < kBlock) {
+        // a slot past the context may hold junk scale bits, and 0 * Inf is no zero: clear the V
+        // scales of those slots in the staged copy (the same wave reads them below, in order)
+        if (blk * kBlock + lane >= Lc) {
+          uint8_t* vs = (uint8_t*)src + (lane >> 4) * Stage<D>::kTileBytes + Stage<D>::kVs + (lane & 15) * (D / 16);
+          if constexpr (D == 256) *(u32x4*)vs = u32x4{0, 0, 0, 0};
+          else if constexpr (D == 128) *(u32x2*)vs = u32x2{0, 0};
+          else *(uint32_t*)vs = 0u;
+        }
+      }
       TileRaw<D> raw[2];
       read_tile<D>(raw[0], src, lane);
       read_tile<D>(raw[1], src + Stage<D>::kTileBytes, lane);
-      const int blk = first + kWavesPerGroup * k;
-      if (blk * kBlock + kBlock - 1 >= mask_from)
-        process_block<D, NB, true>(raw, blk, qd, cz, last_tok, g, acc, base, l_run);
-      else
-        process_block<D, NB, false>(raw, blk, qd, cz, last_tok, g, acc, base, l_run);
+      // binary exponent of the block's largest V scale (positive fp16: bit order is value order);
+      // every scale is below 2^(e5 - 14)
+      float e5;
+      {
+        const uint32_t* vsw = (const uint32_t*)(src + Stage<D>::kVs) + (lane & (D / 4 - 1));
+        const uint32_t m = wave_max_u16x2(__builtin_bit_cast(uint32_t, __builtin_elementwise_max(
+            __builtin_bit_cast(u16x2, vsw[0]), __builtin_bit_cast(u16x2, vsw[Stage<D>::kTileBytes / 4]))));
+        e5 = (float)((m >> 10) & 31);
+      }
+      process_block<D, NB>(raw, blk, masked, e5, qd, cz, last_tok, g, acc, base, l_run);
     }
   }
   __syncthreads();  // every wave is done with its stage buffers (reused below for the merge)
