@@ -131,11 +131,11 @@ int kvq_append(void* pool, int32_t num_pages, int32_t page_size, int32_t num_kv_
  *   out           device fp32 [n_seq][n_rows][n_q_heads][head_dim].
  *   lse           device fp32 [n_seq][n_rows][n_q_heads], or NULL.
  *   workspace     device scratch of at least kvq_decode_workspace_bytes(...) bytes, 16-byte
- *                 aligned, zero-filled before its first use (e.g. allocated with torch.zeros).
- *                 Its first bytes hold one arrival counter per (sequence, KV head) with which
- *                 the last workgroup to finish detects that it must merge the pieces; every
- *                 call leaves those counters at zero again, so one zero-fill serves any number
- *                 of calls of any shape.  Two calls in flight at once must not share it.
+ *                 aligned, for the pieces' partial results (numerators, running max and sum).
+ *                 It needs no initialization and carries nothing from one call to the next;
+ *                 two calls in flight at once must not share it.
+ * With more than one piece per context the call is two launches on `stream`: the split-KV
+ * attention, then the log-sum-exp merge of the pieces.
  * Returns KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE or KVQ_ERR_HIP.
  */
 int kvq_decode_attn(const void* pool, int32_t num_pages, int32_t page_size,

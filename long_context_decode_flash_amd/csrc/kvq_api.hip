@@ -46,14 +46,13 @@ int plan_splits(int n_seq, int num_kv_heads, int max_seq_len, int request, Plan*
   return KVQ_OK;
 }
 
-// Workspace: [arrival counters, units x 4 B, padded to 256 B][partial numerators
-// units x splits x rows x D fp32][partial (max, sum) units x splits x rows x 2 fp32].
-size_t counters_bytes(long long units) { return (size_t)ceil_div(units * 4, 256) * 256; }
-
+// Workspace: [partial numerators units x splits x rows x D fp32][partial (max, sum)
+// units x ml_stride(splits, rows) x 2 fp32].  Nothing in it needs initializing.
 size_t workspace_for(long long units, int splits, int rows, int head_dim) {
+  if (splits == 1) return 16;  // one split writes the output directly
   const size_t acc = (size_t)units * splits * rows * head_dim * sizeof(float);
-  const size_t ml = (size_t)units * splits * rows * 2 * sizeof(float);
-  return counters_bytes(units) + acc + ml;
+  const size_t ml = (size_t)units * kvq::ml_stride(splits, rows) * 2 * sizeof(float);
+  return acc + ml;
 }
 
 int pool_args_ok(const void* pool, int32_t num_pages, int32_t page_size, int32_t num_kv_heads,
@@ -168,8 +167,7 @@ int kvq_decode_attn(const void* pool, int32_t num_pages, int32_t page_size,
   a.splits = plan.splits;
   a.blocks_per_split = plan.blocks_per_split;
   a.scale_log2 = (float)(scale * 1.4426950408889634074);
-  a.ws_count = (unsigned*)workspace;
-  a.ws_acc = (float*)((char*)workspace + counters_bytes(units));
+  a.ws_acc = (float*)workspace;
   a.ws_ml = (float2*)((char*)a.ws_acc + (size_t)units * plan.splits * rows * head_dim * sizeof(float));
   a.out = out;
   a.lse = lse;

@@ -1,5 +1,5 @@
-// kvq_decode.hip — split-KV decode attention over the paged K8/V4 cache with the log-sum-exp
-// merge of the pieces in the same launch.
+// kvq_decode.hip — split-KV decode attention over the paged K8/V4 cache and the log-sum-exp
+// merge of the pieces.
 //
 // The pages describe a decode kernel tuned for one long request over a KV cache handled in
 // pieces of the context, loading only the current piece on chip (blog page "標籤: vLLM",
@@ -21,8 +21,9 @@
 //     high and low parts from one single-rounding multiply so the product keeps fp32 accuracy;
 //   * online softmax in log2 units whose exponent offset only moves in powers of two when a
 //     block needs it, so most blocks rescale nothing;
-//   * the waves merge through LDS; the last workgroup of each (sequence, KV head) to finish
-//     merges the pieces' partials into the output.
+//   * the waves merge through LDS into one partial per workgroup (or straight into the output
+//     when a context is one piece); a second, wide launch merges the pieces' partials, one
+//     workgroup per (sequence, KV head, query row).
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -36,6 +37,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_inff();
+constexpr int cmax(int x, int y) { return x > y ? x : y; }
 
 __device__ inline half2v as_h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
 __device__ inline uint32_t as_u32(half2v h) { return __builtin_bit_cast(uint32_t, h); }
@@ -83,13 +85,6 @@ __device__ inline void mix_hi_lo(float p0, uint32_t sw0, float p1, uint32_t sw1,
 }
 #pragma clang diagnostic pop
 
-__device__ inline void store_agent(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline uint64_t load_agent(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 __device__ inline float h_at(const uint32_t* words, int idx) {
   const uint32_t w = words[idx >> 1];
   return (float)__builtin_bit_cast(_Float16, (uint16_t)((idx & 1) ? (w >> 16) : (w & 0xFFFF)));
@@ -112,6 +107,41 @@ __device__ inline float max_over_rows(float x) {
   const uint32_t v = __builtin_bit_cast(uint32_t, mx(a[0], a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);  // halves meet
   return mx(b[0], b[1]);
+}
+
+// sum of x over the four lanes m16, m16 + 16, m16 + 32, m16 + 48
+__device__ inline float sum_over_rows(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const uint32_t a0 = a[0], a1 = a[1];
+  x = __builtin_bit_cast(float, a0) + __builtin_bit_cast(float, a1);
+  const uint32_t v = __builtin_bit_cast(uint32_t, x);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  const uint32_t b0 = b[0], b1 = b[1];
+  return __builtin_bit_cast(float, b0) + __builtin_bit_cast(float, b1);
+}
+
+// Wave-wide max / sum of a float (the same value in every lane for the max; the sum is taken
+// from lane 0 and broadcast, so every lane agrees on it bit for bit).
+template <bool kSum>
+__device__ inline float wave_reduce(float x) {
+  auto op = [](float p, float q) { return kSum ? p + q : fmaxf(p, q); };
+#define KVQ_DPP(v, ctrl) \
+  __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, 0xF, 0xF, false))
+  x = op(x, KVQ_DPP(x, 0xB1));   // quad_perm [1,0,3,2]
+  x = op(x, KVQ_DPP(x, 0x4E));   // quad_perm [2,3,0,1]
+  x = op(x, KVQ_DPP(x, 0x141));  // row_half_mirror
+  x = op(x, KVQ_DPP(x, 0x140));  // row_mirror
+#undef KVQ_DPP
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const uint32_t a0 = a[0], a1 = a[1];
+  x = op(__builtin_bit_cast(float, a0), __builtin_bit_cast(float, a1));
+  const uint32_t v = __builtin_bit_cast(uint32_t, x);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  const uint32_t b0 = b[0], b1 = b[1];
+  x = op(__builtin_bit_cast(float, b0), __builtin_bit_cast(float, b1));
+  return kSum ? __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x))) : x;
 }
 
 // Largest of the 128 fp16 halves of x over the wave (as 16-bit patterns, in both halves).
@@ -404,7 +434,7 @@ __device__ __attribute__((always_inline)) inline void process_block(
 // One workgroup (4 waves) per (unit, split); wave w takes the split's blocks w, w+4, w+8, ...
 // Each wave streams its blocks through three LDS stage buffers with direct-to-LDS loads, so two
 // blocks are in flight while it computes the third.  The waves merge through LDS into one
-// partial; the last workgroup of a unit to finish merges the unit's partials into the output.
+// partial (the output itself when the context is a single piece).
 template <int D, int NB>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   constexpr int DB = D / 16;
@@ -415,18 +445,16 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   constexpr int NL = Stage<D>::kLoads;
   constexpr int CHUNK = kWavesPerGroup * 32;  // blocks per chunk: 32 per wave, page ids in lanes
   static_assert(2 * NL <= 63, "vmcnt range");
-  // After the main loop the stage buffers hold the wave merge (ROWS x LDS_STRIDE floats) and then
-  // the final merge: (max, sum) of kMaxSplits x ROWS, ROWS floats, PARTS x 4 rows x D floats.
-  constexpr int MERGE_BYTES = kMaxSplits * ROWS * 8 + ROWS * 4 + 16 + 16 * D * (1024 / D);
+  // After the main loop the same LDS holds the wave merge (4 waves x ROWS x LDS_STRIDE floats).
+  constexpr int WAVE_MERGE_BYTES = kWavesPerGroup * ROWS * LDS_STRIDE * 4;
   constexpr int STAGE_BYTES = kWavesPerGroup * NSTAGE * BS;
-  constexpr int LDS_BYTES = STAGE_BYTES > MERGE_BYTES ? STAGE_BYTES : MERGE_BYTES;
-  static_assert(ROWS * LDS_STRIDE * 4 <= LDS_BYTES, "wave merge buffer fits");
+  constexpr int LDS_BYTES = cmax(STAGE_BYTES, WAVE_MERGE_BYTES);
+  static_assert(LDS_BYTES <= 160 * 1024 - 1024, "LDS");
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[LDS_BYTES];
   typedef uint8_t StageBuf[NSTAGE][BS];
   StageBuf* s_stage = (StageBuf*)s_lds;
   __shared__ float s_m[kWavesPerGroup][ROWS];
   __shared__ float s_l[kWavesPerGroup][ROWS];
-  __shared__ int s_last;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -444,11 +472,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const uint8_t* pool_h = a.pool + (size_t)h * bb;
   const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
 
-  // ---- Q^T as three int8 digit planes (B of QK^T): lane holds query row 16*nb + m16 and the
-  // 16 dims 16*(4*jj + g) .. +15 of each 64-dim step jj.  q * 2^F = h*2^16 + m*2^8 + l with
-  // |q * 2^F| < 2^22 for the row's largest |q|; exact for every element within 2^12 of it.
-  i32x4 qd[NB][3][D / 64];
-  float cz[NB];  // 2^-F * softmax_scale * log2(e)
+  // ---- raw query words: lane holds query row 16*nb + m16 and the 16 dims 16*(4*jj + g) .. +15
+  // of each 64-dim step jj (the B-operand layout of QK^T) ----
+  u32x4 qw[NB][D / 64][2];
   int last_tok[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -458,56 +484,124 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int hq = h * a.group + (real ? n % a.group : 0);
     last_tok[nb] = min(real ? L - a.n_rows + i : L - 1, Lc - 1);  // padding rows: q = 0
     const uint16_t* qrow = a.q + (((size_t)b * a.n_rows + i) * a.n_q_heads + hq) * D;
-    float qf[D / 64][16];
+#pragma unroll
+    for (int jj = 0; jj < D / 64; ++jj)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        qw[nb][jj][hf] = real ? *(const u32x4*)(qrow + 16 * (4 * jj + g) + 8 * hf) : u32x4{0, 0, 0, 0};
+  }
+  // first token that some row may mask (causal MTP rows, the ragged end, max_seq_len)
+  const int mask_from = min(L - a.n_rows + 1, Lc);
+
+  // ---- chunks of the split: page ids in lanes, blocks staged through three LDS buffers ----
+  // LDS byte address of this wave's stage buffers (wave-uniform, computed once)
+  const uint32_t my_stage_lds =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)&s_stage[w][0][0]);
+  const uint8_t* my_stage = &s_stage[w][0][0];
+  const int lgP = a.log2_page;
+  const uint32_t lane16 = 16u * lane;
+  const uint32_t page_stride32 = (uint32_t)page_stride;  // < 2^32, checked on the host
+  const ScaleLane sl = scale_lane<D>(P, lane);
+  int c0 = g_blk0, first = 0, n_my = 0, my_pid = 0;
+  uint32_t st_issue = my_stage_lds;
+  auto issue = [&](int k, uint32_t dst) {
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      const int blk = first + kWavesPerGroup * k;
+      int tok0 = blk * kBlock + kTile * tau;
+      if (tok0 >= Lc) tok0 = blk * kBlock;
+      const int phys = __builtin_amdgcn_readlane(my_pid, 32 * tau + k);
+      stage_tile<D>(pool_h + (uint64_t)(uint32_t)phys * page_stride32, P, tok0 & (P - 1),
+                    dst + (uint32_t)(tau * Stage<D>::kTileBytes), lane16, sl);
+    }
+  };
+  // stage buffer of block k: k % 3, tracked incrementally
+  auto next_stage = [&](uint32_t x) { return x == my_stage_lds + 2 * BS ? my_stage_lds : x + BS; };
+  // chunk set-up: this wave's page ids into lanes, then the loads of its first two blocks
+  auto chunk_pages = [&]() {
+    const int c1 = min(c0 + CHUNK, g_blk1);
+    first = c0 + w;
+    n_my = first < c1 ? (c1 - first + kWavesPerGroup - 1) / kWavesPerGroup : 0;
+    // lane kk < 32 holds the physical page of tile 0 of this wave's kk-th block of the chunk,
+    // lane 32 + kk that of tile 1 (a tile past the end stages tile 0 again, all of it masked)
+    const int kk = lane & 31;
+    const int blk = first + kWavesPerGroup * kk;
+    int tok0 = blk * kBlock + kTile * (lane >> 5);
+    if (tok0 >= Lc) tok0 = blk * kBlock;
+    my_pid = kk < n_my ? min(max(pt[tok0 >> lgP], 0), a.num_pages - 1) : 0;
+  };
+  auto chunk_start = [&]() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // page ids in; the DMA counting starts here
+    st_issue = my_stage_lds;
+    if (n_my > 0) issue(0, st_issue);
+    st_issue = next_stage(st_issue);
+    if (n_my > 1) issue(1, st_issue);
+    st_issue = next_stage(st_issue);
+  };
+  // The first chunk's first blocks are in flight while the queries are prepared (an empty split
+  // gets n_my = 0).  The query words are used here on every path, so the compiler's own wait for
+  // them (loaded with the page ids, one round trip for both) sits here and not after the DMAs.
+  chunk_pages();
+  asm volatile("" ::"v"(my_pid));
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int jj = 0; jj < D / 64; ++jj) asm volatile("" ::"v"(qw[nb][jj][0]), "v"(qw[nb][jj][1]));
+  chunk_start();
+
+  // ---- Q^T as three int8 digit planes (B of QK^T).  Per row, q * 2^F = h*2^16 + m*2^8 + l with
+  // balanced digits in [-128, 127] and |q * 2^F| < 2^22 for the row's largest |q|; exact for every
+  // element within 2^12 of it, the rest rounded to the 2^-F grid. ----
+  i32x4 qd[NB][3][D / 64];
+  float cz[NB];  // 2^-F * softmax_scale * log2(e)
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
     float amax = 0.0f;
 #pragma unroll
-    for (int jj = 0; jj < D / 64; ++jj) {
-      const int dim0 = 16 * (4 * jj + g);
+    for (int jj = 0; jj < D / 64; ++jj)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const u32x4 w8 = real ? *(const u32x4*)(qrow + dim0 + 8 * hf) : u32x4{0, 0, 0, 0};
-        const half8 h8 = __builtin_bit_cast(half8, w8);
+        const half8 h8 = __builtin_bit_cast(half8, qw[nb][jj][hf]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          qf[jj][8 * hf + e] = (float)h8[e];
-          amax = fmaxf(amax, fabsf(qf[jj][8 * hf + e]));
-        }
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)h8[e]));
       }
-    }
-    amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
-    amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+    amax = max_over_rows(amax);
     int E = 0;
     if (amax > 0.0f) (void)__builtin_frexpf(amax, &E);  // amax < 2^E
     const int F = amax > 0.0f ? 22 - E : 0;
+    const float scale_f = __builtin_ldexpf(1.0f, F);
     cz[nb] = __builtin_ldexpf(a.scale_log2, -F);
 #pragma unroll
     for (int jj = 0; jj < D / 64; ++jj) {
       uint32_t wd[3][4];
 #pragma unroll
       for (int w4 = 0; w4 < 4; ++w4) {
-        uint32_t bh = 0, bmid = 0, bl = 0;
+        // x + 1.5 * 2^23 rounds x to an integer (ties to even) in the low mantissa bits; adding
+        // 128 * (1 + 2^8 + 2^16) then makes byte k of the word digit k + 128, so xor 0x80 per byte
+        // leaves the balanced digits as int8
+        uint32_t wq[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int qi = (int)__builtin_rintf(__builtin_ldexpf(qf[jj][4 * w4 + e], F));
-          const int dl = ((qi + 128) & 255) - 128;
-          const int r1 = (qi - dl) >> 8;
-          const int dm = ((r1 + 128) & 255) - 128;
-          const int dh = (r1 - dm) >> 8;
-          bh |= (uint32_t)(dh & 255) << (8 * e);
-          bmid |= (uint32_t)(dm & 255) << (8 * e);
-          bl |= (uint32_t)(dl & 255) << (8 * e);
+          const int el = 4 * w4 + e;
+          const half8 h8 = __builtin_bit_cast(half8, qw[nb][jj][el >> 3]);
+          const float x = (float)h8[el & 7];
+          const uint32_t y = __builtin_bit_cast(uint32_t, __builtin_fmaf(x, scale_f, 12582912.0f));
+          wq[e] = (y - (0x4B400000u - 0x808080u)) ^ 0x808080u;
         }
-        wd[0][w4] = bh;
-        wd[1][w4] = bmid;
-        wd[2][w4] = bl;
+        // 4x3 byte transpose: plane k gets byte k of the four words
+        const uint32_t t01 = __builtin_amdgcn_perm(wq[1], wq[0], 0x05010400u);
+        const uint32_t t23 = __builtin_amdgcn_perm(wq[3], wq[2], 0x05010400u);
+        const uint32_t u01 = __builtin_amdgcn_perm(wq[1], wq[0], 0x0C0C0602u);
+        const uint32_t u23 = __builtin_amdgcn_perm(wq[3], wq[2], 0x0C0C0602u);
+        wd[2][w4] = __builtin_amdgcn_perm(t23, t01, 0x05040100u);  // low digits
+        wd[1][w4] = __builtin_amdgcn_perm(t23, t01, 0x07060302u);
+        wd[0][w4] = __builtin_amdgcn_perm(u23, u01, 0x05040100u);  // high digits
       }
 #pragma unroll
       for (int pc = 0; pc < 3; ++pc)
         qd[nb][pc][jj] = __builtin_bit_cast(i32x4, u32x4{wd[pc][0], wd[pc][1], wd[pc][2], wd[pc][3]});
     }
   }
-  // first token that some row may mask (causal MTP rows, the ragged end, max_seq_len)
-  const int mask_from = min(L - a.n_rows + 1, Lc);
 
   floatx4 acc[NB][DB];
   float base[NB], l_run[NB];
@@ -519,47 +613,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     l_run[nb] = 0.0f;
   }
 
-  // LDS byte address of this wave's stage buffers (wave-uniform, computed once)
-  const uint32_t my_stage_lds =
-      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)&s_stage[w][0][0]);
-  const uint8_t* my_stage = &s_stage[w][0][0];
-  const int lgP = a.log2_page;
-  const uint32_t lane16 = 16u * lane;
-  const uint32_t page_stride32 = (uint32_t)page_stride;  // < 2^32, checked on the host
-  const ScaleLane sl = scale_lane<D>(P, lane);
-  for (int c0 = g_blk0; c0 < g_blk1; c0 += CHUNK) {
-    const int c1 = min(c0 + CHUNK, g_blk1);
-    const int first = c0 + w;
-    const int n_my = first < c1 ? (c1 - first + kWavesPerGroup - 1) / kWavesPerGroup : 0;
-    // lane kk < 32 holds the physical page of tile 0 of this wave's kk-th block of the chunk,
-    // lane 32 + kk that of tile 1 (a tile past the end stages tile 0 again, all of it masked)
-    int my_pid;
-    {
-      const int kk = lane & 31;
-      const int blk = first + kWavesPerGroup * kk;
-      int tok0 = blk * kBlock + kTile * (lane >> 5);
-      if (tok0 >= Lc) tok0 = blk * kBlock;
-      my_pid = kk < n_my ? min(max(pt[tok0 >> lgP], 0), a.num_pages - 1) : 0;
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // (also orders it before the DMA counting)
-    auto issue = [&](int k, uint32_t dst) {
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau) {
-        const int blk = first + kWavesPerGroup * k;
-        int tok0 = blk * kBlock + kTile * tau;
-        if (tok0 >= Lc) tok0 = blk * kBlock;
-        const int phys = __builtin_amdgcn_readlane(my_pid, 32 * tau + k);
-        stage_tile<D>(pool_h + (uint64_t)(uint32_t)phys * page_stride32, P, tok0 & (P - 1),
-                      dst + (uint32_t)(tau * Stage<D>::kTileBytes), lane16, sl);
-      }
-    };
-    // stage buffer of block k: k % 3, tracked incrementally
-    uint32_t st_issue = my_stage_lds;
-    auto next_stage = [&](uint32_t x) { return x == my_stage_lds + 2 * BS ? my_stage_lds : x + BS; };
-    if (n_my > 0) issue(0, st_issue);
-    st_issue = next_stage(st_issue);
-    if (n_my > 1) issue(1, st_issue);
-    st_issue = next_stage(st_issue);
+  while (c0 < g_blk1) {
     int st_read = 0;
     for (int k = 0; k < n_my; ++k) {
       if (k + 2 < n_my) {
@@ -600,179 +654,143 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       }
       process_block<D, NB>(raw, blk, masked, e5, qd, cz, last_tok, g, acc, base, l_run);
     }
+    c0 += CHUNK;
+    if (c0 < g_blk1) {
+      chunk_pages();
+      chunk_start();
+    }
   }
   __syncthreads();  // every wave is done with its stage buffers (reused below for the merge)
 
-  // ---- merge the 4 waves through LDS ----
-  float* s_acc = (float*)&s_stage[0][0][0];
+  // ---- merge the 4 waves through LDS: every wave parks its state, then all 256 threads
+  // combine the four copies of each (row, 4 dims): the output itself when the context is one
+  // split, else this workgroup's partial for the merge kernel ----
+  constexpr int NQ = D / 4;  // float4 columns of a row
+  float* s_accw = (float*)s_lds;  // [wave][ROWS][LDS_STRIDE]
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    l_run[nb] += __shfl_xor(l_run[nb], 16, kWave);
-    l_run[nb] += __shfl_xor(l_run[nb], 32, kWave);
+    const float l = sum_over_rows(l_run[nb]);
     if (g == 0) {
       s_m[w][16 * nb + m16] = base[nb];
-      s_l[w][16 * nb + m16] = l_run[nb];
+      s_l[w][16 * nb + m16] = l;
     }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      *(floatx4*)(s_accw + (w * ROWS + 16 * nb + m16) * LDS_STRIDE + 16 * db + 4 * g) = acc[nb][db];
   }
   __syncthreads();
-  float M[NB], l_tot[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int row = 16 * nb + m16;
+  const size_t prow0 = ((size_t)unit * a.splits + split) * a.rows;
+  for (int it = threadIdx.x; it < a.rows * NQ; it += kWave * kWavesPerGroup) {
+    const int n = it / NQ, q = it % NQ;
+    float mw[kWavesPerGroup];
     float mm = kNegInf;
 #pragma unroll
-    for (int v = 0; v < kWavesPerGroup; ++v) mm = fmaxf(mm, s_m[v][row]);
+    for (int v = 0; v < kWavesPerGroup; ++v) {
+      mw[v] = s_m[v][n];
+      mm = fmaxf(mm, mw[v]);
+    }
     const float m_use = (mm == kNegInf) ? 0.0f : mm;
+    floatx4 t = {0.f, 0.f, 0.f, 0.f};
     float lt = 0.0f;
 #pragma unroll
-    for (int v = 0; v < kWavesPerGroup; ++v) lt += s_l[v][row] * __builtin_amdgcn_exp2f(s_m[v][row] - m_use);
-    M[nb] = mm;
-    l_tot[nb] = lt;
-    const float f = __builtin_amdgcn_exp2f(base[nb] - m_use);
-#pragma unroll
-    for (int db = 0; db < DB; ++db) acc[nb][db] *= f;
-  }
-  for (int src = 1; src < kWavesPerGroup; ++src) {
-    if (w == src) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          *(floatx4*)(s_acc + (16 * nb + m16) * LDS_STRIDE + 16 * db + 4 * g) = acc[nb][db];
+    for (int v = 0; v < kWavesPerGroup; ++v) {
+      const float f = __builtin_amdgcn_exp2f(mw[v] - m_use);  // 0 for a wave that saw nothing
+      t += f * *(const floatx4*)(s_accw + (v * ROWS + n) * LDS_STRIDE + 4 * q);
+      lt += f * s_l[v][n];
     }
-    __syncthreads();
-    if (w == 0) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          acc[nb][db] += *(const floatx4*)(s_acc + (16 * nb + m16) * LDS_STRIDE + 16 * db + 4 * g);
-    }
-    __syncthreads();
-  }
-  // The partial goes out with agent-scope stores (write-through to the level every XCD sees), and
-  // the last workgroup reads the partials back with agent-scope loads; that pairing makes them
-  // visible across XCDs without a cache-wide write-back or invalidate.
-  if (w == 0) {
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int n = 16 * nb + m16;
-      if (n < a.rows) {
-        const size_t prow = ((size_t)unit * a.splits + split) * a.rows + n;
-        uint64_t* dst = (uint64_t*)(a.ws_acc + prow * D + 4 * g);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const u32x4 bits = __builtin_bit_cast(u32x4, acc[nb][db]);
-          store_agent(dst + 8 * db, bits[0] | ((uint64_t)bits[1] << 32));
-          store_agent(dst + 8 * db + 1, bits[2] | ((uint64_t)bits[3] << 32));
-        }
-        if (g == 0)
-          store_agent((uint64_t*)(a.ws_ml + prow), __builtin_bit_cast(uint32_t, M[nb]) |
-                                                        ((uint64_t)__builtin_bit_cast(uint32_t, l_tot[nb]) << 32));
-      }
+    if (a.splits == 1) {
+      const int i = n / a.group, hq = h * a.group + n % a.group;
+      const size_t o = ((size_t)b * a.n_rows + i) * a.n_q_heads + hq;
+      *(floatx4*)(a.out + o * D + 4 * q) = t * (lt > 0.0f ? 1.0f / lt : 0.0f);
+      if (q == 0 && a.lse) a.lse[o] = lt > 0.0f ? (mm + log2f(lt)) * 0.69314718055994530942f : kNegInf;
+    } else {
+      *(floatx4*)(a.ws_acc + (prow0 + n) * D + 4 * q) = t;
+      if (q == 0) a.ws_ml[(size_t)unit * ml_stride(a.splits, a.rows) + split * a.rows + n] = float2{mm, lt};
     }
   }
+}
 
-  // ---- the last workgroup of this unit merges every split ----
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's partial stores are complete
-  __syncthreads();
-  if (threadIdx.x == 0)
-    s_last = __hip_atomic_fetch_add(&a.ws_count[unit], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             (unsigned)(a.splits - 1);
-  __syncthreads();
-  if (!s_last) return;
-  {
-    // (max, sum) of every (split, row) into LDS, then per-row max M, weights 2^(m - M) and the
-    // denominator; then the numerators in batches of independent loads.
-    constexpr int NQ = D / 4;                  // float4 columns of a row
-    constexpr int PARTS = (kWave * kWavesPerGroup) / NQ;
-    const int S = a.splits, R = a.rows;
-    const size_t p0 = (size_t)unit * S * R;
-    float2* s_ml = (float2*)&s_stage[0][0][0];  // [S][R]
-    float* s_M = (float*)(s_ml + S * R);          // [R]: 1/den
-    floatx4* s_red = (floatx4*)(s_lds + ((S * R * 8 + R * 4 + 15) & ~15));  // [PARTS][4][NQ]
-    for (int e = threadIdx.x; e < S * R; e += blockDim.x)
-      s_ml[e] = __builtin_bit_cast(float2, load_agent((const uint64_t*)(a.ws_ml + p0 + e)));
-    __syncthreads();
-    for (int n = w; n < R; n += kWavesPerGroup) {
-      float mx = kNegInf;
-      for (int sp = lane; sp < S; sp += kWave) mx = fmaxf(mx, s_ml[sp * R + n].x);
+// The log-sum-exp merge of the splits: one workgroup per (unit, query row).  Thread (g, q) takes
+// float4 column q of the row for splits g, g + NG, ... (an online max over its own splits), and
+// the NG groups combine through LDS.  Partials come from the previous launch on the stream.
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
+  constexpr int NQ = D / 4;
+  constexpr int NG = kWave * kWavesPerGroup / NQ;
+  constexpr int U = 8;  // splits per thread in flight at once
+  __shared__ float s_mx[NG];
+  __shared__ float s_den[NG];
+  __shared__ floatx4 s_num[NG][NQ];
+  const int S = a.splits, R = a.rows;
+  const int unit = blockIdx.x / R, n = blockIdx.x % R;
+  const int b = unit / a.num_kv_heads, h = unit % a.num_kv_heads;
+  const int q = threadIdx.x % NQ, grp = threadIdx.x / NQ;
+  const float2* ml = a.ws_ml + (size_t)unit * ml_stride(S, R);
+  const float* part = a.ws_acc + (size_t)unit * S * R * D;
+  float mx = kNegInf, den = 0.0f;
+  floatx4 num = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = grp; s0 < S; s0 += U * NG) {
+    float2 mv[U];
+    floatx4 v[U];
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
-      float den = 0.0f;
-      for (int sp = lane; sp < S; sp += kWave) {
-        const float2 ml = s_ml[sp * R + n];
-        const float wgt = (ml.x == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(ml.x - mx);
-        s_ml[sp * R + n].x = wgt;  // the weight replaces the max
-        den += wgt * ml.y;
-      }
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off, kWave);
-      if (lane == 0) {
-        s_M[n] = den > 0.0f ? 1.0f / den : 0.0f;
-        if (a.lse) {
-          const int i = n / a.group, hq = h * a.group + n % a.group;
-          const size_t o = ((size_t)b * a.n_rows + i) * a.n_q_heads + hq;
-          a.lse[o] = den > 0.0f ? (mx + log2f(den)) * 0.69314718055994530942f : kNegInf;
-        }
-      }
+    for (int u = 0; u < U; ++u) {  // indices clamped into range: all loads issued at once
+      const int sp = min(s0 + u * NG, S - 1);
+      mv[u] = ml[sp * R + n];
+      v[u] = *(const floatx4*)(part + ((size_t)sp * R + n) * D + 4 * q);
     }
-    __syncthreads();
-    const int q = threadIdx.x % NQ, part = threadIdx.x / NQ;
-    for (int n0 = 0; n0 < R; n0 += 4) {
-      floatx4 num[4] = {};
-      for (int sp0 = part; sp0 < S; sp0 += 8 * PARTS) {
-        // every load is unconditional (indices clamped into range, weight 0 outside), so all 64
-        // of them are in flight at once instead of one round trip each
-        uint64_t v[8][4][2];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int sp = min(sp0 + u * PARTS, S - 1), n = min(n0 + r, R - 1);
-            const uint64_t* src = (const uint64_t*)(a.ws_acc + (p0 + (size_t)sp * R + n) * D + 4 * q);
-            v[u][r][0] = load_agent(src);
-            v[u][r][1] = load_agent(src + 1);
-          }
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int sp = sp0 + u * PARTS, n = n0 + r;
-            const float wgt = (sp < S && n < R) ? s_ml[sp * R + n].x : 0.0f;
-            num[r] += wgt * floatx4{__builtin_bit_cast(float, (uint32_t)v[u][r][0]),
-                                    __builtin_bit_cast(float, (uint32_t)(v[u][r][0] >> 32)),
-                                    __builtin_bit_cast(float, (uint32_t)v[u][r][1]),
-                                    __builtin_bit_cast(float, (uint32_t)(v[u][r][1] >> 32))};
-          }
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s_red[(part * 4 + r) * NQ + q] = num[r];
-      __syncthreads();
-      for (int e = threadIdx.x; e < 4 * NQ; e += blockDim.x) {
-        const int r = e / NQ, qq = e % NQ, n = n0 + r;
-        if (n < R) {
-          floatx4 t = s_red[r * NQ + qq];
-          for (int pp = 1; pp < PARTS; ++pp) t += s_red[(pp * 4 + r) * NQ + qq];
-          const int i = n / a.group, hq = h * a.group + n % a.group;
-          const size_t o = ((size_t)b * a.n_rows + i) * a.n_q_heads + hq;
-          *(floatx4*)(a.out + o * D + 4 * qq) = t * s_M[n];
+    for (int u = 0; u < U; ++u) {
+      const float m = mv[u].x;
+      if (s0 + u * NG < S && m != kNegInf) {
+        if (m > mx) {
+          const float f = __builtin_amdgcn_exp2f(mx - m);  // 0 while mx is -inf
+          num *= f;
+          den *= f;
+          mx = m;
         }
+        const float wgt = __builtin_amdgcn_exp2f(m - mx);
+        num += wgt * v[u];
+        den += wgt * mv[u].y;
       }
-      __syncthreads();
     }
   }
-  if (threadIdx.x == 0)  // leave the counter zeroed for the next call
-    __hip_atomic_store(&a.ws_count[unit], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (q == 0) {
+    s_mx[grp] = mx;
+    s_den[grp] = den;
+  }
+  s_num[grp][q] = num;
+  __syncthreads();
+  if (grp == 0) {
+    float M = kNegInf;
+#pragma unroll
+    for (int k = 0; k < NG; ++k) M = fmaxf(M, s_mx[k]);
+    float dt = 0.0f;
+    floatx4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < NG; ++k) {
+      const float f = s_mx[k] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(s_mx[k] - M);
+      t += f * s_num[k][q];
+      dt += f * s_den[k];
+    }
+    const int i = n / a.group, hq = h * a.group + n % a.group;
+    const size_t o = ((size_t)b * a.n_rows + i) * a.n_q_heads + hq;
+    *(floatx4*)(a.out + o * D + 4 * q) = t * (dt > 0.0f ? 1.0f / dt : 0.0f);
+    if (q == 0 && a.lse) a.lse[o] = dt > 0.0f ? (M + log2f(dt)) * 0.69314718055994530942f : kNegInf;
+  }
 }
 
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
-  const unsigned grid = (unsigned)((long long)a.n_seq * a.num_kv_heads * a.splits);
+  const unsigned units = (unsigned)((long long)a.n_seq * a.num_kv_heads);
+  const unsigned grid = units * (unsigned)a.splits;
   if (a.rows <= 16)
     hipLaunchKernelGGL((decode_kernel<D, 1>), dim3(grid), dim3(kWave * kWavesPerGroup), 0, stream, a);
   else
     hipLaunchKernelGGL((decode_kernel<D, 2>), dim3(grid), dim3(kWave * kWavesPerGroup), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits == 1) return e;
+  hipLaunchKernelGGL((merge_kernel<D>), dim3(units * (unsigned)a.rows), dim3(kWave * kWavesPerGroup), 0,
+                     stream, a);
   return hipGetLastError();
 }
 

@@ -25,6 +25,10 @@ __host__ __device__ constexpr size_t v_scales_at(int P, int D) {
   return (size_t)P * D + 2 * (size_t)P + (size_t)P * D / 2;
 }
 
+// (max, sum) entries per unit in the decode workspace: splits x rows, rounded up to an even
+// count so each unit's entries start 16-byte aligned.
+__host__ __device__ constexpr int ml_stride(int splits, int rows) { return (splits * rows + 1) & ~1; }
+
 struct AppendArgs {
   uint8_t* pool;
   int num_pages, page_size, num_kv_heads;
@@ -45,9 +49,8 @@ struct DecodeArgs {
   int max_pages, max_seq_len;
   int splits, blocks_per_split;  // workgroups per (sequence, KV head), 32-token blocks each
   float scale_log2;  // softmax_scale * log2(e)
-  unsigned* ws_count;  // [units] arrival counters: zero on entry, left zero on exit
   float* ws_acc;     // [units][splits][rows][D] partial numerators
-  float2* ws_ml;     // [units][splits][rows] (running max in log2 units, sum of exp2)
+  float2* ws_ml;     // [units][ml_stride(splits, rows)] (max in log2 units, sum of exp2)
   float* out;
   float* lse;
 };

@@ -166,7 +166,7 @@ def decode_attn(cache: PagedCache, q: torch.Tensor, page_table: torch.Tensor,
     need = decode_workspace_bytes(n_seq, n_rows, n_q_heads, cache.num_kv_heads, D, max_seq_len,
                                   num_splits)
     if workspace is None:
-        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     rc = lib().kvq_decode_attn(
         _dev(cache.pool, "pool", torch.uint8), cache.num_pages, cache.page_size,
         cache.num_kv_heads, D, _dev(q, "q", torch.float16),

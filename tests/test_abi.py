@@ -77,7 +77,12 @@ def test_split_plan(lib):
 
 def test_workspace_size(lib):
     s = kvq.decode_num_splits(2, 4, 92160)
-    assert kvq.decode_workspace_bytes(2, 1, 24, 4, 256, 92160) == 256 + 2 * 4 * s * 6 * (256 + 2) * 4
+    assert kvq.decode_workspace_bytes(2, 1, 24, 4, 256, 92160) == 2 * 4 * s * 6 * (256 + 2) * 4
+    # (max, sum) entries per unit are padded to an even count
+    s3 = kvq.decode_num_splits(1, 1, 4096, 3)
+    assert kvq.decode_workspace_bytes(1, 1, 1, 1, 64, 4096, 3) == s3 * 64 * 4 + (s3 + 1) // 2 * 16
+    # one split writes the output directly and needs only a token workspace
+    assert kvq.decode_workspace_bytes(1, 1, 4, 1, 64, 100) == 16
     assert kvq.decode_workspace_bytes(2, 1, 24, 5, 256, 92160) == 0  # heads not divisible
     assert kvq.decode_workspace_bytes(2, 1, 24, 4, 100, 92160) == 0
 

@@ -230,13 +230,13 @@ def test_decode_rejects_small_workspace():
     q = H.to_dev(inp.q_bits).view(torch.float16)
     with pytest.raises(kvq.KVQError) as e:
         kvq.decode_attn(cache, q, H.to_dev(inp.page_table), H.to_dev(inp.seq_lens), 100,
-                        workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+                        num_splits=2, workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
     assert e.value.code == kvq.KVQ_ERR_WORKSPACE
 
 
 def test_decode_workspace_reused_across_shapes():
-    """One zero-filled workspace serves calls of different shapes in a row: the arrival
-    counters each call uses are left at zero for the next."""
+    """One workspace, never initialized, serves calls of different shapes in a row: nothing a
+    call leaves in it affects the next."""
     import torch
     H.say("[workspace reuse]")
     kvq = H.kvq()
@@ -248,7 +248,7 @@ def test_decode_workspace_reused_across_shapes():
         W.custom(n_seq=3, seq_lens=(70, 5, 260), num_kv_heads=1, n_q_heads=4, head_dim=64,
                  page_size=16, n_rows=2, seed=43),
     ]
-    ws = torch.zeros(1 << 24, dtype=torch.uint8, device="cuda")
+    ws = torch.full((1 << 24,), 0xFF, dtype=torch.uint8, device="cuda")  # NaN bit patterns
     for rep in range(2):
         for splits in (0, 3):
             for inp in cases:
@@ -262,6 +262,3 @@ def test_decode_workspace_reused_across_shapes():
                 out_r, _ = H.oracle_decode(inp, H.oracle_fill(inp))
                 assert H.report(f"  rep {rep} splits {splits} {wl.head_dim}", out.cpu().numpy(),
                                 out_r) <= H.TOL_ABS
-    # the counter region is back to zero
-    units_max = 4
-    assert int(ws[:4 * units_max].view(torch.int32).abs().sum().item()) == 0
