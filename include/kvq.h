@@ -116,9 +116,10 @@ int kvq_append(void* pool, int32_t num_pages, int32_t page_size, int32_t num_kv_
  *
  *   pool, num_pages, page_size, num_kv_heads, head_dim   as for kvq_append (read only).
  *   q             device fp16 bits [n_seq][n_rows][n_q_heads][head_dim].
- *   page_table    device int32 [n_seq][max_pages_per_seq], logical -> physical page.  Only the
- *                 first ceil(L / page_size) entries of a row are read; an entry outside
- *                 [0, num_pages) is clamped into range (wrong values, never a fault).
+ *   page_table    device int32 [n_seq][max_pages_per_seq], logical -> physical page.  Entries
+ *                 up to ceil(max_seq_len / page_size) of a row may be read, but only the first
+ *                 ceil(L / page_size) are used; an entry outside [0, num_pages) is clamped into
+ *                 range (wrong values, never a fault).
  *   seq_lens      device int32 [n_seq]: tokens seen by the last row.  Must satisfy
  *                 n_rows <= L <= max_seq_len; tokens beyond max_seq_len are not attended, and a
  *                 row that sees no token gets out = 0 and lse = -inf.

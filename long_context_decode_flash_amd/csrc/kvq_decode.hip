@@ -23,7 +23,7 @@
 //     block needs it, so most blocks rescale nothing;
 //   * the waves merge through LDS into one partial per workgroup (or straight into the output
 //     when a context is one piece); a second, wide launch merges the pieces' partials, one
-//     workgroup per (sequence, KV head, query row).
+//     lane per (sequence, KV head, query row, 4 dims).
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -473,6 +473,24 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const size_t page_stride = (size_t)a.num_kv_heads * bb;
   const uint8_t* pool_h = a.pool + (size_t)h * bb;
   const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
+  const int nblk_max = (a.max_seq_len + kBlock - 1) / kBlock;
+  const int lgP = a.log2_page;
+  int c0 = g_blk0, first = 0, n_my = 0, my_pid = 0;
+  // Lane kk < 32 holds the physical page of tile 0 of this wave's kk-th block of the chunk, lane
+  // 32 + kk that of tile 1.  The ids are loaded for the blocks below max_seq_len, so the load
+  // does not wait for the sequence length; blocks and tiles past the context are not staged.
+  auto chunk_pages = [&]() {
+    const int c1 = min(c0 + CHUNK, min(g_blk0 + a.blocks_per_split, nblk_max));
+    first = c0 + w;
+    const int n_ids = first < c1 ? (c1 - first + kWavesPerGroup - 1) / kWavesPerGroup : 0;
+    const int kk = lane & 31;
+    const int blk = first + kWavesPerGroup * kk;
+    int tok0 = blk * kBlock + kTile * (lane >> 5);
+    if (tok0 >= a.max_seq_len) tok0 = blk * kBlock;
+    my_pid = pt[kk < n_ids ? tok0 >> lgP : 0];  // every lane loads (entry 0 always exists)
+  };
+  chunk_pages();  // the first chunk's ids load alongside the sequence length and the queries
+
 
   // ---- raw query words: lane holds query row 16*nb + m16 and the 16 dims 16*(4*jj + g) .. +15
   // of each 64-dim step jj (the B-operand layout of QK^T) ----
@@ -500,19 +518,18 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const uint32_t my_stage_lds =
       __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)&s_stage[w][0][0]);
   const uint8_t* my_stage = &s_stage[w][0][0];
-  const int lgP = a.log2_page;
   const uint32_t lane16 = 16u * lane;
   const uint32_t page_stride32 = (uint32_t)page_stride;  // < 2^32, checked on the host
   const ScaleLane sl = scale_lane<D>(P, lane);
-  int c0 = g_blk0, first = 0, n_my = 0, my_pid = 0;
   uint32_t st_issue = my_stage_lds;
   auto issue = [&](int k, uint32_t dst) {
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
       const int blk = first + kWavesPerGroup * k;
       int tok0 = blk * kBlock + kTile * tau;
-      if (tok0 >= Lc) tok0 = blk * kBlock;
-      const int phys = __builtin_amdgcn_readlane(my_pid, 32 * tau + k);
+      const bool past = tok0 >= Lc;  // a tile past the end stages tile 0 again, all of it masked
+      if (past) tok0 = blk * kBlock;
+      const int phys = __builtin_amdgcn_readlane(my_pid, (tau == 1 && !past) ? 32 + k : k);
       stage_tile<D>(pool_h + (uint64_t)(uint32_t)phys * page_stride32, P, tok0 & (P - 1),
                     dst + (uint32_t)(tau * Stage<D>::kTileBytes), lane16, sl);
     }
@@ -520,17 +537,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // stage buffer of block k: k % 3, tracked incrementally
   auto next_stage = [&](uint32_t x) { return x == my_stage_lds + 2 * BS ? my_stage_lds : x + BS; };
   // chunk set-up: this wave's page ids into lanes, then the loads of its first two blocks
-  auto chunk_pages = [&]() {
+  auto chunk_count = [&]() {
     const int c1 = min(c0 + CHUNK, g_blk1);
-    first = c0 + w;
     n_my = first < c1 ? (c1 - first + kWavesPerGroup - 1) / kWavesPerGroup : 0;
-    // lane kk < 32 holds the physical page of tile 0 of this wave's kk-th block of the chunk,
-    // lane 32 + kk that of tile 1 (a tile past the end stages tile 0 again, all of it masked)
-    const int kk = lane & 31;
-    const int blk = first + kWavesPerGroup * kk;
-    int tok0 = blk * kBlock + kTile * (lane >> 5);
-    if (tok0 >= Lc) tok0 = blk * kBlock;
-    my_pid = kk < n_my ? min(max(pt[tok0 >> lgP], 0), a.num_pages - 1) : 0;
+    my_pid = min(max(my_pid, 0), a.num_pages - 1);  // out-of-range ids are clamped, never followed
   };
   auto chunk_start = [&]() {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // page ids in; the DMA counting starts here
@@ -543,7 +553,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // The first chunk's first blocks are in flight while the queries are prepared (an empty split
   // gets n_my = 0).  The query words are used here on every path, so the compiler's own wait for
   // them (loaded with the page ids, one round trip for both) sits here and not after the DMAs.
-  chunk_pages();
+  chunk_count();
   asm volatile("" ::"v"(my_pid));
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
@@ -659,6 +669,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     c0 += CHUNK;
     if (c0 < g_blk1) {
       chunk_pages();
+      chunk_count();
       chunk_start();
     }
   }
@@ -712,73 +723,58 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
 }
 
-// The log-sum-exp merge of the splits: one workgroup per (unit, query row).  Thread (g, q) takes
-// float4 column q of the row for splits g, g + NG, ... (an online max over its own splits), and
-// the NG groups combine through LDS.  Partials come from the previous launch on the stream.
+// The log-sum-exp merge of the splits.  One wave per 64 (unit, query row, 4 dims) items: each
+// lane takes one item over every split, with an online max, so the merge needs no LDS and no
+// barrier and all of a lane's loads of a batch are in flight at once.  The partials come from
+// the previous launch on the stream.
 template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a) {
   constexpr int NQ = D / 4;
-  constexpr int NG = kWave * kWavesPerGroup / NQ;
-  constexpr int U = 8;  // splits per thread in flight at once
-  __shared__ float s_mx[NG];
-  __shared__ float s_den[NG];
-  __shared__ floatx4 s_num[NG][NQ];
+  constexpr int U = 32;  // splits per batch
   const int S = a.splits, R = a.rows;
-  const int unit = blockIdx.x / R, n = blockIdx.x % R;
+  const int items = R * NQ;
+  const int per_unit = (items + kWave - 1) / kWave;
+  const int unit = blockIdx.x / per_unit;
+  const int it = (blockIdx.x % per_unit) * kWave + (int)threadIdx.x;
+  if (it >= items) return;
+  const int n = it / NQ, q = it % NQ;
   const int b = unit / a.num_kv_heads, h = unit % a.num_kv_heads;
-  const int q = threadIdx.x % NQ, grp = threadIdx.x / NQ;
-  const float2* ml = a.ws_ml + (size_t)unit * ml_stride(S, R);
-  const float* part = a.ws_acc + (size_t)unit * S * R * D;
+  const float2* ml = a.ws_ml + (size_t)unit * ml_stride(S, R) + n;
+  const float* part = a.ws_acc + ((size_t)unit * S * R + n) * D + 4 * q;
   float mx = kNegInf, den = 0.0f;
   floatx4 num = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = grp; s0 < S; s0 += U * NG) {
+  for (int s0 = 0; s0 < S; s0 += U) {
     float2 mv[U];
     floatx4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {  // indices clamped into range: all loads issued at once
-      const int sp = min(s0 + u * NG, S - 1);
-      mv[u] = ml[sp * R + n];
-      v[u] = *(const floatx4*)(part + ((size_t)sp * R + n) * D + 4 * q);
+      const int sp = min(s0 + u, S - 1);
+      mv[u] = ml[(size_t)sp * R];
+      v[u] = *(const floatx4*)(part + (size_t)sp * R * D);
     }
+    // the batch's largest max; the running sums move to it (once per batch, exactly)
+    float bm = kNegInf;
+#pragma unroll
+    for (int u = 0; u < U; ++u) bm = s0 + u < S ? fmaxf(bm, mv[u].x) : bm;
+    if (bm > mx) {
+      const float f = __builtin_amdgcn_exp2f(mx - bm);  // 0 while mx is -inf
+      num *= f;
+      den *= f;
+      mx = bm;
+    }
+    const float m_use = mx == kNegInf ? 0.0f : mx;  // no split has seen a token yet
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float m = mv[u].x;
-      if (s0 + u * NG < S && m != kNegInf) {
-        if (m > mx) {
-          const float f = __builtin_amdgcn_exp2f(mx - m);  // 0 while mx is -inf
-          num *= f;
-          den *= f;
-          mx = m;
-        }
-        const float wgt = __builtin_amdgcn_exp2f(m - mx);
-        num += wgt * v[u];
-        den += wgt * mv[u].y;
-      }
+      // a split that saw nothing has max -inf and weight 0
+      const float wgt = s0 + u < S ? __builtin_amdgcn_exp2f(mv[u].x - m_use) : 0.0f;
+      num += wgt * v[u];
+      den += wgt * mv[u].y;
     }
   }
-  if (q == 0) {
-    s_mx[grp] = mx;
-    s_den[grp] = den;
-  }
-  s_num[grp][q] = num;
-  __syncthreads();
-  if (grp == 0) {
-    float M = kNegInf;
-#pragma unroll
-    for (int k = 0; k < NG; ++k) M = fmaxf(M, s_mx[k]);
-    float dt = 0.0f;
-    floatx4 t = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < NG; ++k) {
-      const float f = s_mx[k] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(s_mx[k] - M);
-      t += f * s_num[k][q];
-      dt += f * s_den[k];
-    }
-    const int i = n / a.group, hq = h * a.group + n % a.group;
-    const size_t o = ((size_t)b * a.n_rows + i) * a.n_q_heads + hq;
-    *(floatx4*)(a.out + o * D + 4 * q) = t * (dt > 0.0f ? 1.0f / dt : 0.0f);
-    if (q == 0 && a.lse) a.lse[o] = dt > 0.0f ? (M + log2f(dt)) * 0.69314718055994530942f : kNegInf;
-  }
+  const int i = n / a.group, hq = h * a.group + n % a.group;
+  const size_t o = ((size_t)b * a.n_rows + i) * a.n_q_heads + hq;
+  *(floatx4*)(a.out + o * D + 4 * q) = num * (den > 0.0f ? 1.0f / den : 0.0f);
+  if (q == 0 && a.lse) a.lse[o] = den > 0.0f ? (mx + log2f(den)) * 0.69314718055994530942f : kNegInf;
 }
 
 template <int D>
@@ -791,8 +787,8 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((decode_kernel<D, 2>), dim3(grid), dim3(kWave * kWavesPerGroup), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
-  hipLaunchKernelGGL((merge_kernel<D>), dim3(units * (unsigned)a.rows), dim3(kWave * kWavesPerGroup), 0,
-                     stream, a);
+  const unsigned per_unit = (unsigned)((a.rows * (D / 4) + kWave - 1) / kWave);
+  hipLaunchKernelGGL((merge_kernel<D>), dim3(units * per_unit), dim3(kWave), 0, stream, a);
   return hipGetLastError();
 }
 
