@@ -135,6 +135,8 @@ def main(argv=None):
     ap.add_argument("--copies", type=int, default=8, help="pool copies rotated for a cold cache")
     ap.add_argument("--splits", type=int, default=0, help="0 = automatic split plan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time kvq_append + kvq_decode_attn instead of kvq_decode_step")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -205,18 +207,25 @@ def main(argv=None):
     log(f"[bench] pool {caches[0].pool.numel() / 1e6:.1f} MB x {len(caches)} copies, "
         f"splits {splits}")
 
+    # One step is one kvq_decode_step call (the step's new tokens appended inside the decode
+    # launch); --unfused times kvq_append + kvq_decode_attn instead.
+    k_rows = torch.from_numpy(np.ascontiguousarray(inp.k[:, wl.seq_len - wl.n_new:])).to(dev)
+    v_rows = torch.from_numpy(np.ascontiguousarray(inp.v[:, wl.seq_len - wl.n_new:])).to(dev)
     calls = []
     for c in caches:
-        app = kvq.prepare_append(c, k_new, v_new, s_new, stream=stream) if wl.n_new else None
-        dec = kvq.prepare_decode_attn(c, q, pt, sl, msl, out, lse, ws,
-                                      num_splits=args.splits, stream=stream)
-        calls.append((app, dec))
+        if args.unfused:
+            app = kvq.prepare_append(c, k_new, v_new, s_new, stream=stream) if wl.n_new else None
+            dec = kvq.prepare_decode_attn(c, q, pt, sl, msl, out, lse, ws,
+                                          num_splits=args.splits, stream=stream)
+            calls.append((lambda app=app, dec=dec: (app and app(), dec())))
+        else:
+            calls.append(kvq.prepare_decode_step(c, k_rows if wl.n_new else None,
+                                                 v_rows if wl.n_new else None, q, pt, sl, msl,
+                                                 out, lse, ws, num_splits=args.splits,
+                                                 stream=stream))
 
     def step(i):
-        app, dec = calls[i % len(calls)]
-        if app:
-            app()
-        dec()
+        calls[i % len(calls)]()
 
     for i in range(args.warmup):
         step(i)
@@ -237,25 +246,13 @@ def main(argv=None):
     wall = time.perf_counter() - t_wall
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
-
-    # The decode call alone (its two launches), K calls back to back over the same rotation of
-    # pool copies, bracketed the same way: its mean duration prices the roofline.
-    dec_start = torch.cuda.Event(enable_timing=True)
-    dec_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    dec_start.record(stream)
-    for i in range(args.steps):
-        calls[i % len(calls)][1]()
-    dec_end.record(stream)
-    torch.cuda.synchronize()
-    dec_mean_s = dec_start.elapsed_time(dec_end) * 1e-3 / args.steps
     log(f"[bench] {args.steps} steps in {total_ms:.2f} ms (wall {wall * 1e3:.1f} ms): "
-        f"{ms_per_step * 1e3:.1f} us per step; decode call {dec_mean_s * 1e6:.1f} us")
+        f"{ms_per_step * 1e3:.1f} us per step")
 
     dec_bytes = decode_algorithmic_bytes(wl, inp.seq_lens)
     step_bytes = dec_bytes + (append_algorithmic_bytes(wl) if wl.n_new else 0)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    achieved = dec_bytes / dec_mean_s / 1e9
+    achieved = value  # the step is one call: the attention launch (with the append) + the merge
 
     traffic = None
     pmc_file = os.path.join(ROOT, "profiles", f"decode_{name}_pmc.json")
@@ -304,10 +301,11 @@ def main(argv=None):
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "kvq_decode_attn: decode_kernel (split-KV attention) + merge_kernel "
-                      "(LSE merge of the splits), two launches per call",
-            "algorithmic_bytes_per_launch": dec_bytes,
-            "launch_us_mean": round(dec_mean_s * 1e6, 2),
+            "kernel": ("kvq_append + kvq_decode_attn" if args.unfused else
+                       "kvq_decode_step: decode_kernel (fused append + split-KV attention) + "
+                       "merge_kernel (LSE merge of the splits)"),
+            "algorithmic_bytes_per_launch": step_bytes,
+            "launch_us_mean": round(ms_per_step * 1e3, 2),
         },
     }
 

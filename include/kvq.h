@@ -49,6 +49,7 @@ extern "C" {
 #define KVQ_TILE_TOKENS     16
 #define KVQ_MAX_ROWS_PER_KV 32
 #define KVQ_MAX_N_ROWS      4
+#define KVQ_MAX_STEP_TOKENS 64
 
 /* ---- quantization (defined by this library; the pages give only "K8/V4") ---------------
  * Per token and KV head, with inputs in fp32:
@@ -143,6 +144,31 @@ int kvq_decode_attn(const void* pool, int32_t num_pages, int32_t page_size,
                     int32_t num_kv_heads, int32_t head_dim, const uint16_t* q,
                     const int32_t* page_table, const int32_t* seq_lens, int32_t n_seq,
                     int32_t n_rows, int32_t n_q_heads, int32_t max_pages_per_seq,
+                    int32_t max_seq_len, float softmax_scale, int32_t num_splits, float* out,
+                    float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- kvq_decode_step ---------------------------------------------------------------------
+ * One decode step in one call: kvq_append of each sequence's newest n_new tokens, then
+ * kvq_decode_attn over the cache that now holds them.  The result (pool bytes, out, lse) is the
+ * same as those two calls with slot_mapping taken from the page table, so the appended tokens
+ * must be the last n_new of each sequence: token L - n_new + j of sequence b (L = seq_lens[b])
+ * gets k_new[b][j], v_new[b][j] and is written to page page_table[b][t / page_size], slot
+ * t % page_size.  (An MTP verify step appends its 1 + 3 rows' tokens this way, forum post
+ * "3090 单卡跑 Qwen3.8-27B：NInfer 上机实测（180K 上下文 / C2 并发 / 4bit KV）", 一、部署,
+ * launch-flag table.)  Each new token is quantized by the workgroup that attends its block, before
+ * that block is read, so the step needs no separate append launch.
+ *   pool          as for kvq_decode_attn, but written (the new tokens' slots only).
+ *   k_new, v_new  device fp32 [n_seq][n_new][num_kv_heads][head_dim], contiguous; may be NULL
+ *                 when n_new = 0.
+ *   n_new         0 .. KVQ_MAX_STEP_TOKENS, and n_new <= L for every sequence (tokens at
+ *                 negative positions are skipped).
+ *   other arguments as for kvq_decode_attn (the workspace need is the same).
+ * Returns KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE or KVQ_ERR_HIP.
+ */
+int kvq_decode_step(void* pool, int32_t num_pages, int32_t page_size, int32_t num_kv_heads,
+                    int32_t head_dim, const float* k_new, const float* v_new, int32_t n_new,
+                    const uint16_t* q, const int32_t* page_table, const int32_t* seq_lens,
+                    int32_t n_seq, int32_t n_rows, int32_t n_q_heads, int32_t max_pages_per_seq,
                     int32_t max_seq_len, float softmax_scale, int32_t num_splits, float* out,
                     float* lse, void* workspace, size_t workspace_bytes, void* stream);
 

@@ -119,12 +119,16 @@ int kvq_append(void* pool, int32_t num_pages, int32_t page_size, int32_t num_kv_
   return kvq::launch_append(head_dim, a, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
-int kvq_decode_attn(const void* pool, int32_t num_pages, int32_t page_size,
-                    int32_t num_kv_heads, int32_t head_dim, const uint16_t* q,
-                    const int32_t* page_table, const int32_t* seq_lens, int32_t n_seq,
-                    int32_t n_rows, int32_t n_q_heads, int32_t max_pages_per_seq,
-                    int32_t max_seq_len, float softmax_scale, int32_t num_splits, float* out,
-                    float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int decode_impl(const void* pool, int32_t num_pages, int32_t page_size, int32_t num_kv_heads,
+                int32_t head_dim, const float* k_new, const float* v_new, int32_t n_new,
+                const uint16_t* q, const int32_t* page_table, const int32_t* seq_lens, int32_t n_seq,
+                int32_t n_rows, int32_t n_q_heads, int32_t max_pages_per_seq, int32_t max_seq_len,
+                float softmax_scale, int32_t num_splits, float* out, float* lse, void* workspace,
+                size_t workspace_bytes, void* stream) {
   int rc = pool_args_ok(pool, num_pages, page_size, num_kv_heads, head_dim);
   if (rc != KVQ_OK) return rc;
   if (!q || !page_table || !seq_lens || !out) return KVQ_ERR_ARG;
@@ -171,8 +175,40 @@ int kvq_decode_attn(const void* pool, int32_t num_pages, int32_t page_size,
   a.ws_ml = (float2*)((char*)a.ws_acc + (size_t)units * plan.splits * rows * head_dim * sizeof(float));
   a.out = out;
   a.lse = lse;
+  a.pool_rw = (uint8_t*)pool;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.n_new = n_new;
   (void)hipGetLastError();
   return kvq::launch_decode(head_dim, a, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvq_decode_attn(const void* pool, int32_t num_pages, int32_t page_size,
+                    int32_t num_kv_heads, int32_t head_dim, const uint16_t* q,
+                    const int32_t* page_table, const int32_t* seq_lens, int32_t n_seq,
+                    int32_t n_rows, int32_t n_q_heads, int32_t max_pages_per_seq,
+                    int32_t max_seq_len, float softmax_scale, int32_t num_splits, float* out,
+                    float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(pool, num_pages, page_size, num_kv_heads, head_dim, nullptr, nullptr, 0, q,
+                     page_table, seq_lens, n_seq, n_rows, n_q_heads, max_pages_per_seq, max_seq_len,
+                     softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
+}
+
+int kvq_decode_step(void* pool, int32_t num_pages, int32_t page_size, int32_t num_kv_heads,
+                    int32_t head_dim, const float* k_new, const float* v_new, int32_t n_new,
+                    const uint16_t* q, const int32_t* page_table, const int32_t* seq_lens,
+                    int32_t n_seq, int32_t n_rows, int32_t n_q_heads, int32_t max_pages_per_seq,
+                    int32_t max_seq_len, float softmax_scale, int32_t num_splits, float* out,
+                    float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_new < 0 || n_new > KVQ_MAX_STEP_TOKENS) return KVQ_ERR_ARG;
+  if (n_new > 0 && (!k_new || !v_new)) return KVQ_ERR_ARG;
+  return decode_impl(pool, num_pages, page_size, num_kv_heads, head_dim, k_new, v_new, n_new, q,
+                     page_table, seq_lens, n_seq, n_rows, n_q_heads, max_pages_per_seq, max_seq_len,
+                     softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -1,43 +1,13 @@
-// kvq_append.hip — quantize new tokens' K/V rows and write them into their cache slots.
-//
-// K8/V4 ("rk8v4" in the launch-flag table of the forum post "3090 单卡跑 Qwen3.8-27B：NInfer
-// 上机实测（180K 上下文 / C2 并发 / 4bit KV）", 一、部署): K as int8 with one fp16 scale per token
-// and KV head, V as 4-bit codes with one fp16 scale per 32 dims, the granularity and rounding
-// the library header defines.  One 64-lane wave quantizes one (token, KV head): each lane holds
-// D/64 consecutive dims, the absmax reductions are wave shuffles, and every byte written belongs
-// to this token alone, so concurrent tokens never touch the same byte.
-#include "kvq_internal.h"
+// kvq_append.hip — quantize new tokens' K/V rows and write them into their cache slots: one
+// 64-lane wave per (token, KV head), the row quantizer of kvq_quant.h.  Every byte written
+// belongs to its token alone, so concurrent tokens never touch the same byte.
+#include "kvq_quant.h"
 
 namespace kvq {
 namespace {
 
-__device__ inline float wave_max(float x, int width) {
-  // butterfly over groups of `width` lanes (width a power of two <= 64)
-  for (int off = width / 2; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));
-  return x;
-}
-
-// fp16 scale of one group: round-to-nearest-even of the fp32 quotient, saturated to the largest
-// finite fp16.  Returns the fp16 bits; *s receives its value in fp32.
-__device__ inline uint16_t group_scale(float absmax, float qmax, float* s) {
-  float s32 = absmax / qmax;  // IEEE fp32 division (built with correctly rounded divide)
-  _Float16 h = (_Float16)s32;  // v_cvt_f16_f32: round to nearest even
-  uint16_t bits = __builtin_bit_cast(uint16_t, h);
-  if ((bits & 0x7FFF) == 0x7C00) bits = 0x7BFF;
-  *s = (float)__builtin_bit_cast(_Float16, bits);
-  return bits;
-}
-
-__device__ inline int quantize_one(float x, float s, float qmax) {
-  if (s == 0.0f) return 0;
-  float c = __builtin_rintf(x / s);  // IEEE divide, round half to even
-  c = fminf(fmaxf(c, -qmax), qmax);
-  return (int)c;
-}
-
 template <int D>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
-  constexpr int E = D / kWave;  // dims per lane: 1, 2 or 4
   const int lane = threadIdx.x & (kWave - 1);
   const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= (long long)a.n_tok * a.num_kv_heads) return;
@@ -48,67 +18,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   if (slot < 0 || slot >= (long long)a.num_pages * P) return;  // padding / out of pool: skip
   const int page = (int)(slot / P), s = (int)(slot % P);
   uint8_t* blk = a.pool + ((size_t)page * a.num_kv_heads + h) * block_bytes(P, D);
-  const int tile = s / kTile, t = s % kTile;
-  const int d0 = lane * E;
-
-  const float* krow = a.k + ((size_t)n * a.num_kv_heads + h) * D + d0;
-  const float* vrow = a.v + ((size_t)n * a.num_kv_heads + h) * D + d0;
-  float kx[E], vx[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    kx[e] = krow[e];
-    vx[e] = vrow[e];
-  }
-
-  // ---- K: one scale per token and head (qmax 127) ----
-  float ka = 0.0f;
-#pragma unroll
-  for (int e = 0; e < E; ++e) ka = fmaxf(ka, fabsf(kx[e]));
-  ka = wave_max(ka, kWave);
-  float ks;
-  const uint16_t ks_bits = group_scale(ka, 127.0f, &ks);
-  uint32_t kpacked = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) kpacked |= (uint32_t)(quantize_one(kx[e], ks, 127.0f) & 0xFF) << (8 * e);
-  // K code (t, d) at 16*D*tile + 256*(d/16) + 16*t + d%16; E consecutive dims stay in one chunk
-  uint8_t* kdst = blk + (size_t)16 * D * tile + 256 * (d0 / 16) + 16 * t + d0 % 16;
-  if constexpr (E == 4) {
-    *(uint32_t*)kdst = kpacked;
-  } else if constexpr (E == 2) {
-    *(uint16_t*)kdst = (uint16_t)kpacked;
-  } else {
-    *kdst = (uint8_t)kpacked;
-  }
-  if (lane == 0) *(uint16_t*)(blk + k_scales_at(P, D) + 2 * s) = ks_bits;
-
-  // ---- V: one scale per 32 dims (qmax 7), 32/E lanes per group ----
-  float va = 0.0f;
-#pragma unroll
-  for (int e = 0; e < E; ++e) va = fmaxf(va, fabsf(vx[e]));
-  va = wave_max(va, 32 / E);
-  float vsc;
-  const uint16_t vs_bits = group_scale(va, 7.0f, &vsc);
-  uint32_t vnib = 0;  // E nibbles, dim d0+e at bits 4e
-#pragma unroll
-  for (int e = 0; e < E; ++e) vnib |= (uint32_t)(quantize_one(vx[e], vsc, 7.0f) & 0xF) << (4 * e);
-  const int j = d0 / 32;
-  if (d0 % 32 == 0) *(uint16_t*)(blk + v_scales_at(P, D) + 2 * ((size_t)s * (D / 32) + j)) = vs_bits;
-
-  // Dims d (d/16 even) and d+16 share a byte (low / high nibble).  The lane holding d gets the
-  // partner's nibbles from 16/E lanes up and writes the E bytes.
-  const uint32_t partner = __shfl_down(vnib, 16 / E, kWave);
-  if (((d0 / 16) & 1) == 0) {
-    constexpr int w = (D / 32) < 4 ? (D / 32) : 4;
-    const int r = t % 4;
-    uint8_t* vbase = blk + v_codes_at(P, D) + (size_t)8 * D * tile + 256 * w * (j / w) + 4 * (j % w) + r;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int d = d0 + e;
-      const int vlane = 16 * (t / 4) + d % 16;
-      const uint8_t byte = (uint8_t)(((vnib >> (4 * e)) & 0xF) | (((partner >> (4 * e)) & 0xF) << 4));
-      vbase[4 * w * vlane] = byte;
-    }
-  }
+  const size_t row = ((size_t)n * a.num_kv_heads + h) * D;
+  append_row<D>(blk, P, s, a.k + row, a.v + row, lane);
 }
 
 }  // namespace

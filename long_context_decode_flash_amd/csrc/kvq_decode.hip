@@ -24,7 +24,7 @@
 //   * the waves merge through LDS into one partial per workgroup (or straight into the output
 //     when a context is one piece); a second, wide launch merges the pieces' partials, one
 //     lane per (sequence, KV head, query row, 4 dims).
-#include "kvq_internal.h"
+#include "kvq_quant.h"
 
 namespace kvq {
 namespace {
@@ -553,6 +553,18 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // The first chunk's first blocks are in flight while the queries are prepared (an empty split
   // gets n_my = 0).  The query words are used here on every path, so the compiler's own wait for
   // them (loaded with the page ids, one round trip for both) sits here and not after the DMAs.
+  // Fused append: the wave that will stage the block of a new token quantizes the token's K/V
+  // rows (this KV head) into its slot first; chunk_start's wait covers the stores, so the
+  // block's loads see them.
+  for (int j = 0; j < a.n_new; ++j) {
+    const int t = L - a.n_new + j;
+    const int blk = t >> 5;
+    if (t < 0 || blk < g_blk0 || blk >= g_blk1 || ((blk - g_blk0) & (kWavesPerGroup - 1)) != w) continue;
+    const int page = min(max(pt[t >> lgP], 0), a.num_pages - 1);
+    const size_t row = (((size_t)b * a.n_new + j) * a.num_kv_heads + h) * D;
+    append_row<D>(a.pool_rw + ((size_t)page * a.num_kv_heads + h) * bb, P, t & (P - 1), a.k_new + row,
+                  a.v_new + row, lane);
+  }
   chunk_count();
   asm volatile("" ::"v"(my_pid));
 #pragma unroll

@@ -53,6 +53,12 @@ struct DecodeArgs {
   float2* ws_ml;     // [units][ml_stride(splits, rows)] (max in log2 units, sum of exp2)
   float* out;
   float* lse;
+  // fused append (kvq_decode_step): the last n_new tokens of each sequence, fp32
+  // [n_seq][n_new][num_kv_heads][D], quantized into their slots before they are attended
+  uint8_t* pool_rw;
+  const float* k_new;
+  const float* v_new;
+  int n_new;
 };
 
 hipError_t launch_append(int head_dim, const AppendArgs& a, hipStream_t stream);

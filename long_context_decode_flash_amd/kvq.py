@@ -20,6 +20,7 @@ KVQ_ERR_ARG = -1
 KVQ_ERR_UNSUPPORTED = -2
 KVQ_ERR_WORKSPACE = -3
 KVQ_ERR_HIP = -4
+KVQ_MAX_STEP_TOKENS = 64
 
 _lock = threading.Lock()
 _lib = None
@@ -57,6 +58,9 @@ def lib():
         L.kvq_decode_attn.argtypes = [P, I, I, I, I, P, P, P, I, I, I, I, I, ctypes.c_float, I,
                                       P, P, P, ctypes.c_size_t, P]
         L.kvq_decode_attn.restype = ctypes.c_int
+        L.kvq_decode_step.argtypes = [P, I, I, I, I, P, P, I, P, P, P, I, I, I, I, I,
+                                      ctypes.c_float, I, P, P, P, ctypes.c_size_t, P]
+        L.kvq_decode_step.restype = ctypes.c_int
         _lib = L
         return L
 
@@ -178,6 +182,72 @@ def decode_attn(cache: PagedCache, q: torch.Tensor, page_table: torch.Tensor,
     if rc != KVQ_OK:
         raise KVQError(rc, "kvq_decode_attn")
     return out, lse
+
+
+def _step_args(cache, k_new, v_new, q, page_table, seq_lens, max_seq_len, out, lse, workspace,
+               softmax_scale, num_splits, stream):
+    n_seq, n_rows, n_q_heads, D = (int(x) for x in q.shape)
+    if D != cache.head_dim or tuple(out.shape) != (n_seq, n_rows, n_q_heads, D):
+        raise ValueError("q / out shapes do not match the cache")
+    if k_new is None or k_new.numel() == 0:
+        n_new, kp, vp = 0, None, None
+    else:
+        n_new = int(k_new.shape[1])
+        shape = (n_seq, n_new, cache.num_kv_heads, D)
+        if tuple(k_new.shape) != shape or tuple(v_new.shape) != shape:
+            raise ValueError(f"k_new and v_new must be {shape}")
+        kp, vp = _dev(k_new, "k_new", torch.float32), _dev(v_new, "v_new", torch.float32)
+    return (_dev(cache.pool, "pool", torch.uint8), cache.num_pages, cache.page_size,
+            cache.num_kv_heads, D, kp, vp, n_new, _dev(q, "q", torch.float16),
+            _dev(page_table, "page_table", torch.int32), _dev(seq_lens, "seq_lens", torch.int32),
+            n_seq, n_rows, n_q_heads, int(page_table.shape[1]), int(max_seq_len),
+            float(softmax_scale), int(num_splits), _dev(out, "out", torch.float32),
+            _dev(lse, "lse", torch.float32) if lse is not None else None,
+            _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream_ptr(stream))
+
+
+def decode_step(cache: PagedCache, k_new: torch.Tensor | None, v_new: torch.Tensor | None,
+                q: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                max_seq_len: int, *, softmax_scale: float = 0.0, num_splits: int = 0,
+                out: torch.Tensor | None = None, want_lse: bool = True,
+                lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                stream=None):
+    """kvq_decode_step: append each sequence's newest n_new tokens (k_new, v_new fp32
+    [n_seq][n_new][Hkv][D], the last n_new of seq_lens[b]) and attend, in one call.
+    Returns (out, lse) as decode_attn."""
+    n_seq, n_rows, n_q_heads, D = (int(x) for x in q.shape)
+    dev = q.device
+    if out is None:
+        out = torch.empty((n_seq, n_rows, n_q_heads, D), dtype=torch.float32, device=dev)
+    if want_lse and lse is None:
+        lse = torch.empty((n_seq, n_rows, n_q_heads), dtype=torch.float32, device=dev)
+    if workspace is None:
+        need = decode_workspace_bytes(n_seq, n_rows, n_q_heads, cache.num_kv_heads, D,
+                                      max_seq_len, num_splits)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    rc = lib().kvq_decode_step(*_step_args(cache, k_new, v_new, q, page_table, seq_lens,
+                                           max_seq_len, out, lse, workspace, softmax_scale,
+                                           num_splits, stream))
+    if rc != KVQ_OK:
+        raise KVQError(rc, "kvq_decode_step")
+    return out, lse
+
+
+def prepare_decode_step(cache: PagedCache, k_new: torch.Tensor | None, v_new: torch.Tensor | None,
+                        q: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                        max_seq_len: int, out: torch.Tensor, lse: torch.Tensor | None,
+                        workspace: torch.Tensor, *, softmax_scale: float = 0.0,
+                        num_splits: int = 0, stream=None):
+    """Marshal the arguments of one kvq_decode_step once; the returned callable re-issues it."""
+    args = _step_args(cache, k_new, v_new, q, page_table, seq_lens, max_seq_len, out, lse,
+                      workspace, softmax_scale, num_splits, stream)
+    fn = lib().kvq_decode_step
+
+    def call():
+        rc = fn(*args)
+        if rc != KVQ_OK:
+            raise KVQError(rc, "kvq_decode_step")
+    return call
 
 
 def prepare_append(cache: PagedCache, k: torch.Tensor, v: torch.Tensor,

@@ -135,6 +135,28 @@ class Inputs:
         return (np.ascontiguousarray(np.concatenate(ks)), np.ascontiguousarray(np.concatenate(vs)),
                 np.concatenate(ss))
 
+    def ragged_split(self, n_new: int):
+        """For ragged lengths: the tokens cached before a step that appends each sequence's last
+        n_new tokens, as (k, v, slots) flattened like token_range; and those new tokens, both as
+        the same flattened triple and as (k_new, v_new) fp32 [n_seq][n_new][Hkv][D]."""
+        wl = self.wl
+        pre = ([], [], [])
+        new = ([], [], [])
+        k_new = np.zeros((wl.n_seq, n_new, wl.num_kv_heads, wl.head_dim), np.float32)
+        v_new = np.zeros_like(k_new)
+        for s in range(wl.n_seq):
+            n = int(self.seq_lens[s])
+            t0 = max(n - n_new, 0)
+            for dst, a, b in ((pre, 0, t0), (new, t0, n)):
+                dst[0].append(self.k[s, a:b])
+                dst[1].append(self.v[s, a:b])
+                dst[2].append(slots_for(self.page_table, wl.page_size, s, a, b))
+            k_new[s, n_new - (n - t0):] = self.k[s, t0:n]
+            v_new[s, n_new - (n - t0):] = self.v[s, t0:n]
+        flat = lambda t: (np.ascontiguousarray(np.concatenate(t[0])),
+                          np.ascontiguousarray(np.concatenate(t[1])), np.concatenate(t[2]))
+        return flat(pre), flat(new), k_new, v_new
+
     def prefill(self):
         """Tokens already in the cache before the step: [0, seq_len - n_new)."""
         return self.token_range(0, self.wl.seq_len - self.wl.n_new)

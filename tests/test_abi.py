@@ -157,3 +157,25 @@ def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(kvq, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         kvq.lib()
+
+
+def step_rc(lib, **kw):
+    a = dict(pool=FAKE, num_pages=8, page_size=16, hkv=2, d=64, k=FAKE, v=FAKE, n_new=1, q=FAKE,
+             pt=FAKE, sl=FAKE, n_seq=1, n_rows=1, hq=4, max_pages=8, max_seq_len=100, scale=0.0,
+             splits=0, out=FAKE, lse=None, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return lib.kvq_decode_step(a["pool"], a["num_pages"], a["page_size"], a["hkv"], a["d"],
+                               a["k"], a["v"], a["n_new"], a["q"], a["pt"], a["sl"], a["n_seq"],
+                               a["n_rows"], a["hq"], a["max_pages"], a["max_seq_len"], a["scale"],
+                               a["splits"], a["out"], a["lse"], a["ws"], a["ws_bytes"], None)
+
+
+def test_decode_step_validation(lib):
+    assert step_rc(lib, n_new=-1) == kvq.KVQ_ERR_ARG
+    assert step_rc(lib, n_new=kvq.KVQ_MAX_STEP_TOKENS + 1) == kvq.KVQ_ERR_ARG
+    assert step_rc(lib, k=None) == kvq.KVQ_ERR_ARG
+    assert step_rc(lib, v=None) == kvq.KVQ_ERR_ARG
+    # the decode checks apply as for kvq_decode_attn
+    assert step_rc(lib, pool=None) == kvq.KVQ_ERR_ARG
+    assert step_rc(lib, d=32) == kvq.KVQ_ERR_UNSUPPORTED
+    assert step_rc(lib, ws=None) == kvq.KVQ_ERR_WORKSPACE

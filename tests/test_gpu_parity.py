@@ -262,3 +262,77 @@ def test_decode_workspace_reused_across_shapes():
                 out_r, _ = H.oracle_decode(inp, H.oracle_fill(inp))
                 assert H.report(f"  rep {rep} splits {splits} {wl.head_dim}", out.cpu().numpy(),
                                 out_r) <= H.TOL_ABS
+
+
+# kvq_decode_step (append of each sequence's newest tokens fused into the decode launch) must
+# leave the same pool bytes and return the same bits as kvq_append followed by kvq_decode_attn.
+STEP_CASES = [
+    dict(n_seq=2, seq_lens=(1000, 333), num_kv_heads=2, n_q_heads=12, head_dim=256,
+         page_size=64, n_rows=1, n_new=1, splits=0, seed=51),
+    # MTP verify: 4 new tokens across a 32-token block edge that is also a split edge (7 splits
+    # of 6 blocks over 37 blocks put blocks 35 and 36 in different workgroups)
+    dict(n_seq=1, seq_lens=(1154,), num_kv_heads=4, n_q_heads=24, head_dim=256, page_size=64,
+         n_rows=4, n_new=4, splits=7, seed=52),
+    # ragged, a sequence barely longer than its new tokens, head_dim 64, page 16
+    dict(n_seq=3, seq_lens=(70, 5, 260), num_kv_heads=1, n_q_heads=4, head_dim=64,
+         page_size=16, n_rows=2, n_new=3, splits=0, seed=53),
+    dict(n_seq=1, seq_lens=(500,), num_kv_heads=2, n_q_heads=8, head_dim=128, page_size=32,
+         n_rows=1, n_new=0, splits=2, seed=54),
+    # one split per context (the attention kernel writes the output itself)
+    dict(n_seq=2, seq_lens=(40, 64), num_kv_heads=2, n_q_heads=4, head_dim=128, page_size=16,
+         n_rows=1, n_new=2, splits=1, seed=55),
+]
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=[f"step{i}" for i in range(len(STEP_CASES))])
+def test_decode_step_equals_append_then_decode(case):
+    import torch
+    kvq = H.kvq()
+    c = dict(case)
+    n_new, splits = c.pop("n_new"), c.pop("splits")
+    H.say(f"[decode_step] {case}")
+    inp = W.custom(**c)
+    pre, new, k_new, v_new = inp.ragged_split(n_new)
+    q = H.to_dev(inp.q_bits).view(torch.float16)
+    pt, sl = H.to_dev(inp.page_table), H.to_dev(inp.seq_lens)
+    msl = int(inp.seq_lens.max())
+    a = H.gpu_cache(inp)
+    H.gpu_append(a, *pre)
+    H.gpu_append(a, *new)
+    out_a, lse_a = kvq.decode_attn(a, q, pt, sl, msl, num_splits=splits)
+    b = H.gpu_cache(inp)
+    H.gpu_append(b, *pre)
+    kn = H.to_dev(k_new) if n_new else None
+    vn = H.to_dev(v_new) if n_new else None
+    out_b, lse_b = kvq.decode_step(b, kn, vn, q, pt, sl, msl, num_splits=splits)
+    torch.cuda.synchronize()
+    assert torch.equal(a.pool, b.pool), "pool bytes differ from append + decode"
+    assert torch.equal(out_a, out_b) and torch.equal(lse_a, lse_b)
+    out_r, lse_r = H.oracle_decode(inp, H.oracle_fill(inp))
+    assert np.array_equal(b.pool.cpu().numpy(), H.oracle_fill(inp))
+    assert H.report("  step out", out_b.cpu().numpy(), out_r) <= H.TOL_ABS
+    np.testing.assert_allclose(lse_b.cpu().numpy(), lse_r, rtol=0, atol=1e-4)
+
+
+def test_decode_step_full_size_headline():
+    """The 184,320-token two-sequence step through kvq_decode_step: same pool bytes and bits
+    as kvq_append + kvq_decode_attn."""
+    import torch
+    kvq = H.kvq()
+    wl = W.WORKLOADS["ctx184k_c2"]
+    H.say("[decode_step full size]")
+    inp = W.generate(wl)
+    k_new = inp.k[:, wl.seq_len - wl.n_new:]
+    v_new = inp.v[:, wl.seq_len - wl.n_new:]
+    q = H.to_dev(inp.q_bits).view(torch.float16)
+    pt, sl = H.to_dev(inp.page_table), H.to_dev(inp.seq_lens)
+    a = H.gpu_cache(inp)
+    H.gpu_append(a, *inp.prefill())
+    b = H.gpu_cache(inp)
+    b.pool.copy_(a.pool)
+    H.gpu_append(a, *inp.step_tokens())
+    out_a, lse_a = kvq.decode_attn(a, q, pt, sl, wl.seq_len)
+    out_b, lse_b = kvq.decode_step(b, H.to_dev(k_new), H.to_dev(v_new), q, pt, sl, wl.seq_len)
+    torch.cuda.synchronize()
+    assert torch.equal(a.pool, b.pool)
+    assert torch.equal(out_a, out_b) and torch.equal(lse_a, lse_b)
