@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark of the paged K8/V4 decode step on one MI355X.
 
-A step is one pass of the whole hot path over one batch: ``kvq_append`` of the step's new
-tokens (quantize + paged write) followed by ``kvq_decode_attn`` (split-KV attention + merge)
-for every sequence, query head and query row.  The default workload is the 184,320-token KV
+A step is one pass of the whole hot path over one batch: one ``kvq_decode_step`` call, which
+quantizes the step's new tokens into their slots and runs split-KV attention over every
+sequence, query head and query row (one launch), then merges the splits (a second, small
+launch).  ``--unfused`` times ``kvq_append`` followed by ``kvq_decode_attn`` instead.  The default workload is the 184,320-token KV
 pool shared by two 92,160-token sequences (4 KV heads, 24 query heads, head_dim 256, page 64,
 interleaved random page tables), the shape of the forum post "3090 单卡跑 Qwen3.8-27B：NInfer
 上机实测（180K 上下文 / C2 并发 / 4bit KV）" (一、部署, launch-flag table: 184,320-token pool,
@@ -67,21 +68,27 @@ def append_algorithmic_bytes(wl) -> int:
     return n * wl.num_kv_heads * (2 * wl.head_dim * 4 + token_bytes(wl.head_dim)) + n * 4
 
 
-def cpu_baseline(wl, inp):
-    """The oracle, as it is, on one full step of the workload on the host cores."""
+def cpu_baseline(wl, inp, min_seconds=10.0):
+    """The oracle, as it is, on full steps of the workload on the host cores, repeated until
+    min_seconds have passed (the step's append writes the same slots each time).  Returns the
+    mean seconds per step, the steps run and the threads used."""
     import oracle
     pool = oracle.new_pool(wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim)
     t0 = time.perf_counter()
     oracle.append(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
                   *inp.prefill())
     log(f"[cpu] oracle prefill {time.perf_counter() - t0:.1f}s (not timed)")
+    steps = 0
     t0 = time.perf_counter()
-    oracle.append(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
-                  *inp.step_tokens())
-    oracle.decode_attn(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
-                       inp.q_bits, inp.page_table, inp.seq_lens, wl.n_rows, wl.n_q_heads)
-    dt = time.perf_counter() - t0
-    return dt, oracle.num_threads()
+    while True:
+        oracle.append(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
+                      *inp.step_tokens())
+        oracle.decode_attn(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
+                           inp.q_bits, inp.page_table, inp.seq_lens, wl.n_rows, wl.n_q_heads)
+        steps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            return dt / steps, steps, oracle.num_threads()
 
 
 def _counter_rows(path):
@@ -111,8 +118,9 @@ def ingest_pmc(fetch_csv, write_csv, workload, probe_mib, commands):
     return out
 
 
-def ingest_trace(stats_csv, command):
-    """Markdown summary of a rocprofv3 --kernel-trace --stats run."""
+def ingest_trace(stats_csv, command, bench_log=None):
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run of bench.py, with the step time
+    bench.py itself printed in that run (bench_log) beside the kernels' summed averages."""
     rows = _counter_rows(stats_csv)
     lines = ["# Kernel trace summary", "", "Command:", "", "```", command, "```", "",
              "| kernel | calls | average us | min us | max us | % of GPU time |",
@@ -123,6 +131,16 @@ def ingest_trace(stats_csv, command):
         lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{float(r['Percentage']):.2f} |")
+    step_us = sum(float(r["AverageNs"]) / 1e3 for r in rows
+                  if "decode_kernel" in r["Name"] or "merge_kernel" in r["Name"])
+    lines += ["", f"Sum of the step's kernel averages (decode_kernel + merge_kernel): {step_us:.2f} us."]
+    if bench_log:
+        with open(bench_log) as f:
+            js = [json.loads(x) for x in f if x.startswith("{")]
+        if js:
+            lines.append(f"bench.py's own line in the same profiled run: {js[-1]['ms_per_step'] * 1e3:.2f} us "
+                         "per step (the profiler slows every launch; the unprofiled step time is the "
+                         "bench line's ms_per_step).")
     return "\n".join(lines) + "\n"
 
 
@@ -144,6 +162,8 @@ def main(argv=None):
     ap.add_argument("--ingest-trace", metavar="KERNEL_STATS_CSV",
                     help="write a markdown summary of a rocprofv3 kernel-stats CSV to profiles/")
     ap.add_argument("--command", default="", help="command line recorded with an ingested profile")
+    ap.add_argument("--bench-log", default=None,
+                    help="stdout of bench.py in the profiled run (its JSON line), for --ingest-trace")
     args = ap.parse_args(argv)
 
     if args.ingest_pmc or args.ingest_trace:
@@ -159,14 +179,15 @@ def main(argv=None):
         else:
             path = os.path.join(ROOT, "profiles", f"decode_{name}_kernel_trace.md")
             with open(path, "w") as f:
-                f.write(ingest_trace(args.ingest_trace, args.command))
+                f.write(ingest_trace(args.ingest_trace, args.command, args.bench_log))
         print(path)
         return 0
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
-              "multi-GPU path: the decode shards by KV head or sequence with no exchange, see "
-              "DESIGN.md.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): there is no "
+              "multi-GPU path here (the decode would shard by KV head or by sequence, with one "
+              "partial per row exchanged only when a sequence is cut across GPUs).",
+              file=sys.stderr)
         return 2
 
     import torch
@@ -310,16 +331,16 @@ def main(argv=None):
     }
 
     if not args.no_cpu_baseline:
-        log("[bench] cpu baseline: oracle on one full step")
-        dt, cores = cpu_baseline(wl, inp)
+        log("[bench] cpu baseline: oracle on full steps, about 10 s")
+        dt, n_cpu, cores = cpu_baseline(wl, inp)
         res["cpu_baseline"] = {
             "value": round(step_bytes / dt / 1e9, 4),
             "unit": "GB/s",
             "cores": cores,
             "kind": "oracle",
-            "sample": f"one full step of {name} (append of {wl.n_seq * wl.n_new} tokens + "
-                      f"attention of all {wl.n_seq * wl.n_rows * wl.n_q_heads} output rows over "
-                      f"{wl.seq_len} tokens each), fp64, {dt:.2f} s",
+            "sample": f"{n_cpu} full steps of {name} (each: append of {wl.n_seq * wl.n_new} "
+                      f"tokens + attention of all {wl.n_seq * wl.n_rows * wl.n_q_heads} output rows "
+                      f"over {wl.seq_len} tokens each), fp64, {dt * n_cpu:.1f} s in all",
             "s_per_step": round(dt, 3),
         }
     print(json.dumps(res), flush=True)
