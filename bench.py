@@ -205,9 +205,30 @@ def main(argv=None):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     caches = [kvq.PagedCache.allocate(wl.pool_pages, wl.page_size, wl.num_kv_heads, D, dev)]
-    k_pre, v_pre, s_pre = inp.prefill()
-    kvq.append(caches[0], dev_t(k_pre), dev_t(v_pre), dev_t(s_pre))
-    del k_pre, v_pre
+    k_pre, v_pre, s_pre = (dev_t(x) for x in inp.prefill())
+    # The prefill append (one kvq_append call per sequence, over all its cached tokens, as an
+    # engine's prefill writes them) is timed too: once to fill the pool, then `reps` more times
+    # over the same slots (idempotent), event-timed.
+    n_pre = int(s_pre.numel())
+    per = n_pre // wl.n_seq  # tokens are sequence-major, the same count per sequence
+    apps = [kvq.prepare_append(caches[0], k_pre[i * per:(i + 1) * per], v_pre[i * per:(i + 1) * per],
+                               s_pre[i * per:(i + 1) * per]) for i in range(wl.n_seq)]
+    for app in apps:
+        app()
+    torch.cuda.synchronize()
+    reps = 5
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        for app in apps:
+            app()
+    e1.record()
+    torch.cuda.synchronize()
+    prefill_us = e0.elapsed_time(e1) * 1e3 / reps
+    prefill_bytes = n_pre * wl.num_kv_heads * (2 * D * 4 + token_bytes(D)) + n_pre * 4
+    log(f"[bench] prefill append of {n_pre} tokens: {prefill_us:.1f} us, "
+        f"{prefill_bytes / prefill_us / 1e3:.0f} GB/s")
+    del k_pre, v_pre, apps
     for _ in range(args.copies - 1):
         c = kvq.PagedCache.allocate(wl.pool_pages, wl.page_size, wl.num_kv_heads, D, dev)
         c.pool.copy_(caches[0].pool)
@@ -330,6 +351,14 @@ def main(argv=None):
         },
     }
 
+    res["prefill_append"] = {
+        "tokens": n_pre,
+        "us": round(prefill_us, 1),
+        "algorithmic_bytes": prefill_bytes,
+        "GB_s": round(prefill_bytes / prefill_us / 1e3, 1),
+        "frac_of_hbm_peak": round(prefill_bytes / prefill_us / 1e3 / HBM_PEAK_GBS, 4),
+        "kernel": "kvq_append: append_kernel, one call per sequence over its cached tokens",
+    }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline: oracle on full steps, about 10 s")
         dt, n_cpu, cores = cpu_baseline(wl, inp)

@@ -98,6 +98,10 @@ size_t kvq_block_bytes(int32_t page_size, int32_t head_dim);
  *                 >= num_pages * page_size is skipped (no write), so -1 can mark padding.
  *                 Two tokens with the same slot in one call race; the result is undefined.
  *   n_tok         >= 0 (0 enqueues nothing and returns KVQ_OK).
+ * Tokens are taken in groups of 16 (token indices 16i .. 16i+15).  A group whose slots are the
+ * 16 slots of one tile in order (a prefill or a chunk of one, starting at a tile boundary) is
+ * written as whole tiles, which is the fast case; any other group token by token.  The bytes
+ * are the same either way.
  * Returns KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED or KVQ_ERR_HIP.
  */
 int kvq_append(void* pool, int32_t num_pages, int32_t page_size, int32_t num_kv_heads,

@@ -37,22 +37,34 @@ __device__ inline int quantize_one(float x, float s, float qmax) {
   return (int)c;
 }
 
-// Quantize the K and V rows (fp32, D values each, krow/vrow point at the row's first value)
-// of the token in slot s of the (page, KV head) block at blk.  Called by all 64 lanes of a wave.
+// A wave's share of one token's K and V rows: lane l holds dims E*l .. E*l + E-1.
 template <int D>
-__device__ inline void append_row(uint8_t* blk, int P, int s, const float* krow_base,
-                                  const float* vrow_base, int lane) {
-  constexpr int E = D / kWave;  // dims per lane: 1, 2 or 4
+struct RowVals {
+  static constexpr int E = D / kWave;  // dims per lane: 1, 2 or 4
+  float k[E], v[E];
+};
+
+template <int D>
+__device__ __attribute__((always_inline)) inline RowVals<D> load_row(const float* krow_base, const float* vrow_base, int lane) {
+  RowVals<D> r;
+  const int d0 = lane * RowVals<D>::E;
+#pragma unroll
+  for (int e = 0; e < RowVals<D>::E; ++e) {
+    r.k[e] = krow_base[d0 + e];
+    r.v[e] = vrow_base[d0 + e];
+  }
+  return r;
+}
+
+// Quantize one token's K and V rows (already in the wave's registers) into slot s of the
+// (page, KV head) block at blk.  Called by all 64 lanes of a wave.
+template <int D>
+__device__ __attribute__((always_inline)) inline void store_row(uint8_t* blk, int P, int s, const RowVals<D>& r, int lane) {
+  constexpr int E = RowVals<D>::E;
   const int tile = s / kTile, t = s % kTile;
   const int d0 = lane * E;
-  const float* krow = krow_base + d0;
-  const float* vrow = vrow_base + d0;
-  float kx[E], vx[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    kx[e] = krow[e];
-    vx[e] = vrow[e];
-  }
+  const float* kx = r.k;
+  const float* vx = r.v;
 
   // ---- K: one scale per token and head (qmax 127) ----
   float ka = 0.0f;
@@ -103,6 +115,13 @@ __device__ inline void append_row(uint8_t* blk, int P, int s, const float* krow_
       vbase[4 * w * vlane] = byte;
     }
   }
+}
+
+// Load and quantize one token's rows (krow/vrow point at the rows' first values) into slot s.
+template <int D>
+__device__ inline void append_row(uint8_t* blk, int P, int s, const float* krow_base,
+                                  const float* vrow_base, int lane) {
+  store_row<D>(blk, P, s, load_row<D>(krow_base, vrow_base, lane), lane);
 }
 
 }  // namespace kvq

@@ -57,6 +57,40 @@ def test_append_edge_rows_bit_exact():
         assert np.array_equal(got, inp_pool), (P, D, Hkv, np.flatnonzero(got != inp_pool)[:8])
 
 
+def test_append_tile_and_row_paths_bit_exact():
+    """Groups of 16 tokens that fill one tile in order are written as whole tiles; any other
+    group token by token.  One call mixes both: whole tiles, a run starting mid-tile, a tile with
+    two slots swapped, a tile with a padding slot, and a short last group."""
+    H.say("[append tile / row paths]")
+    rng = np.random.default_rng(78)
+    for P, D, Hkv in ((64, 256, 2), (16, 64, 1), (32, 128, 3)):
+        # segments in disjoint 64-slot regions (no slot written twice, whatever the page size);
+        # each is one 16-token group of the kernel (groups start at multiples of 16 tokens)
+        pages = 12 * 64 // P
+        slots = [np.arange(64, 64 + 48)]                        # 3 whole tiles
+        slots.append(np.arange(192 + 8, 192 + 24))              # mid-tile start
+        sw = np.arange(320, 336)
+        sw[[3, 7]] = sw[[7, 3]]
+        slots.append(sw)                                        # out of order
+        pad = np.arange(384 + 16, 384 + 32)
+        pad[5] = -1
+        slots.append(pad)                                       # padding inside a tile
+        slots.append(np.arange(512, 528))                       # whole tile
+        slots.append(np.arange(576, 581))                       # short last group
+        slots = np.concatenate(slots).astype(np.int32)
+        n = slots.size
+        k = rng.standard_normal((n, Hkv, D)).astype(np.float32)
+        v = rng.standard_normal((n, Hkv, D)).astype(np.float32)
+        k[2] = 0.0
+        v[50] *= np.float32(1e-6)
+        ref = H.oracle.new_pool(pages, P, Hkv, D)
+        H.oracle.append(ref, pages, P, Hkv, D, k, v, slots)
+        cache = H.kvq().PagedCache.allocate(pages, P, Hkv, D)
+        H.gpu_append(cache, k, v, slots)
+        got = cache.pool.cpu().numpy()
+        assert np.array_equal(got, ref), (P, D, Hkv, np.flatnonzero(got != ref)[:8])
+
+
 # ------------------------------------------------------------------ decode, small --------
 
 SMALL = [
