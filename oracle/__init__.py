@@ -1,4 +1,4 @@
-"""CPU oracle for the paged K8/V4 cache and its decode attention.
+"""CPU oracle for the paged K8/V4 (and K8/V8) cache and its decode attention.
 
 TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the benchmark's
 ``cpu_baseline`` leg are the only callers.  The product path never imports this package.
@@ -43,20 +43,20 @@ def _declare(lib):
     lib.kvq_oracle_fp16_from_double.restype = ctypes.c_uint16
     lib.kvq_oracle_quantize_group.argtypes = [P, I, I, P, P]
     lib.kvq_oracle_quantize_group.restype = None
-    lib.kvq_oracle_block_bytes.argtypes = [I, I]
-    lib.kvq_oracle_block_bytes.restype = ctypes.c_size_t
-    lib.kvq_oracle_format_offset.argtypes = [I, I, I, I, I, ctypes.POINTER(ctypes.c_int)]
-    lib.kvq_oracle_format_offset.restype = ctypes.c_longlong
-    lib.kvq_oracle_append.argtypes = [P, I, I, I, I, P, P, P, I]
-    lib.kvq_oracle_append.restype = None
-    lib.kvq_oracle_read_slot.argtypes = [P, I, I, I, I, I, I, P, P, P, P]
-    lib.kvq_oracle_read_slot.restype = None
-    lib.kvq_oracle_decode_attn.argtypes = [P, I, I, I, I, P, P, P, I, I, I, I,
-                                           ctypes.c_double, P, I, P, P]
-    lib.kvq_oracle_decode_attn.restype = None
-    lib.kvq_oracle_attn_weights.argtypes = [P, I, I, I, I, P, P, P, I, I, I,
-                                            ctypes.c_double, I, I, I, P]
-    lib.kvq_oracle_attn_weights.restype = I
+    lib.kvq_oracle_block_bytes_fmt.argtypes = [I, I, I]
+    lib.kvq_oracle_block_bytes_fmt.restype = ctypes.c_size_t
+    lib.kvq_oracle_format_offset_fmt.argtypes = [I, I, I, I, I, I, ctypes.POINTER(ctypes.c_int)]
+    lib.kvq_oracle_format_offset_fmt.restype = ctypes.c_longlong
+    lib.kvq_oracle_append_fmt.argtypes = [P, I, I, I, I, I, P, P, P, I]
+    lib.kvq_oracle_append_fmt.restype = None
+    lib.kvq_oracle_read_slot_fmt.argtypes = [P, I, I, I, I, I, I, I, P, P, P, P]
+    lib.kvq_oracle_read_slot_fmt.restype = None
+    lib.kvq_oracle_decode_attn_fmt.argtypes = [P, I, I, I, I, I, P, P, P, I, I, I, I,
+                                               ctypes.c_double, P, I, P, P]
+    lib.kvq_oracle_decode_attn_fmt.restype = None
+    lib.kvq_oracle_attn_weights_fmt.argtypes = [P, I, I, I, I, I, P, P, P, I, I, I,
+                                                ctypes.c_double, I, I, I, P]
+    lib.kvq_oracle_attn_weights_fmt.restype = I
     lib.kvq_oracle_num_threads.argtypes = []
     lib.kvq_oracle_num_threads.restype = I
     return lib
@@ -94,51 +94,55 @@ class Oracle:
         self.lib.kvq_oracle_quantize_group(_ptr(x), x.size, int(qmax), _ptr(codes), _ptr(sb))
         return codes, int(sb[0])
 
-    def block_bytes(self, page_size: int, head_dim: int) -> int:
-        return int(self.lib.kvq_oracle_block_bytes(page_size, head_dim))
+    # vbits: bits per V code, 4 (K8/V4, the default) or 8 (K8/V8)
+    def block_bytes(self, page_size: int, head_dim: int, vbits: int = 4) -> int:
+        return int(self.lib.kvq_oracle_block_bytes_fmt(page_size, head_dim, vbits))
 
     def pool_bytes(self, num_pages: int, page_size: int, num_kv_heads: int,
-                   head_dim: int) -> int:
-        return num_pages * num_kv_heads * self.block_bytes(page_size, head_dim)
+                   head_dim: int, vbits: int = 4) -> int:
+        return num_pages * num_kv_heads * self.block_bytes(page_size, head_dim, vbits)
 
-    def format_offset(self, what: int, page_size: int, head_dim: int, slot: int, index: int):
+    def format_offset(self, what: int, page_size: int, head_dim: int, slot: int, index: int,
+                      vbits: int = 4):
         """(byte offset within a block, aux) for what = 0 K code, 1 K scale, 2 V code
-        (aux = 1 for the high nibble), 3 V scale (index = scale group)."""
+        (aux = 1 for the high nibble of a 4-bit code), 3 V scale (index = scale group)."""
         aux = ctypes.c_int(0)
-        off = self.lib.kvq_oracle_format_offset(what, page_size, head_dim, slot, index,
-                                                ctypes.byref(aux))
+        off = self.lib.kvq_oracle_format_offset_fmt(what, page_size, head_dim, vbits, slot, index,
+                                                    ctypes.byref(aux))
         return int(off), int(aux.value)
 
     def append(self, pool: np.ndarray, num_pages: int, page_size: int, num_kv_heads: int,
-               head_dim: int, k, v, slot_mapping) -> None:
+               head_dim: int, k, v, slot_mapping, vbits: int = 4) -> None:
         """Quantize tokens k, v (fp32 [n_tok][Hkv][D]) into ``pool`` (uint8, in place)."""
         assert pool.dtype == np.uint8 and pool.flags.c_contiguous
-        assert pool.size >= self.pool_bytes(num_pages, page_size, num_kv_heads, head_dim)
+        assert pool.size >= self.pool_bytes(num_pages, page_size, num_kv_heads, head_dim, vbits)
         k = _c(k, np.float32)
         v = _c(v, np.float32)
         slots = _c(slot_mapping, np.int32)
         n_tok = slots.size
         assert k.size == n_tok * num_kv_heads * head_dim and v.size == k.size
-        self.lib.kvq_oracle_append(_ptr(pool), num_pages, page_size, num_kv_heads, head_dim,
-                                   _ptr(k), _ptr(v), _ptr(slots), n_tok)
+        self.lib.kvq_oracle_append_fmt(_ptr(pool), num_pages, page_size, num_kv_heads, head_dim,
+                                       vbits, _ptr(k), _ptr(v), _ptr(slots), n_tok)
 
-    def new_pool(self, num_pages: int, page_size: int, num_kv_heads: int, head_dim: int):
-        return np.zeros(self.pool_bytes(num_pages, page_size, num_kv_heads, head_dim), np.uint8)
+    def new_pool(self, num_pages: int, page_size: int, num_kv_heads: int, head_dim: int,
+                 vbits: int = 4):
+        return np.zeros(self.pool_bytes(num_pages, page_size, num_kv_heads, head_dim, vbits),
+                        np.uint8)
 
     def read_slot(self, pool: np.ndarray, page_size: int, num_kv_heads: int, head_dim: int,
-                  page: int, slot: int, head: int):
+                  page: int, slot: int, head: int, vbits: int = 4):
         """Codes and scale bits stored for one (page, slot, KV head)."""
         kc = np.zeros(head_dim, np.int8)
         vc = np.zeros(head_dim, np.int8)
         ks = np.zeros(1, np.uint16)
         vs = np.zeros(head_dim // 32, np.uint16)
-        self.lib.kvq_oracle_read_slot(_ptr(pool), page_size, num_kv_heads, head_dim, page, slot,
-                                      head, _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs))
+        self.lib.kvq_oracle_read_slot_fmt(_ptr(pool), page_size, num_kv_heads, head_dim, vbits,
+                                          page, slot, head, _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs))
         return kc, int(ks[0]), vc, vs
 
     def decode_attn(self, pool: np.ndarray, num_pages: int, page_size: int, num_kv_heads: int,
                     head_dim: int, q_bits, page_table, seq_lens, n_rows: int, n_q_heads: int,
-                    softmax_scale: float = 0.0, select=None):
+                    softmax_scale: float = 0.0, select=None, vbits: int = 4):
         """fp64 attention. ``q_bits``: uint16 fp16 bits [n_seq][n_rows][Hq][D].
 
         Returns (out, lse): with ``select`` None, out is [n_seq][n_rows][Hq][D] and lse
@@ -159,8 +163,8 @@ class Oracle:
             count = sel.shape[0]
         out = np.zeros((count, head_dim), np.float64)
         lse = np.zeros(count, np.float64)
-        self.lib.kvq_oracle_decode_attn(_ptr(pool), num_pages, page_size, num_kv_heads,
-                                        head_dim, _ptr(q), _ptr(pt), _ptr(sl), n_seq, n_rows,
+        self.lib.kvq_oracle_decode_attn_fmt(_ptr(pool), num_pages, page_size, num_kv_heads,
+                                            head_dim, vbits, _ptr(q), _ptr(pt), _ptr(sl), n_seq, n_rows,
                                         n_q_heads, max_pages, float(softmax_scale),
                                         None if sel is None else _ptr(sel), count, _ptr(out),
                                         _ptr(lse))
@@ -172,15 +176,15 @@ class Oracle:
     def attn_weights(self, pool: np.ndarray, num_pages: int, page_size: int,
                      num_kv_heads: int, head_dim: int, q_bits, page_table, seq_lens,
                      n_rows: int, n_q_heads: int, b: int, i: int, hq: int,
-                     softmax_scale: float = 0.0):
+                     softmax_scale: float = 0.0, vbits: int = 4):
         """Softmax weights over the L tokens of sequence b for query row i, head hq."""
         q = _c(q_bits, np.uint16)
         pt = _c(page_table, np.int32)
         sl = _c(seq_lens, np.int32)
         max_pages = pt.size // sl.size
         w = np.zeros(max(int(sl[b]), 1), np.float64)
-        n = self.lib.kvq_oracle_attn_weights(_ptr(pool), num_pages, page_size, num_kv_heads,
-                                             head_dim, _ptr(q), _ptr(pt), _ptr(sl), n_rows,
+        n = self.lib.kvq_oracle_attn_weights_fmt(_ptr(pool), num_pages, page_size, num_kv_heads,
+                                                 head_dim, vbits, _ptr(q), _ptr(pt), _ptr(sl), n_rows,
                                              n_q_heads, max_pages, float(softmax_scale), b, i,
                                              hq, _ptr(w))
         return w, n

@@ -9,7 +9,8 @@
  * What it computes (the definition; the GPU's split-KV flash-decoding reaches the same value
  * up to fp32 rounding):
  *   - quantization of each new token's K row to int8 with one fp16 scale, and of its V row to
- *     int4 with one fp16 scale per 32 dims (the engine's "rk8v4"/K8-V4 KV dtype: forum post
+ *     int4 (vb = 4) or int8 (vb = 8) with one fp16 scale per 32 dims (the engine's "rk8v4"
+ *     K8-V4 KV dtype, and the int8 KV it is compared with: forum post
  *     "3090 单卡跑 Qwen3.8-27B：NInfer 上机实测（180K 上下文 / C2 并发 / 4bit KV）", section
  *     一、部署, launch-flag table; the pages leave the scale granularity open, the library
  *     header fixes it and this file follows that definition);
@@ -106,7 +107,11 @@ void kvq_oracle_quantize_group(const float* x, int n, int qmax, int8_t* codes,
 
 /* ---------------------------------------------------------------- page format ------------ */
 
-size_t kvq_oracle_block_bytes(int P, int D) { return (size_t)P * (size_t)(D + 2 + D / 2 + D / 16); }
+/* vb = bits per V code: 4 (K8/V4, two codes per byte) or 8 (K8/V8, one per byte). */
+size_t kvq_oracle_block_bytes_fmt(int P, int D, int vb) {
+  return (size_t)P * (size_t)(D + 2 + D * vb / 8 + D / 16);
+}
+size_t kvq_oracle_block_bytes(int P, int D) { return kvq_oracle_block_bytes_fmt(P, D, 4); }
 
 static size_t k_code_offset(int D, int s, int d) {
   int tile = s / 16, t = s % 16;
@@ -123,37 +128,51 @@ static size_t v_code_offset(int P, int D, int s, int d, int* high_nibble) {
   return (size_t)P * D + (size_t)2 * P + (size_t)8 * D * tile + (size_t)256 * w * (j / w) +
          (size_t)4 * w * lane + (size_t)4 * (j % w) + (size_t)r;
 }
-static size_t v_scale_offset(int P, int D, int s, int j) {
-  return (size_t)P * D + (size_t)2 * P + (size_t)P * D / 2 + (size_t)2 * ((size_t)s * (D / 32) + j);
+/* K8/V8: the two nibbles of a V4 byte become two bytes, 4 apart (dim of the even 16-dim block
+ * first), in 8-byte units; up to two scale groups' units side by side per lane. */
+static size_t v8_code_offset(int P, int D, int s, int d) {
+  int tile = s / 16, t = s % 16, j = d / 32;
+  int v8lane = 16 * (t / 4) + d % 16; /* as for 4-bit codes: four tokens, one dim pair per lane */
+  int w = D / 32 < 2 ? D / 32 : 2;
+  return (size_t)P * D + (size_t)2 * P + (size_t)16 * D * tile + (size_t)512 * w * (j / w) +
+         (size_t)8 * w * v8lane + (size_t)8 * (j % w) + (size_t)4 * ((d / 16) % 2) + (size_t)(t % 4);
+}
+static size_t v_scale_offset_fmt(int P, int D, int vb, int s, int j) {
+  return (size_t)P * D + (size_t)2 * P + (size_t)P * D * vb / 8 + (size_t)2 * ((size_t)s * (D / 32) + j);
 }
 
 /* Byte offset of a quantity within its block, exposed so tests can check the format's
- * bijectivity: what = 0 K code, 1 K scale, 2 V code (returns nibble in *aux), 3 V scale. */
-long long kvq_oracle_format_offset(int what, int P, int D, int s, int d, int* aux) {
+ * bijectivity: what = 0 K code, 1 K scale, 2 V code (returns nibble in *aux; always 0 for
+ * vb = 8), 3 V scale. */
+long long kvq_oracle_format_offset_fmt(int what, int P, int D, int vb, int s, int d, int* aux) {
   *aux = 0;
   switch (what) {
     case 0: return (long long)k_code_offset(D, s, d);
     case 1: return (long long)k_scale_offset(P, D, s);
-    case 2: return (long long)v_code_offset(P, D, s, d, aux);
-    case 3: return (long long)v_scale_offset(P, D, s, d);
+    case 2: return vb == 8 ? (long long)v8_code_offset(P, D, s, d) : (long long)v_code_offset(P, D, s, d, aux);
+    case 3: return (long long)v_scale_offset_fmt(P, D, vb, s, d);
   }
   return -1;
 }
+long long kvq_oracle_format_offset(int what, int P, int D, int s, int d, int* aux) {
+  return kvq_oracle_format_offset_fmt(what, P, D, 4, s, d, aux);
+}
 
-static uint8_t* block_of(uint8_t* pool, int Hkv, int P, int D, int page, int h) {
-  return pool + ((size_t)page * Hkv + h) * kvq_oracle_block_bytes(P, D);
+static uint8_t* block_of(uint8_t* pool, int Hkv, int P, int D, int vb, int page, int h) {
+  return pool + ((size_t)page * Hkv + h) * kvq_oracle_block_bytes_fmt(P, D, vb);
 }
 
 /* Quantize n_tok tokens and write them into their slots (slot < 0 or beyond the pool: skip). */
-void kvq_oracle_append(uint8_t* pool, int num_pages, int P, int Hkv, int D, const float* k,
-                       const float* v, const int32_t* slots, int n_tok) {
+void kvq_oracle_append_fmt(uint8_t* pool, int num_pages, int P, int Hkv, int D, int vb,
+                           const float* k, const float* v, const int32_t* slots, int n_tok) {
+  const int vqmax = vb == 8 ? 127 : 7;
   int8_t* codes = (int8_t*)malloc((size_t)D);
   for (int n = 0; n < n_tok; ++n) {
     long long slot = slots[n];
     if (slot < 0 || slot >= (long long)num_pages * P) continue;
     int page = (int)(slot / P), s = (int)(slot % P);
     for (int h = 0; h < Hkv; ++h) {
-      uint8_t* blk = block_of(pool, Hkv, P, D, page, h);
+      uint8_t* blk = block_of(pool, Hkv, P, D, vb, page, h);
       const float* krow = k + ((size_t)n * Hkv + h) * D;
       const float* vrow = v + ((size_t)n * Hkv + h) * D;
       uint16_t sb;
@@ -163,12 +182,16 @@ void kvq_oracle_append(uint8_t* pool, int num_pages, int P, int Hkv, int D, cons
       blk[so] = (uint8_t)(sb & 0xFF);
       blk[so + 1] = (uint8_t)(sb >> 8);
       for (int j = 0; j < D / 32; ++j) {
-        kvq_oracle_quantize_group(vrow + 32 * j, 32, 7, codes + 32 * j, &sb);
-        size_t vo = v_scale_offset(P, D, s, j);
+        kvq_oracle_quantize_group(vrow + 32 * j, 32, vqmax, codes + 32 * j, &sb);
+        size_t vo = v_scale_offset_fmt(P, D, vb, s, j);
         blk[vo] = (uint8_t)(sb & 0xFF);
         blk[vo + 1] = (uint8_t)(sb >> 8);
       }
       for (int d = 0; d < D; ++d) {
+        if (vb == 8) {
+          blk[v8_code_offset(P, D, s, d)] = (uint8_t)codes[d];
+          continue;
+        }
         int hi;
         size_t o = v_code_offset(P, D, s, d, &hi);
         uint8_t nib = (uint8_t)(codes[d] & 0x0F);
@@ -178,38 +201,50 @@ void kvq_oracle_append(uint8_t* pool, int num_pages, int P, int Hkv, int D, cons
   }
   free(codes);
 }
+void kvq_oracle_append(uint8_t* pool, int num_pages, int P, int Hkv, int D, const float* k,
+                       const float* v, const int32_t* slots, int n_tok) {
+  kvq_oracle_append_fmt(pool, num_pages, P, Hkv, D, 4, k, v, slots, n_tok);
+}
 
 /* Read back one slot of one head: codes and fp16 scale bits (kc[D], ks[1], vc[D], vs[D/32]). */
-void kvq_oracle_read_slot(const uint8_t* pool, int P, int Hkv, int D, int page, int s, int h,
-                          int8_t* kc, uint16_t* ks, int8_t* vc, uint16_t* vs) {
-  const uint8_t* blk = pool + ((size_t)page * Hkv + h) * kvq_oracle_block_bytes(P, D);
+void kvq_oracle_read_slot_fmt(const uint8_t* pool, int P, int Hkv, int D, int vb, int page, int s,
+                              int h, int8_t* kc, uint16_t* ks, int8_t* vc, uint16_t* vs) {
+  const uint8_t* blk = pool + ((size_t)page * Hkv + h) * kvq_oracle_block_bytes_fmt(P, D, vb);
   for (int d = 0; d < D; ++d) kc[d] = (int8_t)blk[k_code_offset(D, s, d)];
   size_t so = k_scale_offset(P, D, s);
   *ks = (uint16_t)(blk[so] | (blk[so + 1] << 8));
   for (int d = 0; d < D; ++d) {
+    if (vb == 8) {
+      vc[d] = (int8_t)blk[v8_code_offset(P, D, s, d)];
+      continue;
+    }
     int hi;
     size_t o = v_code_offset(P, D, s, d, &hi);
     int nib = hi ? (blk[o] >> 4) & 0xF : blk[o] & 0xF;
     vc[d] = (int8_t)(nib >= 8 ? nib - 16 : nib); /* 4-bit two's complement */
   }
   for (int j = 0; j < D / 32; ++j) {
-    size_t vo = v_scale_offset(P, D, s, j);
+    size_t vo = v_scale_offset_fmt(P, D, vb, s, j);
     vs[j] = (uint16_t)(blk[vo] | (blk[vo + 1] << 8));
   }
+}
+void kvq_oracle_read_slot(const uint8_t* pool, int P, int Hkv, int D, int page, int s, int h,
+                          int8_t* kc, uint16_t* ks, int8_t* vc, uint16_t* vs) {
+  kvq_oracle_read_slot_fmt(pool, P, Hkv, D, 4, page, s, h, kc, ks, vc, vs);
 }
 
 /* ---------------------------------------------------------------- attention -------------- */
 
 /* Dequantized K and V of logical token t of sequence b, head h (page-table entries clamped
  * into [0, num_pages) as the library header specifies). */
-static void token_kv(const uint8_t* pool, int num_pages, int P, int Hkv, int D,
+static void token_kv(const uint8_t* pool, int num_pages, int P, int Hkv, int D, int vb,
                      const int32_t* pt_row, int t, int h, double* kd, double* vd, int8_t* kc,
                      int8_t* vc, uint16_t* vs) {
   int page = pt_row[t / P];
   if (page < 0) page = 0;
   if (page >= num_pages) page = num_pages - 1;
   uint16_t ks;
-  kvq_oracle_read_slot(pool, P, Hkv, D, page, t % P, h, kc, &ks, vc, vs);
+  kvq_oracle_read_slot_fmt(pool, P, Hkv, D, vb, page, t % P, h, kc, &ks, vc, vs);
   double sk = kvq_oracle_fp16_to_double(ks);
   for (int d = 0; d < D; ++d) kd[d] = (double)kc[d] * sk;
   for (int d = 0; d < D; ++d) vd[d] = (double)vc[d] * kvq_oracle_fp16_to_double(vs[d / 32]);
@@ -218,7 +253,7 @@ static void token_kv(const uint8_t* pool, int num_pages, int P, int Hkv, int D,
 /* Softmax weights of one output row (sequence b, query row i, query head hq): w[t] for
  * t < L (0 where masked).  Returns the number of attended tokens; *m_out and *sum_out get the
  * max logit and sum of exp(z - max) for the log-sum-exp. */
-static int row_weights(const uint8_t* pool, int num_pages, int P, int Hkv, int D,
+static int row_weights(const uint8_t* pool, int num_pages, int P, int Hkv, int D, int vb,
                        const uint16_t* q, const int32_t* page_table, const int32_t* seq_lens,
                        int R, int Hq, int max_pages, double scale, int b, int i, int hq,
                        double* w, double* m_out, double* sum_out) {
@@ -243,7 +278,7 @@ static int row_weights(const uint8_t* pool, int num_pages, int P, int Hkv, int D
   const int32_t* pt_row = page_table + (size_t)b * max_pages;
   double m = -INFINITY;
   for (int t = 0; t < n; ++t) {
-    token_kv(pool, num_pages, P, Hkv, D, pt_row, t, h, kd, vd, kc, vc, vs);
+    token_kv(pool, num_pages, P, Hkv, D, vb, pt_row, t, h, kd, vd, kc, vc, vs);
     double dot = 0.0;
     for (int d = 0; d < D; ++d) dot += qd[d] * kd[d];
     w[t] = scale * dot; /* logit z_t, replaced by its weight below */
@@ -263,11 +298,11 @@ static int row_weights(const uint8_t* pool, int num_pages, int P, int Hkv, int D
 
 /* Attention outputs for a list of (b, i, hq) triples (sel, n_sel of them), or for every
  * output in [b][i][hq] order when sel is NULL.  out: [count][D] fp64, lse: [count] fp64. */
-void kvq_oracle_decode_attn(const uint8_t* pool, int num_pages, int P, int Hkv, int D,
-                            const uint16_t* q, const int32_t* page_table,
-                            const int32_t* seq_lens, int n_seq, int R, int Hq, int max_pages,
-                            double scale, const int32_t* sel, int n_sel, double* out,
-                            double* lse) {
+void kvq_oracle_decode_attn_fmt(const uint8_t* pool, int num_pages, int P, int Hkv, int D, int vb,
+                                const uint16_t* q, const int32_t* page_table,
+                                const int32_t* seq_lens, int n_seq, int R, int Hq, int max_pages,
+                                double scale, const int32_t* sel, int n_sel, double* out,
+                                double* lse) {
   if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
   int count = sel ? n_sel : n_seq * R * Hq;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -285,7 +320,7 @@ void kvq_oracle_decode_attn(const uint8_t* pool, int num_pages, int P, int Hkv, 
     int L = seq_lens[b];
     double* w = (double*)malloc(sizeof(double) * (L > 0 ? (size_t)L : 1));
     double m, sum;
-    int n = row_weights(pool, num_pages, P, Hkv, D, q, page_table, seq_lens, R, Hq, max_pages,
+    int n = row_weights(pool, num_pages, P, Hkv, D, vb, q, page_table, seq_lens, R, Hq, max_pages,
                         scale, b, i, hq, w, &m, &sum);
     double* o_row = out + (size_t)o * D;
     for (int d = 0; d < D; ++d) o_row[d] = 0.0;
@@ -298,7 +333,7 @@ void kvq_oracle_decode_attn(const uint8_t* pool, int num_pages, int P, int Hkv, 
       const int32_t* pt_row = page_table + (size_t)b * max_pages;
       int h = hq / (Hq / Hkv);
       for (int t = 0; t < n; ++t) {
-        token_kv(pool, num_pages, P, Hkv, D, pt_row, t, h, kd, vd, kc, vc, vs);
+        token_kv(pool, num_pages, P, Hkv, D, vb, pt_row, t, h, kd, vd, kc, vc, vs);
         for (int d = 0; d < D; ++d) o_row[d] += w[t] * vd[d];
       }
       free(kd); free(vd); free(kc); free(vc); free(vs);
@@ -310,17 +345,33 @@ void kvq_oracle_decode_attn(const uint8_t* pool, int num_pages, int P, int Hkv, 
   }
 }
 
-/* Softmax weights of one output row, w[0..L-1] (0 where masked). Returns attended count. */
-int kvq_oracle_attn_weights(const uint8_t* pool, int num_pages, int P, int Hkv, int D,
+void kvq_oracle_decode_attn(const uint8_t* pool, int num_pages, int P, int Hkv, int D,
                             const uint16_t* q, const int32_t* page_table,
-                            const int32_t* seq_lens, int R, int Hq, int max_pages, double scale,
-                            int b, int i, int hq, double* w) {
+                            const int32_t* seq_lens, int n_seq, int R, int Hq, int max_pages,
+                            double scale, const int32_t* sel, int n_sel, double* out,
+                            double* lse) {
+  kvq_oracle_decode_attn_fmt(pool, num_pages, P, Hkv, D, 4, q, page_table, seq_lens, n_seq, R, Hq,
+                             max_pages, scale, sel, n_sel, out, lse);
+}
+
+/* Softmax weights of one output row, w[0..L-1] (0 where masked). Returns attended count. */
+int kvq_oracle_attn_weights_fmt(const uint8_t* pool, int num_pages, int P, int Hkv, int D, int vb,
+                                const uint16_t* q, const int32_t* page_table,
+                                const int32_t* seq_lens, int R, int Hq, int max_pages, double scale,
+                                int b, int i, int hq, double* w) {
   if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
   int L = seq_lens[b];
   for (int t = 0; t < L; ++t) w[t] = 0.0;
   double m, sum;
-  return row_weights(pool, num_pages, P, Hkv, D, q, page_table, seq_lens, R, Hq, max_pages,
+  return row_weights(pool, num_pages, P, Hkv, D, vb, q, page_table, seq_lens, R, Hq, max_pages,
                      scale, b, i, hq, w, &m, &sum);
+}
+int kvq_oracle_attn_weights(const uint8_t* pool, int num_pages, int P, int Hkv, int D,
+                            const uint16_t* q, const int32_t* page_table,
+                            const int32_t* seq_lens, int R, int Hq, int max_pages, double scale,
+                            int b, int i, int hq, double* w) {
+  return kvq_oracle_attn_weights_fmt(pool, num_pages, P, Hkv, D, 4, q, page_table, seq_lens, R, Hq,
+                                     max_pages, scale, b, i, hq, w);
 }
 
 int kvq_oracle_num_threads(void) {

@@ -47,14 +47,15 @@ def argmin_code(x: float, s: float, qmax: int) -> int:
     return best
 
 
-def quantize_token_np(krow, vrow):
-    """K row -> (codes, scale bits); V row -> (codes, [scale bits per 32 dims])."""
+def quantize_token_np(krow, vrow, vqmax=7):
+    """K row -> (codes, scale bits); V row -> (codes, [scale bits per 32 dims]).  vqmax 7: 4-bit
+    V codes (K8/V4), 127: 8-bit (K8/V8)."""
     kc, ks = quantize_group_np(krow, 127)
     D = len(vrow)
     vc = np.zeros(D, np.int8)
     vs = []
     for j in range(D // 32):
-        c, sb = quantize_group_np(vrow[32 * j:32 * j + 32], 7)
+        c, sb = quantize_group_np(vrow[32 * j:32 * j + 32], vqmax)
         vc[32 * j:32 * j + 32] = c
         vs.append(sb)
     return kc, ks, vc, vs

@@ -34,7 +34,7 @@ def _case(i):
 
 
 @functools.lru_cache(maxsize=None)
-def _brute_ref(i):
+def _brute_ref(i, vqmax=7):
     inp = _case(i)
     wl = inp.wl
     n, L, H, D = wl.n_seq, wl.seq_len, wl.num_kv_heads, wl.head_dim
@@ -46,7 +46,7 @@ def _brute_ref(i):
         for t in range(int(inp.seq_lens[b])):
             for h in range(H):
                 kc[b, t, h], ks[b, t, h], vc[b, t, h], vs[b, t, h] = brute.quantize_token_np(
-                    inp.k[b, t, h], inp.v[b, t, h])
+                    inp.k[b, t, h], inp.v[b, t, h], vqmax)
     return brute.attention_brute(inp.q_bits, kc, ks, vc, vs, inp.seq_lens, wl.n_rows,
                                  wl.n_q_heads, H, 1.0 / math.sqrt(D))
 
@@ -106,39 +106,57 @@ def check_quantizer_argmin(o):
     return True
 
 
-def check_format_golden(o):
-    for line in _golden_lines("format_offsets.txt"):
+def _check_format_file(o, name, vbits):
+    for line in _golden_lines(name):
         lhs, rhs = line.split("->")
         what, P, D, s, idx = (int(x) for x in lhs.split())
-        if o.format_offset(what, P, D, s, idx) != tuple(int(x) for x in rhs.split()):
+        if o.format_offset(what, P, D, s, idx, vbits=vbits) != tuple(int(x) for x in rhs.split()):
             return False
     return True
 
 
-def _fill(o, inp):
+def check_format_golden(o):
+    return _check_format_file(o, "format_offsets.txt", 4)
+
+
+def check_format_golden_v8(o):
+    return _check_format_file(o, "format_offsets_v8.txt", 8)
+
+
+def _fill(o, inp, vbits=4):
     wl = inp.wl
-    pool = o.new_pool(wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim)
+    pool = o.new_pool(wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim, vbits)
     k, v, slots = inp.all_tokens()
-    o.append(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim, k, v, slots)
+    o.append(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim, k, v, slots,
+             vbits=vbits)
     return pool
 
 
-def _attend(o, inp, pool, scale=0.0):
+def _attend(o, inp, pool, scale=0.0, vbits=4):
     wl = inp.wl
     return o.decode_attn(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
                          inp.q_bits, inp.page_table, inp.seq_lens, wl.n_rows, wl.n_q_heads,
-                         softmax_scale=scale)
+                         softmax_scale=scale, vbits=vbits)
 
 
-def check_brute_force(o):
-    for i in range(len(BRUTE_CASES)):
+def _brute_force(o, vbits, cases):
+    for i in cases:
         inp = _case(i)
-        out, lse = _attend(o, inp, _fill(o, inp))
-        out_b, lse_b = _brute_ref(i)
+        out, lse = _attend(o, inp, _fill(o, inp, vbits), vbits=vbits)
+        out_b, lse_b = _brute_ref(i, 127 if vbits == 8 else 7)
         if not (np.allclose(out, out_b, rtol=0, atol=1e-12) and
                 np.allclose(lse, lse_b, rtol=0, atol=1e-11)):
             return False
     return True
+
+
+def check_brute_force(o):
+    return _brute_force(o, 4, range(len(BRUTE_CASES)))
+
+
+def check_brute_force_v8(o):
+    """K8/V8: the same brute force with 8-bit V codes (qmax 127)."""
+    return _brute_force(o, 8, range(2))
 
 
 def check_closed_forms(o):
@@ -185,7 +203,8 @@ def check_large_logits(o):
 
 
 CHECKS = [check_fp16, check_quantizer_golden, check_quantizer_argmin, check_format_golden,
-          check_brute_force, check_closed_forms, check_large_logits]
+          check_brute_force, check_closed_forms, check_large_logits, check_format_golden_v8,
+          check_brute_force_v8]
 
 
 def run(o):

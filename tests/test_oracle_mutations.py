@@ -29,8 +29,8 @@ MUTATIONS = {
     "lse_drops_max": ("lse[o] = m + log(sum);", "lse[o] = log(sum);"),
     "default_scale": ("if (scale <= 0.0) scale = 1.0 / sqrt((double)D);\n  int count",
                       "if (scale <= 0.0) scale = 1.0 / (double)D;\n  int count"),
-    "wrong_slot": ("kvq_oracle_read_slot(pool, P, Hkv, D, page, t % P, h, kc, &ks, vc, vs);",
-                   "kvq_oracle_read_slot(pool, P, Hkv, D, page, (t + 1) % P, h, kc, &ks, vc, vs);"),
+    "wrong_slot": ("kvq_oracle_read_slot_fmt(pool, P, Hkv, D, vb, page, t % P, h, kc, &ks, vc, vs);",
+                   "kvq_oracle_read_slot_fmt(pool, P, Hkv, D, vb, page, (t + 1) % P, h, kc, &ks, vc, vs);"),
     "k_tokens_swapped": ("(size_t)16 * t + (size_t)(d % 16)", "(size_t)16 * (t ^ 1) + (size_t)(d % 16)"),
     "v_lane_transposed": ("int lane = 16 * (t / 4) + d % 16;\n  int r = t % 4;",
                           "int lane = 16 * (t % 4) + d % 16;\n  int r = t / 4;"),
@@ -38,6 +38,12 @@ MUTATIONS = {
                         "q + (((size_t)b * R + (R - 1)) * Hq + hq) * D"),
     "no_normalize": ("for (int t = 0; t < n; ++t) w[t] /= sum;", ""),
     "no_running_max": ("if (w[t] > m) m = w[t];", "m = 0.0;"),
+    # K8/V8 (8-bit V codes)
+    "v8_qmax": ("const int vqmax = vb == 8 ? 127 : 7;", "const int vqmax = vb == 8 ? 63 : 7;"),
+    "v8_dim_pair_bit": ("(size_t)4 * ((d / 16) % 2) + (size_t)(t % 4)",
+                        "(size_t)4 * ((d / 32) % 2) + (size_t)(t % 4)"),
+    "v8_scale_section": ("(size_t)P * D * vb / 8 + (size_t)2 * ((size_t)s * (D / 32) + j)",
+                         "(size_t)P * D / 2 + (size_t)2 * ((size_t)s * (D / 32) + j)"),
 }
 
 

@@ -133,27 +133,31 @@ def test_quantizer_invariants():
 
 # ------------------------------------------------------------------ page format ----------
 
+@pytest.mark.parametrize("vbits", [4, 8])
 @pytest.mark.parametrize("P,D", [(16, 64), (64, 256), (32, 128), (16, 256), (256, 64)])
-def test_format_is_a_bijection(P, D):
-    """Each code, nibble and scale has its own place; the four sections tile the block."""
+def test_format_is_a_bijection(P, D, vbits):
+    """Each code, nibble and scale has its own place; the four sections tile the block (4-bit V
+    codes two to a byte, 8-bit ones a byte each)."""
     o = oracle.default()
-    bb = o.block_bytes(P, D)
-    assert bb == P * (D + 2 + D // 2 + D // 16)
-    k = {o.format_offset(0, P, D, s, d)[0] for s in range(P) for d in range(D)}
+    bb = o.block_bytes(P, D, vbits)
+    vbytes = P * D * vbits // 8
+    assert bb == P * (D + 2 + D // 16) + vbytes
+    k = {o.format_offset(0, P, D, s, d, vbits)[0] for s in range(P) for d in range(D)}
     assert k == set(range(0, P * D))
-    ks = {o.format_offset(1, P, D, s, 0)[0] for s in range(P)}
+    ks = {o.format_offset(1, P, D, s, 0, vbits)[0] for s in range(P)}
     assert ks == set(range(P * D, P * D + 2 * P, 2))
-    v = {o.format_offset(2, P, D, s, d) for s in range(P) for d in range(D)}
+    v = {o.format_offset(2, P, D, s, d, vbits) for s in range(P) for d in range(D)}
     v0 = P * D + 2 * P
-    assert v == {(b, nib) for b in range(v0, v0 + P * D // 2) for nib in (0, 1)}
-    vs = {o.format_offset(3, P, D, s, j)[0] for s in range(P) for j in range(D // 32)}
-    vs0 = v0 + P * D // 2
+    nibs = (0, 1) if vbits == 4 else (0,)
+    assert v == {(b, nib) for b in range(v0, v0 + vbytes) for nib in nibs}
+    vs = {o.format_offset(3, P, D, s, j, vbits)[0] for s in range(P) for j in range(D // 32)}
+    vs0 = v0 + vbytes
     assert vs == set(range(vs0, vs0 + 2 * P * D // 32, 2)) and vs0 + 2 * P * D // 32 == bb
     # every byte of one token's codes belongs to that token alone
     owner = {}
     for s in range(P):
         for d in range(D):
-            b, _ = o.format_offset(2, P, D, s, d)
+            b, _ = o.format_offset(2, P, D, s, d, vbits)
             assert owner.setdefault(b, s) == s
 
 
@@ -173,31 +177,33 @@ def test_format_golden_offsets():
     assert n >= 15
 
 
-def test_append_round_trip_and_touches_only_its_slot():
+@pytest.mark.parametrize("vbits", [4, 8])
+def test_append_round_trip_and_touches_only_its_slot(vbits):
     """read_slot returns numpy-quantized codes; bytes of other slots are left as they were."""
     o = oracle.default()
     rng = np.random.default_rng(3)
     for P, D, Hkv in ((16, 64, 1), (64, 256, 2), (32, 128, 3)):
         pages = 5
-        pool = rng.integers(0, 256, o.pool_bytes(pages, P, Hkv, D), dtype=np.uint8)
+        pool = rng.integers(0, 256, o.pool_bytes(pages, P, Hkv, D, vbits), dtype=np.uint8)
         before = pool.copy()
         slots = np.array([0, P - 1, 2 * P + 5, 4 * P + 17 % P], np.int32)
         k = rng.standard_normal((len(slots), Hkv, D)).astype(np.float32)
         v = rng.standard_normal((len(slots), Hkv, D)).astype(np.float32)
-        o.append(pool, pages, P, Hkv, D, k, v, slots)
+        o.append(pool, pages, P, Hkv, D, k, v, slots, vbits=vbits)
         touched = np.zeros(pool.size, bool)
-        bb = o.block_bytes(P, D)
+        bb = o.block_bytes(P, D, vbits)
         for n, slot in enumerate(slots):
             page, s = divmod(int(slot), P)
             for h in range(Hkv):
-                kc, ks, vc, vs = o.read_slot(pool, P, Hkv, D, page, s, h)
-                kc_r, ks_r, vc_r, vs_r = brute.quantize_token_np(k[n, h], v[n, h])
+                kc, ks, vc, vs = o.read_slot(pool, P, Hkv, D, page, s, h, vbits)
+                kc_r, ks_r, vc_r, vs_r = brute.quantize_token_np(k[n, h], v[n, h],
+                                                                 127 if vbits == 8 else 7)
                 assert np.array_equal(kc, kc_r) and ks == ks_r
                 assert np.array_equal(vc, vc_r) and list(vs) == list(vs_r)
                 base = (page * Hkv + h) * bb
                 for what, count in ((0, D), (1, 1), (2, D), (3, D // 32)):
                     for idx in range(count):
-                        off, _ = o.format_offset(what, P, D, s, idx)
+                        off, _ = o.format_offset(what, P, D, s, idx, vbits)
                         touched[base + off] = True
                         if what in (1, 3):
                             touched[base + off + 1] = True
