@@ -47,25 +47,25 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def token_bytes(head_dim: int) -> int:
+def token_bytes(head_dim: int, vbits: int = 4) -> int:
     """Stored bytes per token per KV head: K codes + K scale + V codes + V scales."""
-    return head_dim + 2 + head_dim // 2 + 2 * (head_dim // 32)
+    return head_dim + 2 + head_dim * vbits // 8 + 2 * (head_dim // 32)
 
 
-def decode_algorithmic_bytes(wl, seq_lens) -> int:
+def decode_algorithmic_bytes(wl, seq_lens, vbits: int = 4) -> int:
     """Bytes the method itself must move per decode call: every cached K/V byte of every
     attended token once, the queries, the page-table entries used, the outputs (+ lse)."""
     D = wl.head_dim
-    kv = sum(int(L) for L in seq_lens) * wl.num_kv_heads * token_bytes(D)
+    kv = sum(int(L) for L in seq_lens) * wl.num_kv_heads * token_bytes(D, vbits)
     q = wl.n_seq * wl.n_rows * wl.n_q_heads * D * 2
     pt = sum(-(-int(L) // wl.page_size) for L in seq_lens) * 4
     out = wl.n_seq * wl.n_rows * wl.n_q_heads * (D + 1) * 4
     return kv + q + pt + out
 
 
-def append_algorithmic_bytes(wl) -> int:
+def append_algorithmic_bytes(wl, vbits: int = 4) -> int:
     n = wl.n_seq * wl.n_new
-    return n * wl.num_kv_heads * (2 * wl.head_dim * 4 + token_bytes(wl.head_dim)) + n * 4
+    return n * wl.num_kv_heads * (2 * wl.head_dim * 4 + token_bytes(wl.head_dim, vbits)) + n * 4
 
 
 def cpu_baseline(wl, inp, min_seconds=10.0):
@@ -150,6 +150,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=None, help="name in workloads.WORKLOADS")
+    ap.add_argument("--kv-format", default="k8v4", choices=["k8v4", "k8v8"],
+                    help="KV cache format: 4-bit (the headline) or 8-bit V codes")
     ap.add_argument("--copies", type=int, default=8, help="pool copies rotated for a cold cache")
     ap.add_argument("--splits", type=int, default=0, help="0 = automatic split plan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -204,7 +206,10 @@ def main(argv=None):
     def dev_t(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    caches = [kvq.PagedCache.allocate(wl.pool_pages, wl.page_size, wl.num_kv_heads, D, dev)]
+    fmt = kvq.FORMATS[args.kv_format]
+    vbits = 8 if fmt == kvq.KVQ_FORMAT_K8V8 else 4
+    caches = [kvq.PagedCache.allocate(wl.pool_pages, wl.page_size, wl.num_kv_heads, D, dev,
+                                      kv_format=fmt)]
     k_pre, v_pre, s_pre = (dev_t(x) for x in inp.prefill())
     # The prefill append (one kvq_append call per sequence, over all its cached tokens, as an
     # engine's prefill writes them) is timed too: once to fill the pool, then `reps` more times
@@ -225,12 +230,13 @@ def main(argv=None):
     e1.record()
     torch.cuda.synchronize()
     prefill_us = e0.elapsed_time(e1) * 1e3 / reps
-    prefill_bytes = n_pre * wl.num_kv_heads * (2 * D * 4 + token_bytes(D)) + n_pre * 4
+    prefill_bytes = n_pre * wl.num_kv_heads * (2 * D * 4 + token_bytes(D, vbits)) + n_pre * 4
     log(f"[bench] prefill append of {n_pre} tokens: {prefill_us:.1f} us, "
         f"{prefill_bytes / prefill_us / 1e3:.0f} GB/s")
     del k_pre, v_pre, apps
     for _ in range(args.copies - 1):
-        c = kvq.PagedCache.allocate(wl.pool_pages, wl.page_size, wl.num_kv_heads, D, dev)
+        c = kvq.PagedCache.allocate(wl.pool_pages, wl.page_size, wl.num_kv_heads, D, dev,
+                                    kv_format=fmt)
         c.pool.copy_(caches[0].pool)
         caches.append(c)
     k_new, v_new, s_new = (dev_t(x) for x in inp.step_tokens())
@@ -291,8 +297,8 @@ def main(argv=None):
     log(f"[bench] {args.steps} steps in {total_ms:.2f} ms (wall {wall * 1e3:.1f} ms): "
         f"{ms_per_step * 1e3:.1f} us per step")
 
-    dec_bytes = decode_algorithmic_bytes(wl, inp.seq_lens)
-    step_bytes = dec_bytes + (append_algorithmic_bytes(wl) if wl.n_new else 0)
+    dec_bytes = decode_algorithmic_bytes(wl, inp.seq_lens, vbits)
+    step_bytes = dec_bytes + (append_algorithmic_bytes(wl, vbits) if wl.n_new else 0)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = value  # the step is one call: the attention launch (with the append) + the merge
 
@@ -301,7 +307,8 @@ def main(argv=None):
     if os.path.exists(pmc_file):
         with open(pmc_file) as f:
             pmc = json.load(f)
-        if pmc.get("source_hash") == source_hash() and pmc.get("workload") == name:
+        if (pmc.get("source_hash") == source_hash() and pmc.get("workload") == name and
+                args.kv_format == "k8v4"):
             traffic = pmc.get("hbm_bytes_per_launch")
 
     if args.copy_probe_mib:
@@ -333,7 +340,8 @@ def main(argv=None):
             "kv_heads": wl.num_kv_heads, "q_heads": wl.n_q_heads, "head_dim": D,
             "page_size": wl.page_size, "pool_pages": wl.pool_pages,
             "page_order": wl.page_order, "query_rows": wl.n_rows, "new_tokens_per_seq": wl.n_new,
-            "kv_format": "K int8/token scale, V int4/32-dim scale", "splits": splits,
+            "kv_format": ("K int8/token scale, V int8/32-dim scale" if vbits == 8 else
+                          "K int8/token scale, V int4/32-dim scale"), "splits": splits,
             "pool_copies": len(caches), "parallelism": "single GPU",
         },
         "roofline": {

@@ -38,7 +38,7 @@ extern "C" {
 /* ---- return codes ---------------------------------------------------------------------- */
 #define KVQ_OK               0
 #define KVQ_ERR_ARG         (-1)  /* NULL pointer where one is required, or a size <= 0 / inconsistent */
-#define KVQ_ERR_UNSUPPORTED (-2)  /* head_dim, page_size or rows-per-KV-head outside what is built   */
+#define KVQ_ERR_UNSUPPORTED (-2)  /* head_dim, page_size, rows-per-KV-head or KV format not built     */
 #define KVQ_ERR_WORKSPACE   (-3)  /* workspace NULL or smaller than kvq_decode_workspace_bytes()      */
 #define KVQ_ERR_HIP         (-4)  /* a HIP launch reported an error (hipGetLastError)                 */
 
@@ -88,6 +88,26 @@ extern "C" {
  * tokens never write the same byte.
  */
 size_t kvq_block_bytes(int32_t page_size, int32_t head_dim);
+
+/* ---- KV formats ------------------------------------------------------------------------
+ * The calls above and below use K8/V4.  The _fmt variants take the format first:
+ *   KVQ_FORMAT_K8V4  4-bit V codes, the format above.
+ *   KVQ_FORMAT_K8V8  8-bit V codes: the int8 KV the same forum post sets against rk8v4 (一、部署
+ *                    and its replies: the same decode speed, a 160K- instead of a 180K-token
+ *                    pool).  K, its scales and the V scales are as above, and V is quantized as
+ *                    above with 127 in place of 7, codes in [-127, 127] stored as int8.  The
+ *                    block is [K codes P*D][K scales 2P][V codes P*D][V scales P*D/16], so
+ *                    block_bytes = P * (2D + 2 + D/16) (33,920 B for P=64, D=256).  In a tile,
+ *                    with j = d/32, lane = 16*(t/4) + d%16, w = min(D/32, 2):
+ *                      V code (t, d):  byte  16*D*tile + 512*w*(j/w) + 8*w*lane + 8*(j%w)
+ *                                            + 4*((d/16)%2) + t%4   (int8)
+ *                    (the two nibbles of a 4-bit byte become two bytes, 4 apart).
+ * kvq_decode_num_splits and kvq_decode_workspace_bytes do not depend on the format. */
+#define KVQ_FORMAT_K8V4 0
+#define KVQ_FORMAT_K8V8 1
+
+/* Block bytes of a format (0 for an unknown format or unsupported shape).  Host only. */
+size_t kvq_block_bytes_fmt(int32_t kv_format, int32_t page_size, int32_t head_dim);
 
 /* ---- kvq_append ------------------------------------------------------------------------
  * Quantizes n_tok new tokens and writes each into its cache slot.
@@ -185,6 +205,25 @@ int32_t kvq_decode_num_splits(int32_t n_seq, int32_t num_kv_heads, int32_t max_s
 size_t kvq_decode_workspace_bytes(int32_t n_seq, int32_t n_rows, int32_t n_q_heads,
                                   int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
                                   int32_t num_splits_request);
+
+/* The calls above in a given KV format (pool laid out as that format defines; an unknown
+ * format returns KVQ_ERR_UNSUPPORTED).  Arguments otherwise as documented above. */
+int kvq_append_fmt(int32_t kv_format, void* pool, int32_t num_pages, int32_t page_size,
+                   int32_t num_kv_heads, int32_t head_dim, const float* k, const float* v,
+                   const int32_t* slot_mapping, int32_t n_tok, void* stream);
+int kvq_decode_attn_fmt(int32_t kv_format, const void* pool, int32_t num_pages, int32_t page_size,
+                        int32_t num_kv_heads, int32_t head_dim, const uint16_t* q,
+                        const int32_t* page_table, const int32_t* seq_lens, int32_t n_seq,
+                        int32_t n_rows, int32_t n_q_heads, int32_t max_pages_per_seq,
+                        int32_t max_seq_len, float softmax_scale, int32_t num_splits, float* out,
+                        float* lse, void* workspace, size_t workspace_bytes, void* stream);
+int kvq_decode_step_fmt(int32_t kv_format, void* pool, int32_t num_pages, int32_t page_size,
+                        int32_t num_kv_heads, int32_t head_dim, const float* k_new,
+                        const float* v_new, int32_t n_new, const uint16_t* q,
+                        const int32_t* page_table, const int32_t* seq_lens, int32_t n_seq,
+                        int32_t n_rows, int32_t n_q_heads, int32_t max_pages_per_seq,
+                        int32_t max_seq_len, float softmax_scale, int32_t num_splits, float* out,
+                        float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a return code. */
 const char* kvq_strerror(int code);

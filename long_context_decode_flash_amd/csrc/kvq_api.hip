@@ -10,6 +10,10 @@ namespace {
 
 bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
 bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
+// bits per V code of a KV format, or 0 for an unknown format
+int vbits_of(int32_t kv_format) {
+  return kv_format == KVQ_FORMAT_K8V4 ? 4 : kv_format == KVQ_FORMAT_K8V8 ? 8 : 0;
+}
 
 // Workgroups (4 waves each) the decode grid aims for: one per CU of the 256.
 constexpr long long kTargetGroups = 256;
@@ -56,12 +60,12 @@ size_t workspace_for(long long units, int splits, int rows, int head_dim) {
 }
 
 int pool_args_ok(const void* pool, int32_t num_pages, int32_t page_size, int32_t num_kv_heads,
-                 int32_t head_dim) {
+                 int32_t head_dim, int vb) {
   if (!pool || num_pages <= 0 || num_kv_heads <= 0 || page_size <= 0) return KVQ_ERR_ARG;
-  if (!head_dim_ok(head_dim) || !pow2_in(page_size, 16, 256)) return KVQ_ERR_UNSUPPORTED;
+  if (vb == 0 || !head_dim_ok(head_dim) || !pow2_in(page_size, 16, 256)) return KVQ_ERR_UNSUPPORTED;
   if (((uintptr_t)pool & 15) != 0) return KVQ_ERR_ARG;
   // one page of all KV heads stays below 4 GiB (the kernels address within it in 32 bits)
-  if ((unsigned long long)num_kv_heads * kvq::block_bytes(page_size, head_dim) >= (1ULL << 32))
+  if ((unsigned long long)num_kv_heads * kvq::block_bytes(page_size, head_dim, vb) >= (1ULL << 32))
     return KVQ_ERR_UNSUPPORTED;
   return KVQ_OK;
 }
@@ -70,9 +74,14 @@ int pool_args_ok(const void* pool, int32_t num_pages, int32_t page_size, int32_t
 
 extern "C" {
 
+size_t kvq_block_bytes_fmt(int32_t kv_format, int32_t page_size, int32_t head_dim) {
+  const int vb = vbits_of(kv_format);
+  if (vb == 0 || !head_dim_ok(head_dim) || !pow2_in(page_size, 16, 256)) return 0;
+  return kvq::block_bytes(page_size, head_dim, vb);
+}
+
 size_t kvq_block_bytes(int32_t page_size, int32_t head_dim) {
-  if (!head_dim_ok(head_dim) || !pow2_in(page_size, 16, 256)) return 0;
-  return kvq::block_bytes(page_size, head_dim);
+  return kvq_block_bytes_fmt(KVQ_FORMAT_K8V4, page_size, head_dim);
 }
 
 const char* kvq_strerror(int code) {
@@ -105,31 +114,40 @@ size_t kvq_decode_workspace_bytes(int32_t n_seq, int32_t n_rows, int32_t n_q_hea
   return workspace_for((long long)n_seq * num_kv_heads, p.splits, rows, head_dim);
 }
 
-int kvq_append(void* pool, int32_t num_pages, int32_t page_size, int32_t num_kv_heads,
-               int32_t head_dim, const float* k, const float* v, const int32_t* slot_mapping,
-               int32_t n_tok, void* stream) {
-  int rc = pool_args_ok(pool, num_pages, page_size, num_kv_heads, head_dim);
+int kvq_append_fmt(int32_t kv_format, void* pool, int32_t num_pages, int32_t page_size,
+                   int32_t num_kv_heads, int32_t head_dim, const float* k, const float* v,
+                   const int32_t* slot_mapping, int32_t n_tok, void* stream) {
+  const int vb = vbits_of(kv_format);
+  int rc = pool_args_ok(pool, num_pages, page_size, num_kv_heads, head_dim, vb);
   if (rc != KVQ_OK) return rc;
   if (n_tok < 0) return KVQ_ERR_ARG;
   if (n_tok == 0) return KVQ_OK;
   if (!k || !v || !slot_mapping) return KVQ_ERR_ARG;
   if ((long long)n_tok * num_kv_heads > (1LL << 33)) return KVQ_ERR_ARG;
-  kvq::AppendArgs a{(uint8_t*)pool, num_pages, page_size, num_kv_heads, k, v, slot_mapping, n_tok};
+  kvq::AppendArgs a{(uint8_t*)pool, num_pages, page_size, num_kv_heads, vb, k, v, slot_mapping, n_tok};
   (void)hipGetLastError();  // start from a clean error state
   return kvq::launch_append(head_dim, a, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+int kvq_append(void* pool, int32_t num_pages, int32_t page_size, int32_t num_kv_heads,
+               int32_t head_dim, const float* k, const float* v, const int32_t* slot_mapping,
+               int32_t n_tok, void* stream) {
+  return kvq_append_fmt(KVQ_FORMAT_K8V4, pool, num_pages, page_size, num_kv_heads, head_dim, k, v,
+                        slot_mapping, n_tok, stream);
 }
 
 }  // extern "C"
 
 namespace {
 
-int decode_impl(const void* pool, int32_t num_pages, int32_t page_size, int32_t num_kv_heads,
-                int32_t head_dim, const float* k_new, const float* v_new, int32_t n_new,
+int decode_impl(int32_t kv_format, const void* pool, int32_t num_pages, int32_t page_size,
+                int32_t num_kv_heads, int32_t head_dim, const float* k_new, const float* v_new, int32_t n_new,
                 const uint16_t* q, const int32_t* page_table, const int32_t* seq_lens, int32_t n_seq,
                 int32_t n_rows, int32_t n_q_heads, int32_t max_pages_per_seq, int32_t max_seq_len,
                 float softmax_scale, int32_t num_splits, float* out, float* lse, void* workspace,
                 size_t workspace_bytes, void* stream) {
-  int rc = pool_args_ok(pool, num_pages, page_size, num_kv_heads, head_dim);
+  const int vb = vbits_of(kv_format);
+  int rc = pool_args_ok(pool, num_pages, page_size, num_kv_heads, head_dim, vb);
   if (rc != KVQ_OK) return rc;
   if (!q || !page_table || !seq_lens || !out) return KVQ_ERR_ARG;
   if (n_seq <= 0 || n_q_heads <= 0 || max_pages_per_seq <= 0 || max_seq_len <= 0 ||
@@ -157,6 +175,7 @@ int decode_impl(const void* pool, int32_t num_pages, int32_t page_size, int32_t 
   a.num_pages = num_pages;
   a.page_size = page_size;
   a.num_kv_heads = num_kv_heads;
+  a.vbits = vb;
   a.log2_page = __builtin_ctz((unsigned)page_size);
   a.q = q;
   a.page_table = page_table;
@@ -187,15 +206,43 @@ int decode_impl(const void* pool, int32_t num_pages, int32_t page_size, int32_t 
 
 extern "C" {
 
+int kvq_decode_attn_fmt(int32_t kv_format, const void* pool, int32_t num_pages, int32_t page_size,
+                        int32_t num_kv_heads, int32_t head_dim, const uint16_t* q,
+                        const int32_t* page_table, const int32_t* seq_lens, int32_t n_seq,
+                        int32_t n_rows, int32_t n_q_heads, int32_t max_pages_per_seq,
+                        int32_t max_seq_len, float softmax_scale, int32_t num_splits, float* out,
+                        float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(kv_format, pool, num_pages, page_size, num_kv_heads, head_dim, nullptr, nullptr, 0,
+                     q, page_table, seq_lens, n_seq, n_rows, n_q_heads, max_pages_per_seq,
+                     max_seq_len, softmax_scale, num_splits, out, lse, workspace, workspace_bytes,
+                     stream);
+}
+
 int kvq_decode_attn(const void* pool, int32_t num_pages, int32_t page_size,
                     int32_t num_kv_heads, int32_t head_dim, const uint16_t* q,
                     const int32_t* page_table, const int32_t* seq_lens, int32_t n_seq,
                     int32_t n_rows, int32_t n_q_heads, int32_t max_pages_per_seq,
                     int32_t max_seq_len, float softmax_scale, int32_t num_splits, float* out,
                     float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_impl(pool, num_pages, page_size, num_kv_heads, head_dim, nullptr, nullptr, 0, q,
-                     page_table, seq_lens, n_seq, n_rows, n_q_heads, max_pages_per_seq, max_seq_len,
-                     softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
+  return kvq_decode_attn_fmt(KVQ_FORMAT_K8V4, pool, num_pages, page_size, num_kv_heads, head_dim, q,
+                             page_table, seq_lens, n_seq, n_rows, n_q_heads, max_pages_per_seq,
+                             max_seq_len, softmax_scale, num_splits, out, lse, workspace,
+                             workspace_bytes, stream);
+}
+
+int kvq_decode_step_fmt(int32_t kv_format, void* pool, int32_t num_pages, int32_t page_size,
+                        int32_t num_kv_heads, int32_t head_dim, const float* k_new,
+                        const float* v_new, int32_t n_new, const uint16_t* q,
+                        const int32_t* page_table, const int32_t* seq_lens, int32_t n_seq,
+                        int32_t n_rows, int32_t n_q_heads, int32_t max_pages_per_seq,
+                        int32_t max_seq_len, float softmax_scale, int32_t num_splits, float* out,
+                        float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_new < 0 || n_new > KVQ_MAX_STEP_TOKENS) return KVQ_ERR_ARG;
+  if (n_new > 0 && (!k_new || !v_new)) return KVQ_ERR_ARG;
+  return decode_impl(kv_format, pool, num_pages, page_size, num_kv_heads, head_dim, k_new, v_new, n_new,
+                     q, page_table, seq_lens, n_seq, n_rows, n_q_heads, max_pages_per_seq,
+                     max_seq_len, softmax_scale, num_splits, out, lse, workspace, workspace_bytes,
+                     stream);
 }
 
 int kvq_decode_step(void* pool, int32_t num_pages, int32_t page_size, int32_t num_kv_heads,
@@ -204,11 +251,10 @@ int kvq_decode_step(void* pool, int32_t num_pages, int32_t page_size, int32_t nu
                     int32_t n_seq, int32_t n_rows, int32_t n_q_heads, int32_t max_pages_per_seq,
                     int32_t max_seq_len, float softmax_scale, int32_t num_splits, float* out,
                     float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-  if (n_new < 0 || n_new > KVQ_MAX_STEP_TOKENS) return KVQ_ERR_ARG;
-  if (n_new > 0 && (!k_new || !v_new)) return KVQ_ERR_ARG;
-  return decode_impl(pool, num_pages, page_size, num_kv_heads, head_dim, k_new, v_new, n_new, q,
-                     page_table, seq_lens, n_seq, n_rows, n_q_heads, max_pages_per_seq, max_seq_len,
-                     softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
+  return kvq_decode_step_fmt(KVQ_FORMAT_K8V4, pool, num_pages, page_size, num_kv_heads, head_dim, k_new,
+                             v_new, n_new, q, page_table, seq_lens, n_seq, n_rows, n_q_heads,
+                             max_pages_per_seq, max_seq_len, softmax_scale, num_splits, out, lse,
+                             workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

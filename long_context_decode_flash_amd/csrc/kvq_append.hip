@@ -20,9 +20,9 @@ __device__ inline void copy16(uint8_t* dst, const uint8_t* src, int bytes, int l
   for (int o = 16 * lane; o < bytes; o += 16 * kWave) *(uint4*)(dst + o) = *(const uint4*)(src + o);
 }
 
-template <int D>
+template <int D, int VB>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
-  constexpr int TB = (int)block_bytes(kTile, D);  // one tile as a one-tile page
+  constexpr int TB = (int)block_bytes(kTile, D, VB);  // one tile as a one-tile page
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[4][TB];
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x >> 6;
@@ -50,14 +50,14 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   if (whole) {
     uint8_t* st = s_tile[wv];
 #pragma unroll
-    for (int i = 0; i < kTokensPerWave; ++i) store_row<D>(st, kTile, i, rv[i], lane);
+    for (int i = 0; i < kTokensPerWave; ++i) store_row<D, VB>(st, kTile, i, rv[i], lane);
     const int page = (int)(s0 / P), tile = (int)(s0 % P) / kTile;
-    uint8_t* blk = a.pool + ((size_t)page * a.num_kv_heads + h) * block_bytes(P, D);
+    uint8_t* blk = a.pool + ((size_t)page * a.num_kv_heads + h) * block_bytes(P, D, VB);
     copy16<D>(blk + (size_t)kTile * D * tile, st, kTile * D, lane);                                 // K codes
     copy16<D>(blk + k_scales_at(P, D) + 2 * kTile * tile, st + k_scales_at(kTile, D), 2 * kTile, lane);
-    copy16<D>(blk + v_codes_at(P, D) + (size_t)(kTile / 2) * D * tile, st + v_codes_at(kTile, D), kTile * D / 2,
-              lane);
-    copy16<D>(blk + v_scales_at(P, D) + (size_t)2 * kTile * (D / 32) * tile, st + v_scales_at(kTile, D),
+    constexpr int VT = kTile * D * VB / 8;  // V code bytes of one tile
+    copy16<D>(blk + v_codes_at(P, D) + (size_t)VT * tile, st + v_codes_at(kTile, D), VT, lane);
+    copy16<D>(blk + v_scales_at(P, D, VB) + (size_t)2 * kTile * (D / 32) * tile, st + v_scales_at(kTile, D, VB),
               2 * kTile * (D / 32), lane);
     return;
   }
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     const long long slot = __builtin_amdgcn_readlane((int)my_slot, i);
     if (i < cnt && slot >= 0 && slot < pool_slots) {  // padding / out of pool: skip
       const int page = (int)(slot / P), s = (int)(slot % P);
-      store_row<D>(a.pool + ((size_t)page * a.num_kv_heads + h) * block_bytes(P, D), P, s, rv[i], lane);
+      store_row<D, VB>(a.pool + ((size_t)page * a.num_kv_heads + h) * block_bytes(P, D, VB), P, s, rv[i], lane);
     }
   }
 }
@@ -77,10 +77,20 @@ hipError_t launch_append(int head_dim, const AppendArgs& a, hipStream_t stream) 
   const long long groups = ((long long)a.n_tok + kTokensPerWave - 1) / kTokensPerWave;
   const long long items = groups * a.num_kv_heads;
   const unsigned grid = (unsigned)((items + 3) / 4);
+  const bool v8 = a.vbits == 8;
   switch (head_dim) {
-    case 64: hipLaunchKernelGGL(append_kernel<64>, dim3(grid), dim3(256), 0, stream, a); break;
-    case 128: hipLaunchKernelGGL(append_kernel<128>, dim3(grid), dim3(256), 0, stream, a); break;
-    case 256: hipLaunchKernelGGL(append_kernel<256>, dim3(grid), dim3(256), 0, stream, a); break;
+    case 64:
+      if (v8) hipLaunchKernelGGL((append_kernel<64, 8>), dim3(grid), dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL((append_kernel<64, 4>), dim3(grid), dim3(256), 0, stream, a);
+      break;
+    case 128:
+      if (v8) hipLaunchKernelGGL((append_kernel<128, 8>), dim3(grid), dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL((append_kernel<128, 4>), dim3(grid), dim3(256), 0, stream, a);
+      break;
+    case 256:
+      if (v8) hipLaunchKernelGGL((append_kernel<256, 8>), dim3(grid), dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL((append_kernel<256, 4>), dim3(grid), dim3(256), 0, stream, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -60,6 +60,19 @@ __device__ inline void i4x8_to_h2x4(uint32_t x, uint32_t& lo02, uint32_t& lo13, 
   hi13 = as_u32(__builtin_elementwise_fma(as_h2((x8 & 0x00F000F0u) ^ 0x64806480u), sixteenth, off_hi));
 }
 
+// The 8-bit form: lo_w holds, for four tokens r = 0..3 (byte r), the int8 codes of a dim of the
+// even 16-dim block, hi_w the same dim of the odd block.  Same outputs as i4x8_to_h2x4: byte b
+// (code c) xor 0x80 is c + 128, and 0x6400 | m is the fp16 value 1024 + m, so
+// ((x & 0x00FF00FF) ^ 0x64806480) - 1152 per half is c, exactly.
+__device__ inline void i8x8_to_h2x4(uint32_t lo_w, uint32_t hi_w, uint32_t& lo02, uint32_t& lo13,
+                                    uint32_t& hi02, uint32_t& hi13) {
+  const half2v off = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  lo02 = as_u32(as_h2((lo_w & 0x00FF00FFu) ^ 0x64806480u) + off);
+  lo13 = as_u32(as_h2(((lo_w >> 8) & 0x00FF00FFu) ^ 0x64806480u) + off);
+  hi02 = as_u32(as_h2((hi_w & 0x00FF00FFu) ^ 0x64806480u) + off);
+  hi13 = as_u32(as_h2(((hi_w >> 8) & 0x00FF00FFu) ^ 0x64806480u) + off);
+}
+
 // p0 * s0 and p1 * s1 (p fp32, s an fp16 half of sw0 / sw1 selected by SH) as fp16 hi + lo pairs:
 // hi = rne(p * s) and lo = rne(p * s - hi) straight from the exact products (v_fma_mix*), so the
 // two halves always belong together and hi + lo = p * s to about 2^-22.
@@ -161,10 +174,10 @@ __device__ inline uint32_t wave_max_u16x2(uint32_t x) {
   return mx(x, (x >> 16) | (x << 16));
 }
 
-template <int D>
+template <int D, int VB>
 struct TileRaw {
   static constexpr int kLoadsK = D / 64;                    // 16-byte loads of K codes per lane
-  static constexpr int kVWords = D / 32;                    // V code dwords per lane
+  static constexpr int kVWords = D * VB / 128;              // V code dwords per lane
   static constexpr int kVsWords = D / 16;                   // V scale dwords per lane (4 tokens x D/32)
   u32x4 k[kLoadsK];
   uint32_t v[kVWords];
@@ -174,18 +187,21 @@ struct TileRaw {
 
 // ---- staging of one block (two tiles) in LDS --------------------------------------------
 // A staged tile is an exact copy of the tile's four sections, packed:
-//   [K codes 16*D][V codes 8*D][V scales D][K scales 32]  = 25*D + 32 bytes.
-template <int D>
+//   [K codes 16*D][V codes 16*D*VB/8][V scales D][K scales 32]  (25*D + 32 bytes for 4-bit V
+// codes, 33*D + 32 for 8-bit ones).
+template <int D, int VB>
 struct Stage {
   static constexpr int kK = 0;
   static constexpr int kV = 16 * D;
-  static constexpr int kVs = 24 * D;
-  static constexpr int kKs = 25 * D;
-  static constexpr int kTileBytes = 25 * D + 32;
+  static constexpr int kVBytes = 2 * D * VB;  // V codes of a tile
+  static constexpr int kVs = kV + kVBytes;
+  static constexpr int kKs = kVs + D;
+  static constexpr int kTileBytes = kKs + 32;
   static constexpr int kBlockBytes = 2 * kTileBytes;
   // direct-to-LDS loads per block (vmcnt units): K codes, V codes, then V and K scales in one
   // load (they sit back to back in the stage, D/16 lanes of V scales and 2 of K scales)
-  static constexpr int kLoads = 2 * (D / 64 + (D >= 128 ? D / 128 : 1) + 1);
+  static constexpr int kLoadsV = VB == 8 ? D / 64 : (D >= 128 ? D / 128 : 1);
+  static constexpr int kLoads = 2 * (D / 64 + kLoadsV + 1);
   static constexpr int kScaleLanes = D / 16 + 2;
 };
 
@@ -242,54 +258,66 @@ struct ScaleLane {
   uint32_t off0, step;
 };
 
-template <int D>
+template <int D, int VB>
 __device__ inline ScaleLane scale_lane(int P, int lane) {
-  if (lane < D / 16) return {(uint32_t)v_scales_at(P, D) + 16u * lane, (uint32_t)(D / 16)};
+  if (lane < D / 16) return {(uint32_t)v_scales_at(P, D, VB) + 16u * lane, (uint32_t)(D / 16)};
   const int kl = min(lane - D / 16, 1);  // lanes past the two K-scale lanes are masked off
   return {(uint32_t)k_scales_at(P, D) + 16u * kl, 2u};
 }
 
 // Issue the loads of one tile of the (page, KV head) block at pb (slot0 = the tile's first slot
 // in the page) into LDS at byte address dst (wave-uniform).
-template <int D>
+template <int D, int VB>
 __device__ inline void stage_tile(const uint8_t* pb, int P, int slot0, uint32_t dst, uint32_t lane16,
                                   ScaleLane sl) {
   static_assert(D == 64 || D == 128 || D == 256, "head_dim");
+  using S = Stage<D, VB>;
   const uint32_t tip = (uint32_t)slot0 >> 4;  // offsets within one block are 32-bit
-  dma16<D / 64>(pb + tip * (16u * D), lane16, dst + Stage<D>::kK);
-  const uint8_t* vb = pb + ((uint32_t)v_codes_at(P, D) + tip * (8u * D));
-  if constexpr (D >= 128)
-    dma16<D / 128>(vb, lane16, dst + Stage<D>::kV);
+  dma16<D / 64>(pb + tip * (16u * D), lane16, dst + S::kK);
+  const uint8_t* vb = pb + ((uint32_t)v_codes_at(P, D) + tip * (uint32_t)S::kVBytes);
+  if constexpr (VB == 8)
+    dma16<D / 64>(vb, lane16, dst + S::kV);
+  else if constexpr (D >= 128)
+    dma16<D / 128>(vb, lane16, dst + S::kV);
   else
-    dma16<1, 32>(vb, lane16, dst + Stage<D>::kV);
-  dma16<1, Stage<D>::kScaleLanes>(pb, sl.off0 + (uint32_t)slot0 * sl.step, dst + Stage<D>::kVs);
+    dma16<1, 32>(vb, lane16, dst + S::kV);
+  dma16<1, S::kScaleLanes>(pb, sl.off0 + (uint32_t)slot0 * sl.step, dst + S::kVs);
 }
 
 // Read one staged tile into this lane's registers (the lane's share of every section).
-template <int D>
-__device__ inline void read_tile(TileRaw<D>& r, const uint8_t* src, int lane) {
+template <int D, int VB>
+__device__ inline void read_tile(TileRaw<D, VB>& r, const uint8_t* src, int lane) {
+  using S = Stage<D, VB>;
   const int g = lane >> 4;
 #pragma unroll
-  for (int jj = 0; jj < TileRaw<D>::kLoadsK; ++jj)
-    r.k[jj] = *(const u32x4*)(src + Stage<D>::kK + 1024 * jj + 16 * lane);
-  const u32x2 ks = *(const u32x2*)(src + Stage<D>::kKs + 8 * g);
+  for (int jj = 0; jj < TileRaw<D, VB>::kLoadsK; ++jj)
+    r.k[jj] = *(const u32x4*)(src + S::kK + 1024 * jj + 16 * lane);
+  const u32x2 ks = *(const u32x2*)(src + S::kKs + 8 * g);
   r.ks[0] = ks[0];
   r.ks[1] = ks[1];
-  if constexpr (D == 64) {
-    const u32x2 w = *(const u32x2*)(src + Stage<D>::kV + 8 * lane);
+  if constexpr (VB == 8) {
+    // 16 bytes per lane per 1 KB: two scale groups' (even-block dim, odd-block dim) dwords
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c) {
+      const u32x4 w = *(const u32x4*)(src + S::kV + 1024 * c + 16 * lane);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r.v[4 * c + e] = w[e];
+    }
+  } else if constexpr (D == 64) {
+    const u32x2 w = *(const u32x2*)(src + S::kV + 8 * lane);
     r.v[0] = w[0];
     r.v[1] = w[1];
   } else {
 #pragma unroll
     for (int c = 0; c < D / 128; ++c) {
-      const u32x4 w = *(const u32x4*)(src + Stage<D>::kV + 1024 * c + 16 * lane);
+      const u32x4 w = *(const u32x4*)(src + S::kV + 1024 * c + 16 * lane);
 #pragma unroll
       for (int e = 0; e < 4; ++e) r.v[4 * c + e] = w[e];
     }
   }
 #pragma unroll
-  for (int c = 0; c < TileRaw<D>::kVsWords / 4; ++c) {
-    const u32x4 w = *(const u32x4*)(src + Stage<D>::kVs + g * (D / 4) + 16 * c);
+  for (int c = 0; c < TileRaw<D, VB>::kVsWords / 4; ++c) {
+    const u32x4 w = *(const u32x4*)(src + S::kVs + g * (D / 4) + 16 * c);
 #pragma unroll
     for (int e = 0; e < 4; ++e) r.vs[4 * c + e] = w[e];
   }
@@ -301,9 +329,9 @@ __device__ inline void read_tile(TileRaw<D>& r, const uint8_t* src, int lane) {
 //          sums of 2^(z - base) * (1, v);  it only moves up, in whole powers of two, when a block's
 //          largest logit and V scale would push p * v_scale past 2^15 (fp16 headroom), so most
 //          blocks rescale nothing and every rescale is exact.
-template <int D, int NB>
+template <int D, int NB, int VB>
 __device__ __attribute__((always_inline)) inline void process_block(
-    TileRaw<D> (&raw)[2], int blk, bool masked, float e5, const i32x4 (&qd)[NB][3][D / 64], const float (&cz)[NB],
+    TileRaw<D, VB> (&raw)[2], int blk, bool masked, float e5, const i32x4 (&qd)[NB][3][D / 64], const float (&cz)[NB],
     const int (&last_tok)[NB], int g, floatx4 (&acc)[NB][D / 16], float (&base)[NB],
     float (&l_run)[NB]) {
   constexpr int DB = D / 16;
@@ -400,7 +428,12 @@ __device__ __attribute__((always_inline)) inline void process_block(
   for (int j = 0; j < NG; ++j) {
     uint32_t l02[2], l13[2], h02[2], h13[2];
 #pragma unroll
-    for (int tau = 0; tau < 2; ++tau) i4x8_to_h2x4(raw[tau].v[j], l02[tau], l13[tau], h02[tau], h13[tau]);
+    for (int tau = 0; tau < 2; ++tau) {
+      if constexpr (VB == 8)
+        i8x8_to_h2x4(raw[tau].v[2 * j], raw[tau].v[2 * j + 1], l02[tau], l13[tau], h02[tau], h13[tau]);
+      else
+        i4x8_to_h2x4(raw[tau].v[j], l02[tau], l13[tau], h02[tau], h13[tau]);
+    }
     const half8 vlo = __builtin_bit_cast(half8, u32x4{l02[0], l13[0], l02[1], l13[1]});
     const half8 vhi = __builtin_bit_cast(half8, u32x4{h02[0], h13[0], h02[1], h13[1]});
 #pragma unroll
@@ -437,14 +470,16 @@ __device__ __attribute__((always_inline)) inline void process_block(
 // Each wave streams its blocks through three LDS stage buffers with direct-to-LDS loads, so two
 // blocks are in flight while it computes the third.  The waves merge through LDS into one
 // partial (the output itself when the context is a single piece).
-template <int D, int NB>
+template <int D, int NB, int VB>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   constexpr int DB = D / 16;
   constexpr int ROWS = 16 * NB;
   constexpr int LDS_STRIDE = D + 4;  // floats; padding spreads the 16 rows over banks
-  constexpr int NSTAGE = 3;
-  constexpr int BS = Stage<D>::kBlockBytes;
-  constexpr int NL = Stage<D>::kLoads;
+  // stage buffers per wave: three (two blocks in flight while one is processed), two where a
+  // block of 8-bit V codes at D = 256 leaves no room for a third
+  constexpr int NSTAGE = (VB == 8 && D == 256) ? 2 : 3;
+  constexpr int BS = Stage<D, VB>::kBlockBytes;
+  constexpr int NL = Stage<D, VB>::kLoads;
   constexpr int CHUNK = kWavesPerGroup * 32;  // blocks per chunk: 32 per wave, page ids in lanes
   static_assert(2 * NL <= 63, "vmcnt range");
   // After the main loop the same LDS holds the wave merge (4 waves x ROWS x LDS_STRIDE floats).
@@ -469,7 +504,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int g_blk0 = split * a.blocks_per_split;
   const int g_blk1 = min(g_blk0 + a.blocks_per_split, nblk);
   const int m16 = lane & 15, g = lane >> 4;
-  const size_t bb = block_bytes(P, D);
+  const size_t bb = block_bytes(P, D, VB);
   const size_t page_stride = (size_t)a.num_kv_heads * bb;
   const uint8_t* pool_h = a.pool + (size_t)h * bb;
   const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
@@ -520,7 +555,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const uint8_t* my_stage = &s_stage[w][0][0];
   const uint32_t lane16 = 16u * lane;
   const uint32_t page_stride32 = (uint32_t)page_stride;  // < 2^32, checked on the host
-  const ScaleLane sl = scale_lane<D>(P, lane);
+  const ScaleLane sl = scale_lane<D, VB>(P, lane);
   uint32_t st_issue = my_stage_lds;
   auto issue = [&](int k, uint32_t dst) {
 #pragma unroll
@@ -530,12 +565,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       const bool past = tok0 >= Lc;  // a tile past the end stages tile 0 again, all of it masked
       if (past) tok0 = blk * kBlock;
       const int phys = __builtin_amdgcn_readlane(my_pid, (tau == 1 && !past) ? 32 + k : k);
-      stage_tile<D>(pool_h + (uint64_t)(uint32_t)phys * page_stride32, P, tok0 & (P - 1),
-                    dst + (uint32_t)(tau * Stage<D>::kTileBytes), lane16, sl);
+      stage_tile<D, VB>(pool_h + (uint64_t)(uint32_t)phys * page_stride32, P, tok0 & (P - 1),
+                    dst + (uint32_t)(tau * Stage<D, VB>::kTileBytes), lane16, sl);
     }
   };
   // stage buffer of block k: k % 3, tracked incrementally
-  auto next_stage = [&](uint32_t x) { return x == my_stage_lds + 2 * BS ? my_stage_lds : x + BS; };
+  auto next_stage = [&](uint32_t x) { return x == my_stage_lds + (NSTAGE - 1) * BS ? my_stage_lds : x + BS; };
   // chunk set-up: this wave's page ids into lanes, then the loads of its first two blocks
   auto chunk_count = [&]() {
     const int c1 = min(c0 + CHUNK, g_blk1);
@@ -545,10 +580,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   auto chunk_start = [&]() {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // page ids in; the DMA counting starts here
     st_issue = my_stage_lds;
-    if (n_my > 0) issue(0, st_issue);
-    st_issue = next_stage(st_issue);
-    if (n_my > 1) issue(1, st_issue);
-    st_issue = next_stage(st_issue);
+#pragma unroll
+    for (int i = 0; i < NSTAGE - 1; ++i) {
+      if (n_my > i) issue(i, st_issue);
+      st_issue = next_stage(st_issue);
+    }
   };
   // The first chunk's first blocks are in flight while the queries are prepared (an empty split
   // gets n_my = 0).  The query words are used here on every path, so the compiler's own wait for
@@ -562,7 +598,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     if (t < 0 || blk < g_blk0 || blk >= g_blk1 || ((blk - g_blk0) & (kWavesPerGroup - 1)) != w) continue;
     const int page = min(max(pt[t >> lgP], 0), a.num_pages - 1);
     const size_t row = (((size_t)b * a.n_new + j) * a.num_kv_heads + h) * D;
-    append_row<D>(a.pool_rw + ((size_t)page * a.num_kv_heads + h) * bb, P, t & (P - 1), a.k_new + row,
+    append_row<D, VB>(a.pool_rw + ((size_t)page * a.num_kv_heads + h) * bb, P, t & (P - 1), a.k_new + row,
                   a.v_new + row, lane);
   }
   chunk_count();
@@ -640,15 +676,26 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   while (c0 < g_blk1) {
     int st_read = 0;
     for (int k = 0; k < n_my; ++k) {
-      if (k + 2 < n_my) {
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads of the buffer being refilled are done
-        issue(k + 2, st_issue);
-        st_issue = next_stage(st_issue);
-        wait_vmcnt<2 * NL>();
-      } else if (k + 1 < n_my) {
-        wait_vmcnt<NL>();
+      if constexpr (NSTAGE == 3) {
+        if (k + 2 < n_my) {
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads of the buffer being refilled are done
+          issue(k + 2, st_issue);
+          st_issue = next_stage(st_issue);
+          wait_vmcnt<2 * NL>();
+        } else if (k + 1 < n_my) {
+          wait_vmcnt<NL>();
+        } else {
+          wait_vmcnt<0>();
+        }
       } else {
-        wait_vmcnt<0>();
+        if (k + 1 < n_my) {
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads of the buffer being refilled are done
+          issue(k + 1, st_issue);
+          st_issue = next_stage(st_issue);
+          wait_vmcnt<NL>();
+        } else {
+          wait_vmcnt<0>();
+        }
       }
       const uint8_t* src = my_stage + st_read * BS;
       st_read = st_read == NSTAGE - 1 ? 0 : st_read + 1;
@@ -658,25 +705,25 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         // a slot past the context may hold junk scale bits, and 0 * Inf is no zero: clear the V
         // scales of those slots in the staged copy (the same wave reads them below, in order)
         if (blk * kBlock + lane >= Lc) {
-          uint8_t* vs = (uint8_t*)src + (lane >> 4) * Stage<D>::kTileBytes + Stage<D>::kVs + (lane & 15) * (D / 16);
+          uint8_t* vs = (uint8_t*)src + (lane >> 4) * Stage<D, VB>::kTileBytes + Stage<D, VB>::kVs + (lane & 15) * (D / 16);
           if constexpr (D == 256) *(u32x4*)vs = u32x4{0, 0, 0, 0};
           else if constexpr (D == 128) *(u32x2*)vs = u32x2{0, 0};
           else *(uint32_t*)vs = 0u;
         }
       }
-      TileRaw<D> raw[2];
-      read_tile<D>(raw[0], src, lane);
-      read_tile<D>(raw[1], src + Stage<D>::kTileBytes, lane);
+      TileRaw<D, VB> raw[2];
+      read_tile<D, VB>(raw[0], src, lane);
+      read_tile<D, VB>(raw[1], src + Stage<D, VB>::kTileBytes, lane);
       // binary exponent of the block's largest V scale (positive fp16: bit order is value order);
       // every scale is below 2^(e5 - 14)
       float e5;
       {
-        const uint32_t* vsw = (const uint32_t*)(src + Stage<D>::kVs) + (lane & (D / 4 - 1));
+        const uint32_t* vsw = (const uint32_t*)(src + Stage<D, VB>::kVs) + (lane & (D / 4 - 1));
         const uint32_t m = wave_max_u16x2(__builtin_bit_cast(uint32_t, __builtin_elementwise_max(
-            __builtin_bit_cast(u16x2, vsw[0]), __builtin_bit_cast(u16x2, vsw[Stage<D>::kTileBytes / 4]))));
+            __builtin_bit_cast(u16x2, vsw[0]), __builtin_bit_cast(u16x2, vsw[Stage<D, VB>::kTileBytes / 4]))));
         e5 = (float)((m >> 10) & 31);
       }
-      process_block<D, NB>(raw, blk, masked, e5, qd, cz, last_tok, g, acc, base, l_run);
+      process_block<D, NB, VB>(raw, blk, masked, e5, qd, cz, last_tok, g, acc, base, l_run);
     }
     c0 += CHUNK;
     if (c0 < g_blk1) {
@@ -793,10 +840,18 @@ template <int D>
 hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
   const unsigned units = (unsigned)((long long)a.n_seq * a.num_kv_heads);
   const unsigned grid = units * (unsigned)a.splits;
-  if (a.rows <= 16)
-    hipLaunchKernelGGL((decode_kernel<D, 1>), dim3(grid), dim3(kWave * kWavesPerGroup), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<D, 2>), dim3(grid), dim3(kWave * kWavesPerGroup), 0, stream, a);
+  const dim3 block(kWave * kWavesPerGroup);
+  if (a.vbits == 8) {
+    if (a.rows <= 16)
+      hipLaunchKernelGGL((decode_kernel<D, 1, 8>), dim3(grid), block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<D, 2, 8>), dim3(grid), block, 0, stream, a);
+  } else {
+    if (a.rows <= 16)
+      hipLaunchKernelGGL((decode_kernel<D, 1, 4>), dim3(grid), block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<D, 2, 4>), dim3(grid), block, 0, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   const unsigned per_unit = (unsigned)((a.rows * (D / 4) + kWave - 1) / kWave);

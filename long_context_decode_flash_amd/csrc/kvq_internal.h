@@ -16,13 +16,14 @@ constexpr int kWave = 64;
 constexpr int kWavesPerGroup = 4;  // waves of one decode workgroup
 constexpr int kMaxSplits = 128;    // workgroups per (sequence, KV head) at most
 
-__host__ __device__ constexpr size_t block_bytes(int P, int D) {
-  return (size_t)P * (size_t)(D + 2 + D / 2 + D / 16);
+// VB: bits per V code, 4 (K8/V4: two codes per byte) or 8 (K8/V8: one per byte).
+__host__ __device__ constexpr size_t block_bytes(int P, int D, int VB = 4) {
+  return (size_t)P * (size_t)(D + 2 + D * VB / 8 + D / 16);
 }
 __host__ __device__ constexpr size_t k_scales_at(int P, int D) { return (size_t)P * D; }
 __host__ __device__ constexpr size_t v_codes_at(int P, int D) { return (size_t)P * D + 2 * (size_t)P; }
-__host__ __device__ constexpr size_t v_scales_at(int P, int D) {
-  return (size_t)P * D + 2 * (size_t)P + (size_t)P * D / 2;
+__host__ __device__ constexpr size_t v_scales_at(int P, int D, int VB = 4) {
+  return (size_t)P * D + 2 * (size_t)P + (size_t)P * D * VB / 8;
 }
 
 // (max, sum) entries per unit in the decode workspace: splits x rows, rounded up to an even
@@ -32,6 +33,7 @@ __host__ __device__ constexpr int ml_stride(int splits, int rows) { return (spli
 struct AppendArgs {
   uint8_t* pool;
   int num_pages, page_size, num_kv_heads;
+  int vbits;  // 4 or 8
   const float* k;
   const float* v;
   const int32_t* slots;
@@ -41,6 +43,7 @@ struct AppendArgs {
 struct DecodeArgs {
   const uint8_t* pool;
   int num_pages, page_size, num_kv_heads;
+  int vbits;  // 4 or 8
   int log2_page;  // page_size = 1 << log2_page
   const uint16_t* q;
   const int32_t* page_table;

@@ -1,6 +1,6 @@
-// kvq_quant.h — the K8/V4 quantizer of one (token, KV head) row, written into its cache slot by
-// one 64-lane wave.  Shared by the append kernel and the decode kernel's fused append, so both
-// write the same bytes.
+// kvq_quant.h — the K8/V4 (and K8/V8) quantizer of one (token, KV head) row, written into its
+// cache slot by one 64-lane wave.  Shared by the append kernel and the decode kernel's fused
+// append, so both write the same bytes.
 //
 // K8/V4 ("rk8v4" in the launch-flag table of the forum post "3090 单卡跑 Qwen3.8-27B：NInfer
 // 上机实测（180K 上下文 / C2 并发 / 4bit KV）", 一、部署): K as int8 with one fp16 scale per token
@@ -57,8 +57,8 @@ __device__ __attribute__((always_inline)) inline RowVals<D> load_row(const float
 }
 
 // Quantize one token's K and V rows (already in the wave's registers) into slot s of the
-// (page, KV head) block at blk.  Called by all 64 lanes of a wave.
-template <int D>
+// (page, KV head) block at blk, with VB-bit V codes.  Called by all 64 lanes of a wave.
+template <int D, int VB = 4>
 __device__ __attribute__((always_inline)) inline void store_row(uint8_t* blk, int P, int s, const RowVals<D>& r, int lane) {
   constexpr int E = RowVals<D>::E;
   const int tile = s / kTile, t = s % kTile;
@@ -87,18 +87,32 @@ __device__ __attribute__((always_inline)) inline void store_row(uint8_t* blk, in
   }
   if (lane == 0) *(uint16_t*)(blk + k_scales_at(P, D) + 2 * s) = ks_bits;
 
-  // ---- V: one scale per 32 dims (qmax 7), 32/E lanes per group ----
+  // ---- V: one scale per 32 dims (qmax 7, or 127 for 8-bit codes), 32/E lanes per group ----
+  constexpr float vqmax = VB == 8 ? 127.0f : 7.0f;
   float va = 0.0f;
 #pragma unroll
   for (int e = 0; e < E; ++e) va = fmaxf(va, fabsf(vx[e]));
   va = wave_max(va, 32 / E);
   float vsc;
-  const uint16_t vs_bits = group_scale(va, 7.0f, &vsc);
+  const uint16_t vs_bits = group_scale(va, vqmax, &vsc);
+  const int j = d0 / 32;
+  if (d0 % 32 == 0) *(uint16_t*)(blk + v_scales_at(P, D, VB) + 2 * ((size_t)s * (D / 32) + j)) = vs_bits;
+  if constexpr (VB == 8) {
+    // V8 code (t, d) at 16*D*tile + 512*w*(j/w) + 8*w*lane + 8*(j%w) + 4*((d/16)%2) + t%4 within
+    // the V section, lane = 16*(t/4) + d%16, w = min(D/32, 2): one byte per code
+    constexpr int w = (D / 32) < 2 ? (D / 32) : 2;
+    uint8_t* vbase = blk + v_codes_at(P, D) + (size_t)16 * D * tile + 512 * w * (j / w) + 8 * (j % w) +
+                     4 * ((d0 / 16) & 1) + t % 4;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int vlane = 16 * (t / 4) + (d0 + e) % 16;
+      vbase[8 * w * vlane] = (uint8_t)(quantize_one(vx[e], vsc, vqmax) & 0xFF);
+    }
+    return;
+  }
   uint32_t vnib = 0;  // E nibbles, dim d0+e at bits 4e
 #pragma unroll
   for (int e = 0; e < E; ++e) vnib |= (uint32_t)(quantize_one(vx[e], vsc, 7.0f) & 0xF) << (4 * e);
-  const int j = d0 / 32;
-  if (d0 % 32 == 0) *(uint16_t*)(blk + v_scales_at(P, D) + 2 * ((size_t)s * (D / 32) + j)) = vs_bits;
 
   // Dims d (d/16 even) and d+16 share a byte (low / high nibble).  The lane holding d gets the
   // partner's nibbles from 16/E lanes up and writes the E bytes.
@@ -118,10 +132,10 @@ __device__ __attribute__((always_inline)) inline void store_row(uint8_t* blk, in
 }
 
 // Load and quantize one token's rows (krow/vrow point at the rows' first values) into slot s.
-template <int D>
+template <int D, int VB = 4>
 __device__ inline void append_row(uint8_t* blk, int P, int s, const float* krow_base,
                                   const float* vrow_base, int lane) {
-  store_row<D>(blk, P, s, load_row<D>(krow_base, vrow_base, lane), lane);
+  store_row<D, VB>(blk, P, s, load_row<D>(krow_base, vrow_base, lane), lane);
 }
 
 }  // namespace kvq

@@ -21,6 +21,9 @@ KVQ_ERR_UNSUPPORTED = -2
 KVQ_ERR_WORKSPACE = -3
 KVQ_ERR_HIP = -4
 KVQ_MAX_STEP_TOKENS = 64
+KVQ_FORMAT_K8V4 = 0  # 4-bit V codes
+KVQ_FORMAT_K8V8 = 1  # 8-bit V codes
+FORMATS = {"k8v4": KVQ_FORMAT_K8V4, "k8v8": KVQ_FORMAT_K8V8}
 
 _lock = threading.Lock()
 _lib = None
@@ -61,6 +64,14 @@ def lib():
         L.kvq_decode_step.argtypes = [P, I, I, I, I, P, P, I, P, P, P, I, I, I, I, I,
                                       ctypes.c_float, I, P, P, P, ctypes.c_size_t, P]
         L.kvq_decode_step.restype = ctypes.c_int
+        L.kvq_block_bytes_fmt.argtypes = [I, I, I]
+        L.kvq_block_bytes_fmt.restype = ctypes.c_size_t
+        L.kvq_append_fmt.argtypes = [I] + L.kvq_append.argtypes
+        L.kvq_append_fmt.restype = ctypes.c_int
+        L.kvq_decode_attn_fmt.argtypes = [I] + L.kvq_decode_attn.argtypes
+        L.kvq_decode_attn_fmt.restype = ctypes.c_int
+        L.kvq_decode_step_fmt.argtypes = [I] + L.kvq_decode_step.argtypes
+        L.kvq_decode_step_fmt.restype = ctypes.c_int
         _lib = L
         return L
 
@@ -69,12 +80,13 @@ def strerror(code: int) -> str:
     return lib().kvq_strerror(int(code)).decode()
 
 
-def block_bytes(page_size: int, head_dim: int) -> int:
-    return int(lib().kvq_block_bytes(page_size, head_dim))
+def block_bytes(page_size: int, head_dim: int, kv_format: int = KVQ_FORMAT_K8V4) -> int:
+    return int(lib().kvq_block_bytes_fmt(kv_format, page_size, head_dim))
 
 
-def pool_bytes(num_pages: int, page_size: int, num_kv_heads: int, head_dim: int) -> int:
-    return num_pages * num_kv_heads * block_bytes(page_size, head_dim)
+def pool_bytes(num_pages: int, page_size: int, num_kv_heads: int, head_dim: int,
+               kv_format: int = KVQ_FORMAT_K8V4) -> int:
+    return num_pages * num_kv_heads * block_bytes(page_size, head_dim, kv_format)
 
 
 def decode_num_splits(n_seq: int, num_kv_heads: int, max_seq_len: int,
@@ -109,21 +121,22 @@ def _dev(t: torch.Tensor, name: str, dtype: torch.dtype | None = None) -> int:
 
 @dataclass
 class PagedCache:
-    """A caller-owned pool tensor (uint8, on the GPU) and its geometry."""
+    """A caller-owned pool tensor (uint8, on the GPU), its geometry and its KV format."""
     pool: torch.Tensor
     num_pages: int
     page_size: int
     num_kv_heads: int
     head_dim: int
+    kv_format: int = KVQ_FORMAT_K8V4
 
     @staticmethod
     def allocate(num_pages: int, page_size: int, num_kv_heads: int, head_dim: int,
-                 device="cuda") -> "PagedCache":
-        n = pool_bytes(num_pages, page_size, num_kv_heads, head_dim)
+                 device="cuda", kv_format: int = KVQ_FORMAT_K8V4) -> "PagedCache":
+        n = pool_bytes(num_pages, page_size, num_kv_heads, head_dim, kv_format)
         if n == 0:
             raise KVQError(KVQ_ERR_UNSUPPORTED, "PagedCache.allocate")
         pool = torch.zeros(n, dtype=torch.uint8, device=device)
-        return PagedCache(pool, num_pages, page_size, num_kv_heads, head_dim)
+        return PagedCache(pool, num_pages, page_size, num_kv_heads, head_dim, kv_format)
 
     def append(self, k, v, slot_mapping, stream=None) -> None:
         append(self, k, v, slot_mapping, stream=stream)
@@ -139,8 +152,8 @@ def append(cache: PagedCache, k: torch.Tensor, v: torch.Tensor, slot_mapping: to
     shape = (n_tok, cache.num_kv_heads, cache.head_dim)
     if tuple(k.shape) != shape or tuple(v.shape) != shape:
         raise ValueError(f"k and v must be {shape}")
-    rc = lib().kvq_append(
-        _dev(cache.pool, "pool", torch.uint8), cache.num_pages, cache.page_size,
+    rc = lib().kvq_append_fmt(
+        cache.kv_format, _dev(cache.pool, "pool", torch.uint8), cache.num_pages, cache.page_size,
         cache.num_kv_heads, cache.head_dim, _dev(k, "k", torch.float32),
         _dev(v, "v", torch.float32), _dev(slot_mapping, "slot_mapping", torch.int32), n_tok,
         _stream_ptr(stream))
@@ -171,8 +184,8 @@ def decode_attn(cache: PagedCache, q: torch.Tensor, page_table: torch.Tensor,
                                   num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    rc = lib().kvq_decode_attn(
-        _dev(cache.pool, "pool", torch.uint8), cache.num_pages, cache.page_size,
+    rc = lib().kvq_decode_attn_fmt(
+        cache.kv_format, _dev(cache.pool, "pool", torch.uint8), cache.num_pages, cache.page_size,
         cache.num_kv_heads, D, _dev(q, "q", torch.float16),
         _dev(page_table, "page_table", torch.int32), _dev(seq_lens, "seq_lens", torch.int32),
         n_seq, n_rows, n_q_heads, int(page_table.shape[1]), int(max_seq_len),
@@ -197,7 +210,7 @@ def _step_args(cache, k_new, v_new, q, page_table, seq_lens, max_seq_len, out, l
         if tuple(k_new.shape) != shape or tuple(v_new.shape) != shape:
             raise ValueError(f"k_new and v_new must be {shape}")
         kp, vp = _dev(k_new, "k_new", torch.float32), _dev(v_new, "v_new", torch.float32)
-    return (_dev(cache.pool, "pool", torch.uint8), cache.num_pages, cache.page_size,
+    return (cache.kv_format, _dev(cache.pool, "pool", torch.uint8), cache.num_pages, cache.page_size,
             cache.num_kv_heads, D, kp, vp, n_new, _dev(q, "q", torch.float16),
             _dev(page_table, "page_table", torch.int32), _dev(seq_lens, "seq_lens", torch.int32),
             n_seq, n_rows, n_q_heads, int(page_table.shape[1]), int(max_seq_len),
@@ -225,7 +238,7 @@ def decode_step(cache: PagedCache, k_new: torch.Tensor | None, v_new: torch.Tens
         need = decode_workspace_bytes(n_seq, n_rows, n_q_heads, cache.num_kv_heads, D,
                                       max_seq_len, num_splits)
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    rc = lib().kvq_decode_step(*_step_args(cache, k_new, v_new, q, page_table, seq_lens,
+    rc = lib().kvq_decode_step_fmt(*_step_args(cache, k_new, v_new, q, page_table, seq_lens,
                                            max_seq_len, out, lse, workspace, softmax_scale,
                                            num_splits, stream))
     if rc != KVQ_OK:
@@ -241,7 +254,7 @@ def prepare_decode_step(cache: PagedCache, k_new: torch.Tensor | None, v_new: to
     """Marshal the arguments of one kvq_decode_step once; the returned callable re-issues it."""
     args = _step_args(cache, k_new, v_new, q, page_table, seq_lens, max_seq_len, out, lse,
                       workspace, softmax_scale, num_splits, stream)
-    fn = lib().kvq_decode_step
+    fn = lib().kvq_decode_step_fmt
 
     def call():
         rc = fn(*args)
@@ -258,11 +271,11 @@ def prepare_append(cache: PagedCache, k: torch.Tensor, v: torch.Tensor,
     shape = (n_tok, cache.num_kv_heads, cache.head_dim)
     if tuple(k.shape) != shape or tuple(v.shape) != shape:
         raise ValueError(f"k and v must be {shape}")
-    args = (_dev(cache.pool, "pool", torch.uint8), cache.num_pages, cache.page_size,
-            cache.num_kv_heads, cache.head_dim, _dev(k, "k", torch.float32),
+    args = (cache.kv_format, _dev(cache.pool, "pool", torch.uint8), cache.num_pages,
+            cache.page_size, cache.num_kv_heads, cache.head_dim, _dev(k, "k", torch.float32),
             _dev(v, "v", torch.float32), _dev(slot_mapping, "slot_mapping", torch.int32), n_tok,
             _stream_ptr(stream))
-    fn = lib().kvq_append
+    fn = lib().kvq_append_fmt
 
     def call():
         rc = fn(*args)
@@ -279,14 +292,14 @@ def prepare_decode_attn(cache: PagedCache, q: torch.Tensor, page_table: torch.Te
     n_seq, n_rows, n_q_heads, D = (int(x) for x in q.shape)
     if D != cache.head_dim or tuple(out.shape) != (n_seq, n_rows, n_q_heads, D):
         raise ValueError("q / out shapes do not match the cache")
-    args = (_dev(cache.pool, "pool", torch.uint8), cache.num_pages, cache.page_size,
-            cache.num_kv_heads, D, _dev(q, "q", torch.float16),
+    args = (cache.kv_format, _dev(cache.pool, "pool", torch.uint8), cache.num_pages,
+            cache.page_size, cache.num_kv_heads, D, _dev(q, "q", torch.float16),
             _dev(page_table, "page_table", torch.int32), _dev(seq_lens, "seq_lens", torch.int32),
             n_seq, n_rows, n_q_heads, int(page_table.shape[1]), int(max_seq_len),
             float(softmax_scale), int(num_splits), _dev(out, "out", torch.float32),
             _dev(lse, "lse", torch.float32) if lse is not None else None,
             _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream_ptr(stream))
-    fn = lib().kvq_decode_attn
+    fn = lib().kvq_decode_attn_fmt
 
     def call():
         rc = fn(*args)

@@ -33,9 +33,14 @@ def to_dev(a: np.ndarray):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def gpu_cache(inp: W.Inputs):
+# KV formats: the library's format code and the oracle's bits per V code
+VBITS = {0: 4, 1: 8}
+
+
+def gpu_cache(inp: W.Inputs, kv_format=0):
     wl = inp.wl
-    return kvq().PagedCache.allocate(wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim)
+    return kvq().PagedCache.allocate(wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
+                                     kv_format=kv_format)
 
 
 def gpu_append(cache, k, v, slots):
@@ -44,9 +49,9 @@ def gpu_append(cache, k, v, slots):
     torch.cuda.synchronize()
 
 
-def gpu_fill(inp: W.Inputs, cache=None, split_step=True):
+def gpu_fill(inp: W.Inputs, cache=None, split_step=True, kv_format=0):
     """Fill a pool on the GPU: the cached context, then the step's appended tokens."""
-    cache = cache or gpu_cache(inp)
+    cache = cache or gpu_cache(inp, kv_format)
     if split_step and inp.wl.n_new and np.all(inp.seq_lens == inp.wl.seq_len):
         gpu_append(cache, *inp.prefill())
         gpu_append(cache, *inp.step_tokens())
@@ -69,25 +74,27 @@ def gpu_decode(inp: W.Inputs, cache, num_splits=0, max_seq_len=None, page_table=
     return out.cpu().numpy(), lse.cpu().numpy()
 
 
-def oracle_fill(inp: W.Inputs):
+def oracle_fill(inp: W.Inputs, kv_format=0):
     wl = inp.wl
-    pool = oracle.new_pool(wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim)
+    vb = VBITS[kv_format]
+    pool = oracle.new_pool(wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim, vb)
     if wl.n_new and np.all(inp.seq_lens == wl.seq_len):
         oracle.append(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
-                      *inp.prefill())
+                      *inp.prefill(), vbits=vb)
         oracle.append(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
-                      *inp.step_tokens())
+                      *inp.step_tokens(), vbits=vb)
     else:
         oracle.append(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
-                      *inp.all_tokens())
+                      *inp.all_tokens(), vbits=vb)
     return pool
 
 
-def oracle_decode(inp: W.Inputs, pool, select=None, softmax_scale=0.0):
+def oracle_decode(inp: W.Inputs, pool, select=None, softmax_scale=0.0, kv_format=0):
     wl = inp.wl
     return oracle.decode_attn(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
                               inp.q_bits, inp.page_table, inp.seq_lens, wl.n_rows,
-                              wl.n_q_heads, softmax_scale=softmax_scale, select=select)
+                              wl.n_q_heads, softmax_scale=softmax_scale, select=select,
+                              vbits=VBITS[kv_format])
 
 
 @functools.lru_cache(maxsize=2)

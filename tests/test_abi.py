@@ -110,6 +110,26 @@ def test_append_validation(lib):
     assert append_rc(lib, n_tok=0) == kvq.KVQ_OK  # nothing to do, nothing enqueued
 
 
+def test_kv_formats(lib):
+    """K8/V4 and K8/V8 block sizes; an unknown format is refused before any HIP call."""
+    assert lib.kvq_block_bytes_fmt(kvq.KVQ_FORMAT_K8V4, 64, 256) == 64 * (256 + 2 + 128 + 16)
+    assert lib.kvq_block_bytes_fmt(kvq.KVQ_FORMAT_K8V8, 64, 256) == 64 * (2 * 256 + 2 + 16)
+    assert lib.kvq_block_bytes_fmt(kvq.KVQ_FORMAT_K8V8, 16, 64) == 16 * (2 * 64 + 2 + 4)
+    assert lib.kvq_block_bytes(64, 256) == lib.kvq_block_bytes_fmt(kvq.KVQ_FORMAT_K8V4, 64, 256)
+    assert lib.kvq_block_bytes_fmt(2, 64, 256) == 0
+    assert lib.kvq_block_bytes_fmt(-1, 64, 256) == 0
+    assert lib.kvq_append_fmt(2, FAKE, 4, 16, 1, 64, FAKE, FAKE, FAKE, 1, None) == \
+        kvq.KVQ_ERR_UNSUPPORTED
+    assert lib.kvq_append_fmt(kvq.KVQ_FORMAT_K8V8, FAKE, 4, 16, 1, 64, FAKE, FAKE, FAKE, 0,
+                              None) == kvq.KVQ_OK
+    assert lib.kvq_decode_attn_fmt(7, FAKE, 8, 16, 2, 64, FAKE, FAKE, FAKE, 1, 1, 4, 8, 100,
+                                   0.0, 0, FAKE, None, FAKE, 1 << 30, None) == \
+        kvq.KVQ_ERR_UNSUPPORTED
+    assert lib.kvq_decode_step_fmt(7, FAKE, 8, 16, 2, 64, None, None, 0, FAKE, FAKE, FAKE, 1, 1,
+                                   4, 8, 100, 0.0, 0, FAKE, None, FAKE, 1 << 30, None) == \
+        kvq.KVQ_ERR_UNSUPPORTED
+
+
 def decode_rc(lib, **kw):
     a = dict(pool=FAKE, num_pages=8, page_size=16, hkv=2, d=64, q=FAKE, pt=FAKE, sl=FAKE,
              n_seq=1, n_rows=1, hq=4, max_pages=8, max_seq_len=100, scale=0.0, splits=0,

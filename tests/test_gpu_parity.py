@@ -57,11 +57,13 @@ def test_append_edge_rows_bit_exact():
         assert np.array_equal(got, inp_pool), (P, D, Hkv, np.flatnonzero(got != inp_pool)[:8])
 
 
-def test_append_tile_and_row_paths_bit_exact():
+@pytest.mark.parametrize("kv_format", [0, 1], ids=["k8v4", "k8v8"])
+def test_append_tile_and_row_paths_bit_exact(kv_format):
     """Groups of 16 tokens that fill one tile in order are written as whole tiles; any other
     group token by token.  One call mixes both: whole tiles, a run starting mid-tile, a tile with
     two slots swapped, a tile with a padding slot, and a short last group."""
-    H.say("[append tile / row paths]")
+    H.say(f"[append tile / row paths] format {kv_format}")
+    vb = H.VBITS[kv_format]
     rng = np.random.default_rng(78)
     for P, D, Hkv in ((64, 256, 2), (16, 64, 1), (32, 128, 3)):
         # segments in disjoint 64-slot regions (no slot written twice, whatever the page size);
@@ -83,9 +85,9 @@ def test_append_tile_and_row_paths_bit_exact():
         v = rng.standard_normal((n, Hkv, D)).astype(np.float32)
         k[2] = 0.0
         v[50] *= np.float32(1e-6)
-        ref = H.oracle.new_pool(pages, P, Hkv, D)
-        H.oracle.append(ref, pages, P, Hkv, D, k, v, slots)
-        cache = H.kvq().PagedCache.allocate(pages, P, Hkv, D)
+        ref = H.oracle.new_pool(pages, P, Hkv, D, vb)
+        H.oracle.append(ref, pages, P, Hkv, D, k, v, slots, vbits=vb)
+        cache = H.kvq().PagedCache.allocate(pages, P, Hkv, D, kv_format=kv_format)
         H.gpu_append(cache, k, v, slots)
         got = cache.pool.cpu().numpy()
         assert np.array_equal(got, ref), (P, D, Hkv, np.flatnonzero(got != ref)[:8])
@@ -227,6 +229,72 @@ def test_decode_batch_equals_each_sequence_alone():
         one.seq_lens = inp.seq_lens[b:b + 1].copy()
         o1, l1 = H.gpu_decode(one, cache, num_splits=6, max_seq_len=700)
         assert np.array_equal(o1[0], out[b]) and np.array_equal(l1[0], lse[b])
+
+
+# ------------------------------------------------------------------ K8/V8 ---------------
+# 8-bit V codes (KVQ_FORMAT_K8V8): the same bar, pool bytes bit-exact and outputs within 2e-3.
+
+V8_SMALL = SMALL + [W.custom(n_seq=2, seq_lens=(700, 333), num_kv_heads=2, n_q_heads=12,
+                             head_dim=128, page_size=32, n_rows=2, seed=61, name="d128").wl]
+
+
+@pytest.mark.parametrize("wl", V8_SMALL, ids=lambda w: w.name)
+def test_v8_decode_small_every_output(wl):
+    H.say(f"[k8v8 small] {wl.name} L={wl.seq_len}")
+    inp = W.generate(wl)
+    cache = H.gpu_fill(inp, kv_format=1)
+    pool_ref = H.oracle_fill(inp, 1)
+    assert np.array_equal(cache.pool.cpu().numpy(), pool_ref)
+    for splits in (0, 3):
+        out, lse = H.gpu_decode(inp, cache, num_splits=splits)
+        out_r, lse_r = H.oracle_decode(inp, pool_ref, kv_format=1)
+        assert H.report(f"  out (splits {splits})", out, out_r) <= H.TOL_ABS
+        np.testing.assert_allclose(lse, lse_r, rtol=0, atol=1e-4)
+
+
+def test_v8_step_equals_append_then_decode():
+    """kvq_decode_step in K8/V8: the same pool bytes and outputs as kvq_append followed by
+    kvq_decode_attn, and the oracle's."""
+    import torch
+    H.say("[k8v8 step]")
+    kvq = H.kvq()
+    inp = W.custom(n_seq=1, seq_lens=(1154,), num_kv_heads=4, n_q_heads=24, head_dim=256,
+                   page_size=64, n_rows=4, seed=62)
+    wl = inp.wl
+    n_new = 4
+    pre, new_flat, k_new, v_new = inp.ragged_split(n_new)
+    a = H.gpu_cache(inp, 1)
+    H.gpu_append(a, *pre)
+    H.gpu_append(a, *new_flat)
+    out_a, lse_a = H.gpu_decode(inp, a, num_splits=7)
+    b = H.gpu_cache(inp, 1)
+    H.gpu_append(b, *pre)
+    q = H.to_dev(inp.q_bits).view(torch.float16)
+    out_b, lse_b = kvq.decode_step(b, H.to_dev(k_new), H.to_dev(v_new), q, H.to_dev(inp.page_table),
+                                   H.to_dev(inp.seq_lens), wl.seq_len, num_splits=7)
+    torch.cuda.synchronize()
+    assert np.array_equal(a.pool.cpu().numpy(), b.pool.cpu().numpy())
+    assert np.array_equal(out_a, out_b.cpu().numpy()) and np.array_equal(lse_a, lse_b.cpu().numpy())
+    out_r, _ = H.oracle_decode(inp, H.oracle_fill(inp, 1), kv_format=1)
+    assert H.report("  out", out_a, out_r) <= H.TOL_ABS
+
+
+def test_v8_full_size_headline():
+    """The 184K-token two-sequence workload in K8/V8 with the automatic plan: the whole pool
+    bit-exact, sampled rows against the oracle."""
+    H.say("[k8v8 full] ctx184k_c2")
+    inp = W.generate(W.WORKLOADS["ctx184k_c2"])
+    wl = inp.wl
+    pool_ref = H.oracle_fill(inp, 1)
+    cache = H.gpu_fill(inp, kv_format=1)
+    got = cache.pool.cpu().numpy()
+    assert np.array_equal(got, pool_ref), np.flatnonzero(got != pool_ref)[:8]
+    out, lse = H.gpu_decode(inp, cache)
+    sel = [(0, 0, 0), (1, 0, 23), (0, 0, 11), (1, 0, 6)]
+    out_r, lse_r = H.oracle_decode(inp, pool_ref, select=sel, kv_format=1)
+    got = np.stack([out[b, i, hq] for b, i, hq in sel])
+    assert H.report("  out", got, out_r) <= H.TOL_ABS
+    np.testing.assert_allclose(np.array([lse[b, i, hq] for b, i, hq in sel]), lse_r, rtol=0, atol=1e-4)
 
 
 # ------------------------------------------------------------------ decode, full size ----
