@@ -135,6 +135,33 @@ class Inputs:
         return (np.ascontiguousarray(np.concatenate(ks)), np.ascontiguousarray(np.concatenate(vs)),
                 np.concatenate(ss))
 
+    def ring(self, ring_pages: int, extra_cols: int = 2):
+        """The same tokens on ring pages: sequence s owns pool pages [s * ring_pages, (s + 1) *
+        ring_pages) in a seeded order, and logical page n of it sits in table entry
+        n % ring_pages.  Returns (table [n_seq][ring_pages + extra_cols] int32, (k, v, slots) of
+        the tokens a ring that size still holds: each sequence's last ring_pages logical pages,
+        below its length, flattened as token_range does).  The extra columns name pages of
+        another sequence, so a lookup that ignores the ring reads the wrong tokens."""
+        wl = self.wl
+        P = wl.page_size
+        assert wl.n_seq * ring_pages <= wl.pool_pages
+        rng = np.random.default_rng(wl.seed + 77)
+        table = np.zeros((wl.n_seq, ring_pages + extra_cols), np.int32)
+        for s in range(wl.n_seq):
+            table[s, :ring_pages] = s * ring_pages + rng.permutation(ring_pages)
+            other = (s + 1) % wl.n_seq
+            table[s, ring_pages:] = other * ring_pages + (np.arange(extra_cols) % ring_pages)
+        ks, vs, ss = [], [], []
+        for s in range(wl.n_seq):
+            n = int(self.seq_lens[s])
+            t0 = max(0, (n - 1) // P - ring_pages + 1) * P
+            t = np.arange(t0, n, dtype=np.int64)
+            ks.append(self.k[s, t0:n])
+            vs.append(self.v[s, t0:n])
+            ss.append((table[s, (t // P) % ring_pages].astype(np.int64) * P + t % P).astype(np.int32))
+        return table, (np.ascontiguousarray(np.concatenate(ks)),
+                       np.ascontiguousarray(np.concatenate(vs)), np.concatenate(ss))
+
     def ragged_split(self, n_new: int):
         """For ragged lengths: the tokens cached before a step that appends each sequence's last
         n_new tokens, as (k, v, slots) flattened like token_range; and those new tokens, both as

@@ -51,12 +51,12 @@ def _declare(lib):
     lib.kvq_oracle_append_fmt.restype = None
     lib.kvq_oracle_read_slot_fmt.argtypes = [P, I, I, I, I, I, I, I, P, P, P, P]
     lib.kvq_oracle_read_slot_fmt.restype = None
-    lib.kvq_oracle_decode_attn_fmt.argtypes = [P, I, I, I, I, I, P, P, P, I, I, I, I,
+    lib.kvq_oracle_decode_attn_win.argtypes = [P, I, I, I, I, I, I, I, P, P, P, I, I, I, I,
                                                ctypes.c_double, P, I, P, P]
-    lib.kvq_oracle_decode_attn_fmt.restype = None
-    lib.kvq_oracle_attn_weights_fmt.argtypes = [P, I, I, I, I, I, P, P, P, I, I, I,
+    lib.kvq_oracle_decode_attn_win.restype = None
+    lib.kvq_oracle_attn_weights_win.argtypes = [P, I, I, I, I, I, I, I, P, P, P, I, I, I,
                                                 ctypes.c_double, I, I, I, P]
-    lib.kvq_oracle_attn_weights_fmt.restype = I
+    lib.kvq_oracle_attn_weights_win.restype = I
     lib.kvq_oracle_num_threads.argtypes = []
     lib.kvq_oracle_num_threads.restype = I
     return lib
@@ -142,11 +142,14 @@ class Oracle:
 
     def decode_attn(self, pool: np.ndarray, num_pages: int, page_size: int, num_kv_heads: int,
                     head_dim: int, q_bits, page_table, seq_lens, n_rows: int, n_q_heads: int,
-                    softmax_scale: float = 0.0, select=None, vbits: int = 4):
+                    softmax_scale: float = 0.0, select=None, vbits: int = 4, window: int = 0,
+                    ring_pages: int = 0):
         """fp64 attention. ``q_bits``: uint16 fp16 bits [n_seq][n_rows][Hq][D].
 
         Returns (out, lse): with ``select`` None, out is [n_seq][n_rows][Hq][D] and lse
         [n_seq][n_rows][Hq]; with ``select`` a list of (b, i, hq), out is [len][D], lse [len].
+        ``window`` > 0: row i sees only the last ``window`` tokens up to its own position;
+        ``ring_pages`` > 0: logical page n lives in page-table entry n mod ``ring_pages``.
         """
         q = _c(q_bits, np.uint16)
         pt = _c(page_table, np.int32)
@@ -163,11 +166,12 @@ class Oracle:
             count = sel.shape[0]
         out = np.zeros((count, head_dim), np.float64)
         lse = np.zeros(count, np.float64)
-        self.lib.kvq_oracle_decode_attn_fmt(_ptr(pool), num_pages, page_size, num_kv_heads,
-                                            head_dim, vbits, _ptr(q), _ptr(pt), _ptr(sl), n_seq, n_rows,
-                                        n_q_heads, max_pages, float(softmax_scale),
-                                        None if sel is None else _ptr(sel), count, _ptr(out),
-                                        _ptr(lse))
+        self.lib.kvq_oracle_decode_attn_win(_ptr(pool), num_pages, page_size, num_kv_heads,
+                                            head_dim, vbits, window, ring_pages, _ptr(q), _ptr(pt),
+                                            _ptr(sl), n_seq, n_rows, n_q_heads, max_pages,
+                                            float(softmax_scale),
+                                            None if sel is None else _ptr(sel), count, _ptr(out),
+                                            _ptr(lse))
         if select is None:
             return (out.reshape(n_seq, n_rows, n_q_heads, head_dim),
                     lse.reshape(n_seq, n_rows, n_q_heads))
@@ -176,17 +180,18 @@ class Oracle:
     def attn_weights(self, pool: np.ndarray, num_pages: int, page_size: int,
                      num_kv_heads: int, head_dim: int, q_bits, page_table, seq_lens,
                      n_rows: int, n_q_heads: int, b: int, i: int, hq: int,
-                     softmax_scale: float = 0.0, vbits: int = 4):
+                     softmax_scale: float = 0.0, vbits: int = 4, window: int = 0,
+                     ring_pages: int = 0):
         """Softmax weights over the L tokens of sequence b for query row i, head hq."""
         q = _c(q_bits, np.uint16)
         pt = _c(page_table, np.int32)
         sl = _c(seq_lens, np.int32)
         max_pages = pt.size // sl.size
         w = np.zeros(max(int(sl[b]), 1), np.float64)
-        n = self.lib.kvq_oracle_attn_weights_fmt(_ptr(pool), num_pages, page_size, num_kv_heads,
-                                                 head_dim, vbits, _ptr(q), _ptr(pt), _ptr(sl), n_rows,
-                                             n_q_heads, max_pages, float(softmax_scale), b, i,
-                                             hq, _ptr(w))
+        n = self.lib.kvq_oracle_attn_weights_win(_ptr(pool), num_pages, page_size, num_kv_heads,
+                                                 head_dim, vbits, window, ring_pages, _ptr(q),
+                                                 _ptr(pt), _ptr(sl), n_rows, n_q_heads, max_pages,
+                                                 float(softmax_scale), b, i, hq, _ptr(w))
         return w, n
 
 

@@ -18,7 +18,11 @@
  *     blog page "標籤: vLLM", section 重點說明 part 2 on segmented KV);
  *   - exact attention in fp64 over the dequantized entries, token by token in logical order
  *     through the page table, with the causal mask of an MTP verify step (same forum post,
- *     --spec mtp --draft-tokens 3).
+ *     --spec mtp --draft-tokens 3);
+ *   - optionally a sliding window over ring pages (blog page "標籤: vLLM", section 重點說明
+ *     part 2, which names the ring-buffer / sliding-window approach without details): row i
+ *     sees only the last `window` tokens up to its own position, and logical page n of a
+ *     sequence lives in page-table entry n mod ring_pages.
  *
  * Build: gcc -O2 -std=c11 -fopenmp -ffp-contract=off -shared -fPIC (no fast-math: the quantizer
  * relies on IEEE fp32 division and round-half-to-even).
@@ -236,11 +240,12 @@ void kvq_oracle_read_slot(const uint8_t* pool, int P, int Hkv, int D, int page, 
 /* ---------------------------------------------------------------- attention -------------- */
 
 /* Dequantized K and V of logical token t of sequence b, head h (page-table entries clamped
- * into [0, num_pages) as the library header specifies). */
-static void token_kv(const uint8_t* pool, int num_pages, int P, int Hkv, int D, int vb,
+ * into [0, num_pages) as the library header specifies).  ring > 0: logical page t / P sits in
+ * entry (t / P) mod ring of the sequence's page-table row; ring = 0: in entry t / P. */
+static void token_kv(const uint8_t* pool, int num_pages, int P, int Hkv, int D, int vb, int ring,
                      const int32_t* pt_row, int t, int h, double* kd, double* vd, int8_t* kc,
                      int8_t* vc, uint16_t* vs) {
-  int page = pt_row[t / P];
+  int page = pt_row[ring > 0 ? (t / P) % ring : t / P];
   if (page < 0) page = 0;
   if (page >= num_pages) page = num_pages - 1;
   uint16_t ks;
@@ -250,19 +255,29 @@ static void token_kv(const uint8_t* pool, int num_pages, int P, int Hkv, int D, 
   for (int d = 0; d < D; ++d) vd[d] = (double)vc[d] * kvq_oracle_fp16_to_double(vs[d / 32]);
 }
 
+/* First and last token row i of a sequence of L tokens sees: the causal mask of an MTP verify
+ * step ends row i at L - R + i; a window of W > 0 tokens starts it W - 1 tokens earlier (never
+ * before token 0). */
+static void row_range(int L, int R, int i, int window, int* first, int* last) {
+  *last = L - R + i;
+  *first = window > 0 ? *last - window + 1 : 0;
+  if (*first < 0) *first = 0;
+}
+
 /* Softmax weights of one output row (sequence b, query row i, query head hq): w[t] for
  * t < L (0 where masked).  Returns the number of attended tokens; *m_out and *sum_out get the
  * max logit and sum of exp(z - max) for the log-sum-exp. */
 static int row_weights(const uint8_t* pool, int num_pages, int P, int Hkv, int D, int vb,
-                       const uint16_t* q, const int32_t* page_table, const int32_t* seq_lens,
-                       int R, int Hq, int max_pages, double scale, int b, int i, int hq,
-                       double* w, double* m_out, double* sum_out) {
+                       int window, int ring, const uint16_t* q, const int32_t* page_table,
+                       const int32_t* seq_lens, int R, int Hq, int max_pages, double scale, int b,
+                       int i, int hq, double* w, double* m_out, double* sum_out) {
   int G = Hq / Hkv;
   int h = hq / G;
   int L = seq_lens[b];
-  int last = L - R + i; /* causal mask: row i sees tokens 0 .. L - R + i */
-  int n = last + 1;
-  if (n <= 0) {
+  int first, last;
+  row_range(L, R, i, window, &first, &last);
+  int n = last - first + 1;
+  if (last < 0 || n <= 0) {
     *m_out = -INFINITY;
     *sum_out = 0.0;
     return 0;
@@ -277,19 +292,19 @@ static int row_weights(const uint8_t* pool, int num_pages, int P, int Hkv, int D
   for (int d = 0; d < D; ++d) qd[d] = kvq_oracle_fp16_to_double(qrow[d]);
   const int32_t* pt_row = page_table + (size_t)b * max_pages;
   double m = -INFINITY;
-  for (int t = 0; t < n; ++t) {
-    token_kv(pool, num_pages, P, Hkv, D, vb, pt_row, t, h, kd, vd, kc, vc, vs);
+  for (int t = first; t <= last; ++t) {
+    token_kv(pool, num_pages, P, Hkv, D, vb, ring, pt_row, t, h, kd, vd, kc, vc, vs);
     double dot = 0.0;
     for (int d = 0; d < D; ++d) dot += qd[d] * kd[d];
     w[t] = scale * dot; /* logit z_t, replaced by its weight below */
     if (w[t] > m) m = w[t];
   }
   double sum = 0.0;
-  for (int t = 0; t < n; ++t) {
+  for (int t = first; t <= last; ++t) {
     w[t] = exp(w[t] - m);
     sum += w[t];
   }
-  for (int t = 0; t < n; ++t) w[t] /= sum;
+  for (int t = first; t <= last; ++t) w[t] /= sum;
   *m_out = m;
   *sum_out = sum;
   free(qd); free(kd); free(vd); free(kc); free(vc); free(vs);
@@ -298,8 +313,8 @@ static int row_weights(const uint8_t* pool, int num_pages, int P, int Hkv, int D
 
 /* Attention outputs for a list of (b, i, hq) triples (sel, n_sel of them), or for every
  * output in [b][i][hq] order when sel is NULL.  out: [count][D] fp64, lse: [count] fp64. */
-void kvq_oracle_decode_attn_fmt(const uint8_t* pool, int num_pages, int P, int Hkv, int D, int vb,
-                                const uint16_t* q, const int32_t* page_table,
+void kvq_oracle_decode_attn_win(const uint8_t* pool, int num_pages, int P, int Hkv, int D, int vb,
+                                int window, int ring, const uint16_t* q, const int32_t* page_table,
                                 const int32_t* seq_lens, int n_seq, int R, int Hq, int max_pages,
                                 double scale, const int32_t* sel, int n_sel, double* out,
                                 double* lse) {
@@ -320,8 +335,8 @@ void kvq_oracle_decode_attn_fmt(const uint8_t* pool, int num_pages, int P, int H
     int L = seq_lens[b];
     double* w = (double*)malloc(sizeof(double) * (L > 0 ? (size_t)L : 1));
     double m, sum;
-    int n = row_weights(pool, num_pages, P, Hkv, D, vb, q, page_table, seq_lens, R, Hq, max_pages,
-                        scale, b, i, hq, w, &m, &sum);
+    int n = row_weights(pool, num_pages, P, Hkv, D, vb, window, ring, q, page_table, seq_lens, R,
+                        Hq, max_pages, scale, b, i, hq, w, &m, &sum);
     double* o_row = out + (size_t)o * D;
     for (int d = 0; d < D; ++d) o_row[d] = 0.0;
     if (n > 0) {
@@ -332,8 +347,10 @@ void kvq_oracle_decode_attn_fmt(const uint8_t* pool, int num_pages, int P, int H
       uint16_t* vs = (uint16_t*)malloc(sizeof(uint16_t) * (D / 32));
       const int32_t* pt_row = page_table + (size_t)b * max_pages;
       int h = hq / (Hq / Hkv);
-      for (int t = 0; t < n; ++t) {
-        token_kv(pool, num_pages, P, Hkv, D, vb, pt_row, t, h, kd, vd, kc, vc, vs);
+      int first, last;
+      row_range(L, R, i, window, &first, &last);
+      for (int t = first; t <= last; ++t) {
+        token_kv(pool, num_pages, P, Hkv, D, vb, ring, pt_row, t, h, kd, vd, kc, vc, vs);
         for (int d = 0; d < D; ++d) o_row[d] += w[t] * vd[d];
       }
       free(kd); free(vd); free(kc); free(vc); free(vs);
@@ -343,6 +360,15 @@ void kvq_oracle_decode_attn_fmt(const uint8_t* pool, int num_pages, int P, int H
     }
     free(w);
   }
+}
+
+void kvq_oracle_decode_attn_fmt(const uint8_t* pool, int num_pages, int P, int Hkv, int D, int vb,
+                                const uint16_t* q, const int32_t* page_table,
+                                const int32_t* seq_lens, int n_seq, int R, int Hq, int max_pages,
+                                double scale, const int32_t* sel, int n_sel, double* out,
+                                double* lse) {
+  kvq_oracle_decode_attn_win(pool, num_pages, P, Hkv, D, vb, 0, 0, q, page_table, seq_lens, n_seq,
+                             R, Hq, max_pages, scale, sel, n_sel, out, lse);
 }
 
 void kvq_oracle_decode_attn(const uint8_t* pool, int num_pages, int P, int Hkv, int D,
@@ -355,16 +381,23 @@ void kvq_oracle_decode_attn(const uint8_t* pool, int num_pages, int P, int Hkv, 
 }
 
 /* Softmax weights of one output row, w[0..L-1] (0 where masked). Returns attended count. */
-int kvq_oracle_attn_weights_fmt(const uint8_t* pool, int num_pages, int P, int Hkv, int D, int vb,
-                                const uint16_t* q, const int32_t* page_table,
-                                const int32_t* seq_lens, int R, int Hq, int max_pages, double scale,
-                                int b, int i, int hq, double* w) {
+int kvq_oracle_attn_weights_win(const uint8_t* pool, int num_pages, int P, int Hkv, int D, int vb,
+                                int window, int ring, const uint16_t* q,
+                                const int32_t* page_table, const int32_t* seq_lens, int R, int Hq,
+                                int max_pages, double scale, int b, int i, int hq, double* w) {
   if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
   int L = seq_lens[b];
   for (int t = 0; t < L; ++t) w[t] = 0.0;
   double m, sum;
-  return row_weights(pool, num_pages, P, Hkv, D, vb, q, page_table, seq_lens, R, Hq, max_pages,
-                     scale, b, i, hq, w, &m, &sum);
+  return row_weights(pool, num_pages, P, Hkv, D, vb, window, ring, q, page_table, seq_lens, R, Hq,
+                     max_pages, scale, b, i, hq, w, &m, &sum);
+}
+int kvq_oracle_attn_weights_fmt(const uint8_t* pool, int num_pages, int P, int Hkv, int D, int vb,
+                                const uint16_t* q, const int32_t* page_table,
+                                const int32_t* seq_lens, int R, int Hq, int max_pages, double scale,
+                                int b, int i, int hq, double* w) {
+  return kvq_oracle_attn_weights_win(pool, num_pages, P, Hkv, D, vb, 0, 0, q, page_table, seq_lens,
+                                     R, Hq, max_pages, scale, b, i, hq, w);
 }
 int kvq_oracle_attn_weights(const uint8_t* pool, int num_pages, int P, int Hkv, int D,
                             const uint16_t* q, const int32_t* page_table,

@@ -61,8 +61,10 @@ def quantize_token_np(krow, vrow, vqmax=7):
     return kc, ks, vc, vs
 
 
-def attention_brute(q_bits, kc, ks, vc, vs, seq_lens, n_rows, n_q_heads, num_kv_heads, scale):
-    """Pure-Python fp64 attention.
+def attention_brute(q_bits, kc, ks, vc, vs, seq_lens, n_rows, n_q_heads, num_kv_heads, scale,
+                    window=0):
+    """Pure-Python fp64 attention (``window`` > 0: each row sees only its last ``window``
+    tokens, its own position included).
 
     q_bits: [n_seq][n_rows][Hq][D] fp16 bits; kc/vc: [n_seq][L][Hkv][D] codes;
     ks: [n_seq][L][Hkv] scale bits; vs: [n_seq][L][Hkv][D/32] scale bits.
@@ -81,8 +83,9 @@ def attention_brute(q_bits, kc, ks, vc, vs, seq_lens, n_rows, n_q_heads, num_kv_
                 h = hq // G
                 q = [fp16_value_np(int(x)) for x in q_bits[b][i][hq]]
                 last = L - n_rows + i
+                first = max(0, last - window + 1) if window > 0 else 0
                 z = []
-                for t in range(last + 1):
+                for t in range(first, last + 1):
                     sk = fp16_value_np(int(ks[b][t][h]))
                     dot = 0.0
                     for d in range(D):
@@ -96,7 +99,7 @@ def attention_brute(q_bits, kc, ks, vc, vs, seq_lens, n_rows, n_q_heads, num_kv_
                 e = [math.exp(x - m) for x in z]
                 tot = sum(e)
                 o = [0.0] * D
-                for t, et in enumerate(e):
+                for t, et in zip(range(first, last + 1), e):
                     w = et / tot
                     for d in range(D):
                         sv = fp16_value_np(int(vs[b][t][h][d // 32]))

@@ -34,7 +34,7 @@ def _case(i):
 
 
 @functools.lru_cache(maxsize=None)
-def _brute_ref(i, vqmax=7):
+def _brute_ref(i, vqmax=7, window=0):
     inp = _case(i)
     wl = inp.wl
     n, L, H, D = wl.n_seq, wl.seq_len, wl.num_kv_heads, wl.head_dim
@@ -48,7 +48,7 @@ def _brute_ref(i, vqmax=7):
                 kc[b, t, h], ks[b, t, h], vc[b, t, h], vs[b, t, h] = brute.quantize_token_np(
                     inp.k[b, t, h], inp.v[b, t, h], vqmax)
     return brute.attention_brute(inp.q_bits, kc, ks, vc, vs, inp.seq_lens, wl.n_rows,
-                                 wl.n_q_heads, H, 1.0 / math.sqrt(D))
+                                 wl.n_q_heads, H, 1.0 / math.sqrt(D), window)
 
 
 def _golden_lines(name):
@@ -202,7 +202,45 @@ def check_large_logits(o):
     return abs(lse[0, 0, 0] - (max(z) + math.log1p(math.exp(-abs(gap))))) < 1e-9 * abs(max(z))
 
 
-CHECKS = [check_fp16, check_quantizer_golden, check_quantizer_argmin, check_format_golden,
+def check_window_ring(o):
+    """Sliding window over ring pages: the oracle, reading a ring table that holds only each
+    sequence's last ring_pages pages, against the pure-Python brute force of windowed
+    attention over the logical tokens (MTP rows, ragged lengths, GQA 3); and a one-token window,
+    whose output is the row's own V and whose log-sum-exp is its own logit."""
+    wl_i, window, ring = 1, 10, 2
+    inp = _case(wl_i)
+    wl = inp.wl
+    table, (k, v, slots) = inp.ring(ring)
+    pool = o.new_pool(wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim)
+    o.append(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim, k, v, slots)
+    out, lse = o.decode_attn(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
+                             inp.q_bits, table, inp.seq_lens, wl.n_rows, wl.n_q_heads,
+                             window=window, ring_pages=ring)
+    out_b, lse_b = _brute_ref(wl_i, 7, window)
+    if not (np.allclose(out, out_b, rtol=0, atol=1e-12) and
+            np.allclose(lse, lse_b, rtol=0, atol=1e-11)):
+        return False
+    # window 1: row i of sequence b sees token L - R + i alone
+    out, lse = o.decode_attn(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
+                             inp.q_bits, table, inp.seq_lens, wl.n_rows, wl.n_q_heads,
+                             window=1, ring_pages=ring)
+    G = wl.n_q_heads // wl.num_kv_heads
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    for b in range(wl.n_seq):
+        for i in range(wl.n_rows):
+            t = int(inp.seq_lens[b]) - wl.n_rows + i
+            for hq in range(wl.n_q_heads):
+                kc, ks, vc, vs = brute.quantize_token_np(inp.k[b, t, hq // G], inp.v[b, t, hq // G])
+                vd = vc.astype(float) * np.repeat([brute.fp16_value_np(x) for x in vs], 32)
+                q = inp.q_bits[b, i, hq].view(np.float16).astype(float)
+                z = scale * (q @ (kc.astype(float) * brute.fp16_value_np(ks)))
+                if not (np.allclose(out[b, i, hq], vd, rtol=0, atol=1e-13) and
+                        abs(lse[b, i, hq] - z) < 1e-12):
+                    return False
+    return True
+
+
+CHECKS = [check_window_ring, check_fp16, check_quantizer_golden, check_quantizer_argmin, check_format_golden,
           check_brute_force, check_closed_forms, check_large_logits, check_format_golden_v8,
           check_brute_force_v8]
 

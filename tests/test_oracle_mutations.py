@@ -22,7 +22,13 @@ MUTATIONS = {
     "v_nibble_unsigned": ("(int8_t)(nib >= 8 ? nib - 16 : nib)", "(int8_t)(nib)"),
     "k_scale_dropped": ("kd[d] = (double)kc[d] * sk;", "kd[d] = (double)kc[d];"),
     "v_scale_group": ("kvq_oracle_fp16_to_double(vs[d / 32])", "kvq_oracle_fp16_to_double(vs[d / 64])"),
-    "mask_off_by_one": ("int last = L - R + i;", "int last = L - R + i - 1;"),
+    "mask_off_by_one": ("*last = L - R + i;", "*last = L - R + i - 1;"),
+    # sliding window over ring pages
+    "window_off_by_one": ("*first = window > 0 ? *last - window + 1 : 0;",
+                          "*first = window > 0 ? *last - window : 0;"),
+    "window_from_row0": ("*first = window > 0 ? *last - window + 1 : 0;",
+                         "*first = window > 0 ? L - R - window + 1 : 0;"),
+    "ring_ignored": ("pt_row[ring > 0 ? (t / P) % ring : t / P]", "pt_row[t / P]"),
     "gqa_map_logits": ("int h = hq / G;", "int h = hq % Hkv;"),
     "gqa_map_values": ("int h = hq / (Hq / Hkv);", "int h = hq % Hkv;"),
     "exp_sign": ("w[t] = exp(w[t] - m);", "w[t] = exp(m - w[t]);"),
@@ -36,7 +42,7 @@ MUTATIONS = {
                           "int lane = 16 * (t % 4) + d % 16;\n  int r = t / 4;"),
     "wrong_query_row": ("q + (((size_t)b * R + i) * Hq + hq) * D",
                         "q + (((size_t)b * R + (R - 1)) * Hq + hq) * D"),
-    "no_normalize": ("for (int t = 0; t < n; ++t) w[t] /= sum;", ""),
+    "no_normalize": ("for (int t = first; t <= last; ++t) w[t] /= sum;", ""),
     "no_running_max": ("if (w[t] > m) m = w[t];", "m = 0.0;"),
     # K8/V8 (8-bit V codes)
     "v8_qmax": ("const int vqmax = vb == 8 ? 127 : 7;", "const int vqmax = vb == 8 ? 63 : 7;"),
