@@ -225,6 +225,51 @@ int kvq_decode_step_fmt(int32_t kv_format, void* pool, int32_t num_pages, int32_
                         int32_t max_seq_len, float softmax_scale, int32_t num_splits, float* out,
                         float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- sliding window over ring pages ---------------------------------------------------
+ * kvq_decode_attn / kvq_decode_step (in format kv_format) where each row sees only the last
+ * `window` tokens up to its own position, and the pages of a sequence may be a ring: the
+ * ring-buffer / sliding-window KV that blog page "標籤: vLLM" (section 重點說明, part 2) names
+ * for steady latency at long context.  With L = seq_lens[b], row i is at position
+ * p = L - n_rows + i and
+ *   z_t = softmax_scale * q . K^[t]   for t = max(0, p - window + 1) .. p
+ * (window = 0: from token 0, as kvq_decode_attn).  The pieces cover only the blocks from the
+ * first row's window start on, so the work per call is bounded by the window, not by L.
+ *   window        0, or the number of tokens each row sees (its own included).
+ *   ring_pages    0: token t is at page page_table[b][t / page_size], slot t % page_size, and
+ *                 max_seq_len <= max_pages_per_seq * page_size as before.  > 0 (needs
+ *                 window > 0): logical page n of a sequence is entry n % ring_pages of its row,
+ *                 so a sequence needs only ring_pages pages however long it grows; L may exceed
+ *                 max_pages_per_seq * page_size (max_seq_len still bounds it).  Requires
+ *                 ring_pages <= max_pages_per_seq and
+ *                 ring_pages >= (window + n_rows - 1 + page_size - 2) / page_size + 1, the most
+ *                 pages window + n_rows - 1 consecutive tokens can touch; then no token a row
+ *                 sees has been overwritten by a later one.  The caller's slot_mapping for
+ *                 kvq_append follows the same map.
+ *   n_new         (step) at most window + n_rows - 1: every appended token is one some row sees.
+ * The workspace need is kvq_decode_workspace_bytes_win; kvq_decode_num_splits_win gives the
+ * pieces per context.  Returns as kvq_decode_attn; an inconsistent window / ring gives
+ * KVQ_ERR_ARG. */
+int kvq_decode_attn_win(int32_t kv_format, const void* pool, int32_t num_pages, int32_t page_size,
+                        int32_t num_kv_heads, int32_t head_dim, const uint16_t* q,
+                        const int32_t* page_table, const int32_t* seq_lens, int32_t n_seq,
+                        int32_t n_rows, int32_t n_q_heads, int32_t max_pages_per_seq,
+                        int32_t max_seq_len, int32_t window, int32_t ring_pages,
+                        float softmax_scale, int32_t num_splits, float* out, float* lse,
+                        void* workspace, size_t workspace_bytes, void* stream);
+int kvq_decode_step_win(int32_t kv_format, void* pool, int32_t num_pages, int32_t page_size,
+                        int32_t num_kv_heads, int32_t head_dim, const float* k_new,
+                        const float* v_new, int32_t n_new, const uint16_t* q,
+                        const int32_t* page_table, const int32_t* seq_lens, int32_t n_seq,
+                        int32_t n_rows, int32_t n_q_heads, int32_t max_pages_per_seq,
+                        int32_t max_seq_len, int32_t window, int32_t ring_pages,
+                        float softmax_scale, int32_t num_splits, float* out, float* lse,
+                        void* workspace, size_t workspace_bytes, void* stream);
+int32_t kvq_decode_num_splits_win(int32_t n_seq, int32_t num_kv_heads, int32_t max_seq_len,
+                                  int32_t n_rows, int32_t window, int32_t num_splits_request);
+size_t kvq_decode_workspace_bytes_win(int32_t n_seq, int32_t n_rows, int32_t n_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
+                                      int32_t window, int32_t num_splits_request);
+
 /* Static description of a return code. */
 const char* kvq_strerror(int code);
 

@@ -140,12 +140,26 @@ int kvq_append(void* pool, int32_t num_pages, int32_t page_size, int32_t num_kv_
 
 namespace {
 
+// Tokens whose blocks one context piece plan covers: the whole context, or with a window the
+// W + n_rows - 1 positions the rows see plus up to 31 tokens of the first block before them.
+long long span_tokens(int32_t max_seq_len, int32_t n_rows, int32_t window) {
+  if (window <= 0) return max_seq_len;
+  const long long w = (long long)window + n_rows - 1 + (kvq::kBlock - 1);
+  return w < max_seq_len ? w : max_seq_len;
+}
+
+// Ring pages every call must hold so that no token a row sees has been overwritten: W + n_rows
+// - 1 consecutive tokens at any offset within a page span at most this many pages.
+long long ring_pages_needed(int32_t page_size, int32_t n_rows, int32_t window) {
+  return ((long long)window + n_rows - 1 + page_size - 2) / page_size + 1;
+}
+
 int decode_impl(int32_t kv_format, const void* pool, int32_t num_pages, int32_t page_size,
                 int32_t num_kv_heads, int32_t head_dim, const float* k_new, const float* v_new, int32_t n_new,
                 const uint16_t* q, const int32_t* page_table, const int32_t* seq_lens, int32_t n_seq,
                 int32_t n_rows, int32_t n_q_heads, int32_t max_pages_per_seq, int32_t max_seq_len,
-                float softmax_scale, int32_t num_splits, float* out, float* lse, void* workspace,
-                size_t workspace_bytes, void* stream) {
+                int32_t window, int32_t ring_pages, float softmax_scale, int32_t num_splits,
+                float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   const int vb = vbits_of(kv_format);
   int rc = pool_args_ok(pool, num_pages, page_size, num_kv_heads, head_dim, vb);
   if (rc != KVQ_OK) return rc;
@@ -157,11 +171,20 @@ int decode_impl(int32_t kv_format, const void* pool, int32_t num_pages, int32_t 
   if (n_q_heads % num_kv_heads != 0) return KVQ_ERR_ARG;
   const int group = n_q_heads / num_kv_heads;
   if ((long long)group * n_rows > KVQ_MAX_ROWS_PER_KV) return KVQ_ERR_UNSUPPORTED;
-  if ((long long)max_seq_len > (long long)max_pages_per_seq * page_size) return KVQ_ERR_ARG;
+  if (window < 0 || ring_pages < 0 || (ring_pages > 0 && window == 0)) return KVQ_ERR_ARG;
+  if (ring_pages > 0) {
+    if (ring_pages > max_pages_per_seq || ring_pages < ring_pages_needed(page_size, n_rows, window))
+      return KVQ_ERR_ARG;
+  } else if ((long long)max_seq_len > (long long)max_pages_per_seq * page_size) {
+    return KVQ_ERR_ARG;
+  }
+  // a fused step appends only tokens some row sees (the pieces that attend them write them)
+  if (window > 0 && (long long)n_new > (long long)window + n_rows - 1) return KVQ_ERR_ARG;
   if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return KVQ_ERR_ARG;
   if (((uintptr_t)q & 15) != 0) return KVQ_ERR_ARG;
   Plan plan;
-  rc = plan_splits(n_seq, num_kv_heads, max_seq_len, num_splits, &plan);
+  rc = plan_splits(n_seq, num_kv_heads, (int)span_tokens(max_seq_len, n_rows, window), num_splits,
+                   &plan);
   if (rc != KVQ_OK) return rc;
   const int rows = group * n_rows;
   const long long units = (long long)n_seq * num_kv_heads;
@@ -187,6 +210,8 @@ int decode_impl(int32_t kv_format, const void* pool, int32_t num_pages, int32_t 
   a.rows = rows;
   a.max_pages = max_pages_per_seq;
   a.max_seq_len = max_seq_len;
+  a.window = window;
+  a.ring = ring_pages;
   a.splits = plan.splits;
   a.blocks_per_split = plan.blocks_per_split;
   a.scale_log2 = (float)(scale * 1.4426950408889634074);
@@ -214,8 +239,8 @@ int kvq_decode_attn_fmt(int32_t kv_format, const void* pool, int32_t num_pages, 
                         float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(kv_format, pool, num_pages, page_size, num_kv_heads, head_dim, nullptr, nullptr, 0,
                      q, page_table, seq_lens, n_seq, n_rows, n_q_heads, max_pages_per_seq,
-                     max_seq_len, softmax_scale, num_splits, out, lse, workspace, workspace_bytes,
-                     stream);
+                     max_seq_len, 0, 0, softmax_scale, num_splits, out, lse, workspace,
+                     workspace_bytes, stream);
 }
 
 int kvq_decode_attn(const void* pool, int32_t num_pages, int32_t page_size,
@@ -241,8 +266,8 @@ int kvq_decode_step_fmt(int32_t kv_format, void* pool, int32_t num_pages, int32_
   if (n_new > 0 && (!k_new || !v_new)) return KVQ_ERR_ARG;
   return decode_impl(kv_format, pool, num_pages, page_size, num_kv_heads, head_dim, k_new, v_new, n_new,
                      q, page_table, seq_lens, n_seq, n_rows, n_q_heads, max_pages_per_seq,
-                     max_seq_len, softmax_scale, num_splits, out, lse, workspace, workspace_bytes,
-                     stream);
+                     max_seq_len, 0, 0, softmax_scale, num_splits, out, lse, workspace,
+                     workspace_bytes, stream);
 }
 
 int kvq_decode_step(void* pool, int32_t num_pages, int32_t page_size, int32_t num_kv_heads,
@@ -255,6 +280,53 @@ int kvq_decode_step(void* pool, int32_t num_pages, int32_t page_size, int32_t nu
                              v_new, n_new, q, page_table, seq_lens, n_seq, n_rows, n_q_heads,
                              max_pages_per_seq, max_seq_len, softmax_scale, num_splits, out, lse,
                              workspace, workspace_bytes, stream);
+}
+
+int32_t kvq_decode_num_splits_win(int32_t n_seq, int32_t num_kv_heads, int32_t max_seq_len,
+                                  int32_t n_rows, int32_t window, int32_t num_splits_request) {
+  if (n_rows < 1 || window < 0) return KVQ_ERR_ARG;
+  Plan p;
+  const int rc = plan_splits(n_seq, num_kv_heads, (int)span_tokens(max_seq_len, n_rows, window),
+                             num_splits_request, &p);
+  return rc == KVQ_OK ? p.splits : rc;
+}
+
+size_t kvq_decode_workspace_bytes_win(int32_t n_seq, int32_t n_rows, int32_t n_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
+                                      int32_t window, int32_t num_splits_request) {
+  if (n_rows <= 0 || window < 0) return 0;
+  return kvq_decode_workspace_bytes(n_seq, n_rows, n_q_heads, num_kv_heads, head_dim,
+                                    (int32_t)span_tokens(max_seq_len, n_rows, window),
+                                    num_splits_request);
+}
+
+int kvq_decode_attn_win(int32_t kv_format, const void* pool, int32_t num_pages, int32_t page_size,
+                        int32_t num_kv_heads, int32_t head_dim, const uint16_t* q,
+                        const int32_t* page_table, const int32_t* seq_lens, int32_t n_seq,
+                        int32_t n_rows, int32_t n_q_heads, int32_t max_pages_per_seq,
+                        int32_t max_seq_len, int32_t window, int32_t ring_pages,
+                        float softmax_scale, int32_t num_splits, float* out, float* lse,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(kv_format, pool, num_pages, page_size, num_kv_heads, head_dim, nullptr, nullptr, 0,
+                     q, page_table, seq_lens, n_seq, n_rows, n_q_heads, max_pages_per_seq,
+                     max_seq_len, window, ring_pages, softmax_scale, num_splits, out, lse,
+                     workspace, workspace_bytes, stream);
+}
+
+int kvq_decode_step_win(int32_t kv_format, void* pool, int32_t num_pages, int32_t page_size,
+                        int32_t num_kv_heads, int32_t head_dim, const float* k_new,
+                        const float* v_new, int32_t n_new, const uint16_t* q,
+                        const int32_t* page_table, const int32_t* seq_lens, int32_t n_seq,
+                        int32_t n_rows, int32_t n_q_heads, int32_t max_pages_per_seq,
+                        int32_t max_seq_len, int32_t window, int32_t ring_pages,
+                        float softmax_scale, int32_t num_splits, float* out, float* lse,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_new < 0 || n_new > KVQ_MAX_STEP_TOKENS) return KVQ_ERR_ARG;
+  if (n_new > 0 && (!k_new || !v_new)) return KVQ_ERR_ARG;
+  return decode_impl(kv_format, pool, num_pages, page_size, num_kv_heads, head_dim, k_new, v_new, n_new,
+                     q, page_table, seq_lens, n_seq, n_rows, n_q_heads, max_pages_per_seq,
+                     max_seq_len, window, ring_pages, softmax_scale, num_splits, out, lse,
+                     workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

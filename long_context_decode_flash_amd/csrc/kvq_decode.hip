@@ -329,10 +329,10 @@ __device__ inline void read_tile(TileRaw<D, VB>& r, const uint8_t* src, int lane
 //          sums of 2^(z - base) * (1, v);  it only moves up, in whole powers of two, when a block's
 //          largest logit and V scale would push p * v_scale past 2^15 (fp16 headroom), so most
 //          blocks rescale nothing and every rescale is exact.
-template <int D, int NB, int VB>
+template <int D, int NB, int VB, bool WIN>
 __device__ __attribute__((always_inline)) inline void process_block(
     TileRaw<D, VB> (&raw)[2], int blk, bool masked, float e5, const i32x4 (&qd)[NB][3][D / 64], const float (&cz)[NB],
-    const int (&last_tok)[NB], int g, floatx4 (&acc)[NB][D / 16], float (&base)[NB],
+    const int (&first_tok)[NB], const int (&last_tok)[NB], int g, floatx4 (&acc)[NB][D / 16], float (&base)[NB],
     float (&l_run)[NB]) {
   constexpr int DB = D / 16;
   constexpr int NG = D / 32;
@@ -383,7 +383,8 @@ __device__ __attribute__((always_inline)) inline void process_block(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = blk * kBlock + kTile * tau + 4 * g + e;
-          z[tau][e] = (t <= last_tok[nb]) ? z[tau][e] : kNegInf;
+          const bool seen = WIN ? (t <= last_tok[nb] && t >= first_tok[nb]) : t <= last_tok[nb];
+          z[tau][e] = seen ? z[tau][e] : kNegInf;
         }
     }
 #pragma unroll
@@ -456,6 +457,14 @@ __device__ __attribute__((always_inline)) inline void process_block(
                        hw[2 * tau + 1], lw[2 * tau + 1]);
         }
       }
+      // The halves come from inline asm, which the compiler's hazard tracking does not see, so
+      // it may issue an MFMA reading them one instruction after the last write (that read stale
+      // data).  This nop, ordered after every write and before every read of the eight
+      // registers, gives the matrix core the two wait states a VALU result needs before an MFMA
+      // reads it.  (The same values from plain fp16 code, which the compiler tracks, measured
+      // slower: it builds the upper-half products with two more instructions.)
+      asm("s_nop 1" : "+v"(hw[0]), "+v"(hw[1]), "+v"(hw[2]), "+v"(hw[3]), "+v"(lw[0]), "+v"(lw[1]),
+          "+v"(lw[2]), "+v"(lw[3]));
       const half8 phi = __builtin_bit_cast(half8, u32x4{hw[0], hw[1], hw[2], hw[3]});
       const half8 plo = __builtin_bit_cast(half8, u32x4{lw[0], lw[1], lw[2], lw[3]});
       acc[nb][2 * j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vlo, phi, acc[nb][2 * j], 0, 0, 0);
@@ -470,7 +479,7 @@ __device__ __attribute__((always_inline)) inline void process_block(
 // Each wave streams its blocks through three LDS stage buffers with direct-to-LDS loads, so two
 // blocks are in flight while it computes the third.  The waves merge through LDS into one
 // partial (the output itself when the context is a single piece).
-template <int D, int NB, int VB>
+template <int D, int NB, int VB, bool WIN>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   constexpr int DB = D / 16;
   constexpr int ROWS = 16 * NB;
@@ -502,7 +511,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int L = a.seq_lens[b];
   const int Lc = min(L, a.max_seq_len);  // tokens past max_seq_len are not attended
   const int nblk = (max(Lc, 0) + kBlock - 1) / kBlock;
-  const int g_blk0 = split * a.blocks_per_split;
+  // first token any row sees: the first row's window start (WIN: a sliding window; without
+  // one the first page ids load without waiting for the sequence length)
+  const int t_lo = WIN ? max(L - a.n_rows - a.window + 1, 0) : 0;
+  const int g_blk0 = (t_lo >> 5) + split * a.blocks_per_split;
   const int g_blk1 = min(g_blk0 + a.blocks_per_split, nblk);
   const int m16 = lane & 15, g = lane >> 4;
   const size_t bb = block_bytes(P, D, VB);
@@ -511,6 +523,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
   const int nblk_max = (a.max_seq_len + kBlock - 1) / kBlock;
   const int lgP = a.log2_page;
+  const int ring = WIN ? a.ring : 0;
+  // page-table entry of logical page n (a ring reuses its entries cyclically)
+  auto entry = [&](int n) { return WIN && ring > 0 ? n % ring : n; };
   int c0 = g_blk0, first = 0, n_my = 0, my_pid = 0;
   // Lane kk < 32 holds the physical page of tile 0 of this wave's kk-th block of the chunk, lane
   // 32 + kk that of tile 1.  The ids are loaded for the blocks below max_seq_len, so the load
@@ -523,7 +538,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int blk = first + kWavesPerGroup * kk;
     int tok0 = blk * kBlock + kTile * (lane >> 5);
     if (tok0 >= a.max_seq_len) tok0 = blk * kBlock;
-    my_pid = pt[kk < n_ids ? tok0 >> lgP : 0];  // every lane loads (entry 0 always exists)
+    my_pid = pt[kk < n_ids ? entry(tok0 >> lgP) : 0];  // every lane loads (entry 0 always exists)
   };
   chunk_pages();  // the first chunk's ids load alongside the sequence length and the queries
 
@@ -531,7 +546,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // ---- raw query words: lane holds query row 16*nb + m16 and the 16 dims 16*(4*jj + g) .. +15
   // of each 64-dim step jj (the B-operand layout of QK^T) ----
   u32x4 qw[NB][D / 64][2];
-  int last_tok[NB];
+  int last_tok[NB], first_tok[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int n = 16 * nb + m16;
@@ -539,6 +554,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int i = real ? n / a.group : 0;
     const int hq = h * a.group + (real ? n % a.group : 0);
     last_tok[nb] = min(real ? L - a.n_rows + i : L - 1, Lc - 1);  // padding rows: q = 0
+    first_tok[nb] = WIN ? (real ? L - a.n_rows + i : L - 1) - a.window + 1 : 0;
     const uint16_t* qrow = a.q + (((size_t)b * a.n_rows + i) * a.n_q_heads + hq) * D;
 #pragma unroll
     for (int jj = 0; jj < D / 64; ++jj)
@@ -546,8 +562,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       for (int hf = 0; hf < 2; ++hf)
         qw[nb][jj][hf] = real ? *(const u32x4*)(qrow + 16 * (4 * jj + g) + 8 * hf) : u32x4{0, 0, 0, 0};
   }
-  // first token that some row may mask (causal MTP rows, the ragged end, max_seq_len)
+  // first token that some row may mask (causal MTP rows, the ragged end, max_seq_len), and the
+  // token below which some row may mask (the last row's window start)
   const int mask_from = min(L - a.n_rows + 1, Lc);
+  const int mask_below = WIN ? L - a.window : 0;
 
   // ---- chunks of the split: page ids in lanes, blocks staged through three LDS buffers ----
   // LDS byte address of this wave's stage buffers (wave-uniform, computed once)
@@ -597,7 +615,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int t = L - a.n_new + j;
     const int blk = t >> 5;
     if (t < 0 || blk < g_blk0 || blk >= g_blk1 || ((blk - g_blk0) & (kWavesPerGroup - 1)) != w) continue;
-    const int page = min(max(pt[t >> lgP], 0), a.num_pages - 1);
+    const int page = min(max(pt[entry(t >> lgP)], 0), a.num_pages - 1);
     const size_t row = (((size_t)b * a.n_new + j) * a.num_kv_heads + h) * D;
     append_row<D, VB>(a.pool_rw + ((size_t)page * a.num_kv_heads + h) * bb, P, t & (P - 1), a.k_new + row,
                   a.v_new + row, lane);
@@ -701,11 +719,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       const uint8_t* src = my_stage + st_read * BS;
       st_read = st_read == NSTAGE - 1 ? 0 : st_read + 1;
       const int blk = first + kWavesPerGroup * k;
-      const bool masked = blk * kBlock + kBlock - 1 >= mask_from;
+      const bool masked = blk * kBlock + kBlock - 1 >= mask_from || (WIN && blk * kBlock < mask_below);
       if (masked && lane < kBlock) {
-        // a slot past the context may hold junk scale bits, and 0 * Inf is no zero: clear the V
-        // scales of those slots in the staged copy (the same wave reads them below, in order)
-        if (blk * kBlock + lane >= Lc) {
+        // a slot no row sees (past the context, or before every window) may hold junk scale
+        // bits, and 0 * Inf is no zero: clear the V scales of those slots in the staged copy
+        // (the same wave reads them below, in order)
+        if (blk * kBlock + lane >= Lc || (WIN && blk * kBlock + lane < t_lo)) {
           uint8_t* vs = (uint8_t*)src + (lane >> 4) * Stage<D, VB>::kTileBytes + Stage<D, VB>::kVs + (lane & 15) * (D / 16);
           if constexpr (D == 256) *(u32x4*)vs = u32x4{0, 0, 0, 0};
           else if constexpr (D == 128) *(u32x2*)vs = u32x2{0, 0};
@@ -724,7 +743,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             __builtin_bit_cast(u16x2, vsw[0]), __builtin_bit_cast(u16x2, vsw[Stage<D, VB>::kTileBytes / 4]))));
         e5 = (float)((m >> 10) & 31);
       }
-      process_block<D, NB, VB>(raw, blk, masked, e5, qd, cz, last_tok, g, acc, base, l_run);
+      process_block<D, NB, VB, WIN>(raw, blk, masked, e5, qd, cz, first_tok, last_tok, g, acc, base, l_run);
     }
     c0 += CHUNK;
     if (c0 < g_blk1) {
@@ -837,22 +856,30 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a) {
   if (q == 0 && a.lse) a.lse[o] = den > 0.0f ? (mx + log2f(den)) * 0.69314718055994530942f : kNegInf;
 }
 
+template <int D, bool WIN>
+void launch_attn(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t stream) {
+  if (a.vbits == 8) {
+    if (a.rows <= 16)
+      hipLaunchKernelGGL((decode_kernel<D, 1, 8, WIN>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<D, 2, 8, WIN>), grid, block, 0, stream, a);
+  } else {
+    if (a.rows <= 16)
+      hipLaunchKernelGGL((decode_kernel<D, 1, 4, WIN>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<D, 2, 4, WIN>), grid, block, 0, stream, a);
+  }
+}
+
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
   const unsigned units = (unsigned)((long long)a.n_seq * a.num_kv_heads);
   const unsigned grid = units * (unsigned)a.splits;
   const dim3 block(kWave * kWavesPerGroup);
-  if (a.vbits == 8) {
-    if (a.rows <= 16)
-      hipLaunchKernelGGL((decode_kernel<D, 1, 8>), dim3(grid), block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((decode_kernel<D, 2, 8>), dim3(grid), block, 0, stream, a);
-  } else {
-    if (a.rows <= 16)
-      hipLaunchKernelGGL((decode_kernel<D, 1, 4>), dim3(grid), block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((decode_kernel<D, 2, 4>), dim3(grid), block, 0, stream, a);
-  }
+  if (a.window > 0)
+    launch_attn<D, true>(a, dim3(grid), block, stream);
+  else
+    launch_attn<D, false>(a, dim3(grid), block, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   const unsigned per_unit = (unsigned)((a.rows * (D / 4) + kWave - 1) / kWave);

@@ -50,6 +50,10 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   int n_seq, n_rows, n_q_heads, group, rows;  // rows = group * n_rows (query rows per KV head)
   int max_pages, max_seq_len;
+  // window > 0: row i sees only tokens L - n_rows + i - window + 1 ..; the splits then cover the
+  // blocks from the first row's window start on.  ring > 0: logical page n of a sequence is in
+  // page-table entry n % ring.  0 and 0: the whole context through a linear page table.
+  int window, ring;
   int splits, blocks_per_split;  // workgroups per (sequence, KV head), 32-token blocks each
   float scale_log2;  // softmax_scale * log2(e)
   float* ws_acc;     // [units][splits][rows][D] partial numerators

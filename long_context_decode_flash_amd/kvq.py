@@ -72,6 +72,17 @@ def lib():
         L.kvq_decode_attn_fmt.restype = ctypes.c_int
         L.kvq_decode_step_fmt.argtypes = [I] + L.kvq_decode_step.argtypes
         L.kvq_decode_step_fmt.restype = ctypes.c_int
+        # sliding window over ring pages: (window, ring_pages) after max_seq_len
+        at = L.kvq_decode_attn_fmt.argtypes
+        L.kvq_decode_attn_win.argtypes = at[:14] + [I, I] + at[14:]
+        L.kvq_decode_attn_win.restype = ctypes.c_int
+        st = L.kvq_decode_step_fmt.argtypes
+        L.kvq_decode_step_win.argtypes = st[:17] + [I, I] + st[17:]
+        L.kvq_decode_step_win.restype = ctypes.c_int
+        L.kvq_decode_num_splits_win.argtypes = [I, I, I, I, I, I]
+        L.kvq_decode_num_splits_win.restype = I
+        L.kvq_decode_workspace_bytes_win.argtypes = [I, I, I, I, I, I, I, I]
+        L.kvq_decode_workspace_bytes_win.restype = ctypes.c_size_t
         _lib = L
         return L
 
@@ -90,17 +101,42 @@ def pool_bytes(num_pages: int, page_size: int, num_kv_heads: int, head_dim: int,
 
 
 def decode_num_splits(n_seq: int, num_kv_heads: int, max_seq_len: int,
-                      num_splits: int = 0) -> int:
-    r = int(lib().kvq_decode_num_splits(n_seq, num_kv_heads, max_seq_len, num_splits))
+                      num_splits: int = 0, *, n_rows: int = 1, window: int = 0) -> int:
+    if window:
+        r = int(lib().kvq_decode_num_splits_win(n_seq, num_kv_heads, max_seq_len, n_rows, window,
+                                                 num_splits))
+    else:
+        r = int(lib().kvq_decode_num_splits(n_seq, num_kv_heads, max_seq_len, num_splits))
     if r < 0:
         raise KVQError(r, "kvq_decode_num_splits")
     return r
 
 
 def decode_workspace_bytes(n_seq: int, n_rows: int, n_q_heads: int, num_kv_heads: int,
-                           head_dim: int, max_seq_len: int, num_splits: int = 0) -> int:
+                           head_dim: int, max_seq_len: int, num_splits: int = 0, *,
+                           window: int = 0) -> int:
+    if window:
+        return int(lib().kvq_decode_workspace_bytes_win(n_seq, n_rows, n_q_heads, num_kv_heads,
+                                                         head_dim, max_seq_len, window,
+                                                         num_splits))
     return int(lib().kvq_decode_workspace_bytes(n_seq, n_rows, n_q_heads, num_kv_heads,
                                                  head_dim, max_seq_len, num_splits))
+
+
+def _attn_fn(window: int, ring_pages: int):
+    """The decode entry point for these window / ring arguments, and a function that inserts
+    them into an argument tuple of the plain (format) call."""
+    if window or ring_pages:
+        return (lib().kvq_decode_attn_win,
+                lambda a: a[:14] + (int(window), int(ring_pages)) + a[14:])
+    return lib().kvq_decode_attn_fmt, lambda a: a
+
+
+def _step_fn(window: int, ring_pages: int):
+    if window or ring_pages:
+        return (lib().kvq_decode_step_win,
+                lambda a: a[:17] + (int(window), int(ring_pages)) + a[17:])
+    return lib().kvq_decode_step_fmt, lambda a: a
 
 
 def _stream_ptr(stream) -> int:
@@ -165,9 +201,10 @@ def decode_attn(cache: PagedCache, q: torch.Tensor, page_table: torch.Tensor,
                 seq_lens: torch.Tensor, max_seq_len: int, *, softmax_scale: float = 0.0,
                 num_splits: int = 0, out: torch.Tensor | None = None, want_lse: bool = True,
                 lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                stream=None):
+                stream=None, window: int = 0, ring_pages: int = 0):
     """kvq_decode_attn. q: fp16 [n_seq][n_rows][Hq][D]; page_table: int32 [n_seq][max_pages];
-    seq_lens: int32 [n_seq]. Returns (out fp32 [n_seq][n_rows][Hq][D], lse or None)."""
+    seq_lens: int32 [n_seq]. Returns (out fp32 [n_seq][n_rows][Hq][D], lse or None).
+    ``window`` / ``ring_pages`` > 0 select kvq_decode_attn_win (sliding window, ring pages)."""
     if q.dim() != 4 or q.shape[3] != cache.head_dim:
         raise ValueError("q must be [n_seq][n_rows][n_q_heads][head_dim]")
     n_seq, n_rows, n_q_heads, D = (int(x) for x in q.shape)
@@ -181,17 +218,18 @@ def decode_attn(cache: PagedCache, q: torch.Tensor, page_table: torch.Tensor,
     if want_lse and lse is None:
         lse = torch.empty((n_seq, n_rows, n_q_heads), dtype=torch.float32, device=dev)
     need = decode_workspace_bytes(n_seq, n_rows, n_q_heads, cache.num_kv_heads, D, max_seq_len,
-                                  num_splits)
+                                  num_splits, window=window)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    rc = lib().kvq_decode_attn_fmt(
+    fn, ins = _attn_fn(window, ring_pages)
+    rc = fn(*ins((
         cache.kv_format, _dev(cache.pool, "pool", torch.uint8), cache.num_pages, cache.page_size,
         cache.num_kv_heads, D, _dev(q, "q", torch.float16),
         _dev(page_table, "page_table", torch.int32), _dev(seq_lens, "seq_lens", torch.int32),
         n_seq, n_rows, n_q_heads, int(page_table.shape[1]), int(max_seq_len),
         float(softmax_scale), int(num_splits), _dev(out, "out", torch.float32),
         _dev(lse, "lse", torch.float32) if lse is not None else None,
-        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream_ptr(stream))
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream_ptr(stream))))
     if rc != KVQ_OK:
         raise KVQError(rc, "kvq_decode_attn")
     return out, lse
@@ -224,10 +262,10 @@ def decode_step(cache: PagedCache, k_new: torch.Tensor | None, v_new: torch.Tens
                 max_seq_len: int, *, softmax_scale: float = 0.0, num_splits: int = 0,
                 out: torch.Tensor | None = None, want_lse: bool = True,
                 lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                stream=None):
+                stream=None, window: int = 0, ring_pages: int = 0):
     """kvq_decode_step: append each sequence's newest n_new tokens (k_new, v_new fp32
     [n_seq][n_new][Hkv][D], the last n_new of seq_lens[b]) and attend, in one call.
-    Returns (out, lse) as decode_attn."""
+    Returns (out, lse) as decode_attn (``window`` / ``ring_pages`` as there)."""
     n_seq, n_rows, n_q_heads, D = (int(x) for x in q.shape)
     dev = q.device
     if out is None:
@@ -236,11 +274,11 @@ def decode_step(cache: PagedCache, k_new: torch.Tensor | None, v_new: torch.Tens
         lse = torch.empty((n_seq, n_rows, n_q_heads), dtype=torch.float32, device=dev)
     if workspace is None:
         need = decode_workspace_bytes(n_seq, n_rows, n_q_heads, cache.num_kv_heads, D,
-                                      max_seq_len, num_splits)
+                                      max_seq_len, num_splits, window=window)
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    rc = lib().kvq_decode_step_fmt(*_step_args(cache, k_new, v_new, q, page_table, seq_lens,
-                                           max_seq_len, out, lse, workspace, softmax_scale,
-                                           num_splits, stream))
+    fn, ins = _step_fn(window, ring_pages)
+    rc = fn(*ins(_step_args(cache, k_new, v_new, q, page_table, seq_lens, max_seq_len, out, lse,
+                            workspace, softmax_scale, num_splits, stream)))
     if rc != KVQ_OK:
         raise KVQError(rc, "kvq_decode_step")
     return out, lse
@@ -250,11 +288,11 @@ def prepare_decode_step(cache: PagedCache, k_new: torch.Tensor | None, v_new: to
                         q: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
                         max_seq_len: int, out: torch.Tensor, lse: torch.Tensor | None,
                         workspace: torch.Tensor, *, softmax_scale: float = 0.0,
-                        num_splits: int = 0, stream=None):
+                        num_splits: int = 0, stream=None, window: int = 0, ring_pages: int = 0):
     """Marshal the arguments of one kvq_decode_step once; the returned callable re-issues it."""
-    args = _step_args(cache, k_new, v_new, q, page_table, seq_lens, max_seq_len, out, lse,
-                      workspace, softmax_scale, num_splits, stream)
-    fn = lib().kvq_decode_step_fmt
+    fn, ins = _step_fn(window, ring_pages)
+    args = ins(_step_args(cache, k_new, v_new, q, page_table, seq_lens, max_seq_len, out, lse,
+                          workspace, softmax_scale, num_splits, stream))
 
     def call():
         rc = fn(*args)
@@ -287,19 +325,20 @@ def prepare_append(cache: PagedCache, k: torch.Tensor, v: torch.Tensor,
 def prepare_decode_attn(cache: PagedCache, q: torch.Tensor, page_table: torch.Tensor,
                         seq_lens: torch.Tensor, max_seq_len: int, out: torch.Tensor,
                         lse: torch.Tensor | None, workspace: torch.Tensor, *,
-                        softmax_scale: float = 0.0, num_splits: int = 0, stream=None):
+                        softmax_scale: float = 0.0, num_splits: int = 0, stream=None,
+                        window: int = 0, ring_pages: int = 0):
     """Marshal the arguments of one kvq_decode_attn once; the returned callable re-issues it."""
     n_seq, n_rows, n_q_heads, D = (int(x) for x in q.shape)
     if D != cache.head_dim or tuple(out.shape) != (n_seq, n_rows, n_q_heads, D):
         raise ValueError("q / out shapes do not match the cache")
-    args = (cache.kv_format, _dev(cache.pool, "pool", torch.uint8), cache.num_pages,
+    fn, ins = _attn_fn(window, ring_pages)
+    args = ins((cache.kv_format, _dev(cache.pool, "pool", torch.uint8), cache.num_pages,
             cache.page_size, cache.num_kv_heads, D, _dev(q, "q", torch.float16),
             _dev(page_table, "page_table", torch.int32), _dev(seq_lens, "seq_lens", torch.int32),
             n_seq, n_rows, n_q_heads, int(page_table.shape[1]), int(max_seq_len),
             float(softmax_scale), int(num_splits), _dev(out, "out", torch.float32),
             _dev(lse, "lse", torch.float32) if lse is not None else None,
-            _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream_ptr(stream))
-    fn = lib().kvq_decode_attn_fmt
+            _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream_ptr(stream)))
 
     def call():
         rc = fn(*args)

@@ -135,13 +135,14 @@ class Inputs:
         return (np.ascontiguousarray(np.concatenate(ks)), np.ascontiguousarray(np.concatenate(vs)),
                 np.concatenate(ss))
 
-    def ring(self, ring_pages: int, extra_cols: int = 2):
+    def ring(self, ring_pages: int, extra_cols: int = 2, lens=None):
         """The same tokens on ring pages: sequence s owns pool pages [s * ring_pages, (s + 1) *
         ring_pages) in a seeded order, and logical page n of it sits in table entry
         n % ring_pages.  Returns (table [n_seq][ring_pages + extra_cols] int32, (k, v, slots) of
         the tokens a ring that size still holds: each sequence's last ring_pages logical pages,
         below its length, flattened as token_range does).  The extra columns name pages of
-        another sequence, so a lookup that ignores the ring reads the wrong tokens."""
+        another sequence, so a lookup that ignores the ring reads the wrong tokens.  ``lens``
+        (default seq_lens) are the lengths whose resident tokens are returned."""
         wl = self.wl
         P = wl.page_size
         assert wl.n_seq * ring_pages <= wl.pool_pages
@@ -152,8 +153,9 @@ class Inputs:
             other = (s + 1) % wl.n_seq
             table[s, ring_pages:] = other * ring_pages + (np.arange(extra_cols) % ring_pages)
         ks, vs, ss = [], [], []
+        lens = self.seq_lens if lens is None else lens
         for s in range(wl.n_seq):
-            n = int(self.seq_lens[s])
+            n = int(lens[s])
             t0 = max(0, (n - 1) // P - ring_pages + 1) * P
             t = np.arange(t0, n, dtype=np.int64)
             ks.append(self.k[s, t0:n])
@@ -161,6 +163,12 @@ class Inputs:
             ss.append((table[s, (t // P) % ring_pages].astype(np.int64) * P + t % P).astype(np.int32))
         return table, (np.ascontiguousarray(np.concatenate(ks)),
                        np.ascontiguousarray(np.concatenate(vs)), np.concatenate(ss))
+
+    def ring_slots(self, table: np.ndarray, ring_pages: int, seq: int, t0: int, t1: int):
+        """Slots of logical tokens [t0, t1) of ``seq`` on the ring ``table``."""
+        P = self.wl.page_size
+        t = np.arange(t0, t1, dtype=np.int64)
+        return (table[seq, (t // P) % ring_pages].astype(np.int64) * P + t % P).astype(np.int32)
 
     def ragged_split(self, n_new: int):
         """For ragged lengths: the tokens cached before a step that appends each sequence's last

@@ -199,3 +199,53 @@ def test_decode_step_validation(lib):
     assert step_rc(lib, pool=None) == kvq.KVQ_ERR_ARG
     assert step_rc(lib, d=32) == kvq.KVQ_ERR_UNSUPPORTED
     assert step_rc(lib, ws=None) == kvq.KVQ_ERR_WORKSPACE
+
+
+def win_rc(lib, step=False, **kw):
+    a = dict(fmt=0, pool=FAKE, num_pages=8, page_size=16, hkv=2, d=64, k=FAKE, v=FAKE, n_new=1,
+             q=FAKE, pt=FAKE, sl=FAKE, n_seq=1, n_rows=1, hq=4, max_pages=8, max_seq_len=100,
+             window=40, ring=0, scale=0.0, splits=0, out=FAKE, lse=None, ws=FAKE,
+             ws_bytes=1 << 30)
+    a.update(kw)
+    tail = (a["n_seq"], a["n_rows"], a["hq"], a["max_pages"], a["max_seq_len"], a["window"],
+            a["ring"], a["scale"], a["splits"], a["out"], a["lse"], a["ws"], a["ws_bytes"], None)
+    if step:
+        return lib.kvq_decode_step_win(a["fmt"], a["pool"], a["num_pages"], a["page_size"],
+                                       a["hkv"], a["d"], a["k"], a["v"], a["n_new"], a["q"],
+                                       a["pt"], a["sl"], *tail)
+    return lib.kvq_decode_attn_win(a["fmt"], a["pool"], a["num_pages"], a["page_size"], a["hkv"],
+                                   a["d"], a["q"], a["pt"], a["sl"], *tail)
+
+
+def test_window_ring_validation(lib):
+    E = kvq
+    for step in (False, True):
+        assert win_rc(lib, step, window=-1) == E.KVQ_ERR_ARG
+        assert win_rc(lib, step, ring=-1) == E.KVQ_ERR_ARG
+        assert win_rc(lib, step, window=0, ring=4) == E.KVQ_ERR_ARG     # a ring needs a window
+        assert win_rc(lib, step, ring=9) == E.KVQ_ERR_ARG               # more than the table
+        # 40 + 1 - 1 tokens at any offset in 16-token pages touch up to 4 pages
+        assert win_rc(lib, step, ring=3) == E.KVQ_ERR_ARG
+        # 50 + 4 - 1 tokens touch up to 5 pages (an offset of 15 plus 53 tokens)
+        assert win_rc(lib, step, ring=4, n_rows=4, window=50) == E.KVQ_ERR_ARG
+        assert win_rc(lib, step, ring=5, n_rows=4, window=50, ws=None) == E.KVQ_ERR_WORKSPACE
+        # a ring lets positions run past the page table: the call gets as far as the workspace
+        assert win_rc(lib, step, ring=4, max_seq_len=1 << 20, ws=None) == E.KVQ_ERR_WORKSPACE
+        # without a ring the page table must hold max_seq_len
+        assert win_rc(lib, step, max_seq_len=129) == E.KVQ_ERR_ARG
+        assert win_rc(lib, step, fmt=7) == E.KVQ_ERR_UNSUPPORTED
+    # a fused step appends only tokens some row sees
+    assert win_rc(lib, True, window=4, n_rows=2, n_new=6) == E.KVQ_ERR_ARG
+    assert win_rc(lib, True, window=4, n_rows=2, n_new=5, ws=None) == E.KVQ_ERR_WORKSPACE
+
+
+def test_window_split_plan(lib):
+    # a window plans its pieces over W + n_rows - 1 tokens plus one block, not the context
+    for window, n_rows, msl in ((4096, 1, 1 << 20), (65536, 4, 262144), (100, 1, 50)):
+        span = min(window + n_rows - 1 + 31, msl)
+        assert kvq.decode_num_splits(2, 4, msl, n_rows=n_rows, window=window) == \
+            kvq.decode_num_splits(2, 4, span)
+        assert kvq.decode_workspace_bytes(2, n_rows, 24, 4, 256, msl, window=window) == \
+            kvq.decode_workspace_bytes(2, n_rows, 24, 4, 256, span)
+    assert lib.kvq_decode_num_splits_win(1, 4, 1000, 1, -1, 0) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_decode_workspace_bytes_win(1, 1, 4, 4, 64, 1000, -1, 0) == 0

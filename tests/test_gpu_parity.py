@@ -235,7 +235,9 @@ def test_decode_batch_equals_each_sequence_alone():
 # 8-bit V codes (KVQ_FORMAT_K8V8): the same bar, pool bytes bit-exact and outputs within 2e-3.
 
 V8_SMALL = SMALL + [W.custom(n_seq=2, seq_lens=(700, 333), num_kv_heads=2, n_q_heads=12,
-                             head_dim=128, page_size=32, n_rows=2, seed=61, name="d128").wl]
+                             head_dim=128, page_size=32, n_rows=2, seed=61, name="d128").wl,
+                    W.custom(n_seq=1, seq_lens=(300,), num_kv_heads=1, n_q_heads=4,
+                             head_dim=64, page_size=16, n_rows=1, seed=300, name="d64_ragged").wl]
 
 
 @pytest.mark.parametrize("wl", V8_SMALL, ids=lambda w: w.name)
