@@ -52,13 +52,20 @@ def token_bytes(head_dim: int, vbits: int = 4) -> int:
     return head_dim + 2 + head_dim * vbits // 8 + 2 * (head_dim // 32)
 
 
-def decode_algorithmic_bytes(wl, seq_lens, vbits: int = 4) -> int:
+def attended_range(L: int, n_rows: int, window: int):
+    """First and one-past-last token some row of a sequence of L tokens sees."""
+    return (max(0, L - n_rows - window + 1) if window > 0 else 0), L
+
+
+def decode_algorithmic_bytes(wl, seq_lens, vbits: int = 4, window: int = 0) -> int:
     """Bytes the method itself must move per decode call: every cached K/V byte of every
-    attended token once, the queries, the page-table entries used, the outputs (+ lse)."""
+    attended token once (with a window, the tokens some row's window covers), the queries, the
+    page-table entries used, the outputs (+ lse)."""
     D = wl.head_dim
-    kv = sum(int(L) for L in seq_lens) * wl.num_kv_heads * token_bytes(D, vbits)
+    spans = [attended_range(int(L), wl.n_rows, window) for L in seq_lens]
+    kv = sum(t1 - t0 for t0, t1 in spans) * wl.num_kv_heads * token_bytes(D, vbits)
     q = wl.n_seq * wl.n_rows * wl.n_q_heads * D * 2
-    pt = sum(-(-int(L) // wl.page_size) for L in seq_lens) * 4
+    pt = sum((t1 - 1) // wl.page_size - t0 // wl.page_size + 1 for t0, t1 in spans) * 4
     out = wl.n_seq * wl.n_rows * wl.n_q_heads * (D + 1) * 4
     return kv + q + pt + out
 
@@ -68,7 +75,7 @@ def append_algorithmic_bytes(wl, vbits: int = 4) -> int:
     return n * wl.num_kv_heads * (2 * wl.head_dim * 4 + token_bytes(wl.head_dim, vbits)) + n * 4
 
 
-def cpu_baseline(wl, inp, min_seconds=10.0):
+def cpu_baseline(wl, inp, min_seconds=10.0, window=0):
     """The oracle, as it is, on full steps of the workload on the host cores, repeated until
     min_seconds have passed (the step's append writes the same slots each time).  Returns the
     mean seconds per step, the steps run and the threads used."""
@@ -84,7 +91,8 @@ def cpu_baseline(wl, inp, min_seconds=10.0):
         oracle.append(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
                       *inp.step_tokens())
         oracle.decode_attn(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
-                           inp.q_bits, inp.page_table, inp.seq_lens, wl.n_rows, wl.n_q_heads)
+                           inp.q_bits, inp.page_table, inp.seq_lens, wl.n_rows, wl.n_q_heads,
+                           window=window)
         steps += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds:
@@ -154,6 +162,8 @@ def main(argv=None):
                     help="KV cache format: 4-bit (the headline) or 8-bit V codes")
     ap.add_argument("--copies", type=int, default=8, help="pool copies rotated for a cold cache")
     ap.add_argument("--splits", type=int, default=0, help="0 = automatic split plan")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window: each row sees only its last W tokens (0 = all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="time kvq_append + kvq_decode_attn instead of kvq_decode_step")
@@ -244,9 +254,11 @@ def main(argv=None):
     pt = dev_t(inp.page_table)
     sl = dev_t(inp.seq_lens)
     msl = int(wl.seq_len)
-    splits = kvq.decode_num_splits(wl.n_seq, wl.num_kv_heads, msl, args.splits)
+    win = args.window
+    splits = kvq.decode_num_splits(wl.n_seq, wl.num_kv_heads, msl, args.splits, n_rows=wl.n_rows,
+                                   window=win)
     ws = torch.zeros(kvq.decode_workspace_bytes(wl.n_seq, wl.n_rows, wl.n_q_heads,
-                                                wl.num_kv_heads, D, msl, args.splits),
+                                                wl.num_kv_heads, D, msl, args.splits, window=win),
                      dtype=torch.uint8, device=dev)
     out = torch.empty((wl.n_seq, wl.n_rows, wl.n_q_heads, D), dtype=torch.float32, device=dev)
     lse = torch.empty((wl.n_seq, wl.n_rows, wl.n_q_heads), dtype=torch.float32, device=dev)
@@ -264,13 +276,13 @@ def main(argv=None):
         if args.unfused:
             app = kvq.prepare_append(c, k_new, v_new, s_new, stream=stream) if wl.n_new else None
             dec = kvq.prepare_decode_attn(c, q, pt, sl, msl, out, lse, ws,
-                                          num_splits=args.splits, stream=stream)
+                                          num_splits=args.splits, stream=stream, window=win)
             calls.append((lambda app=app, dec=dec: (app and app(), dec())))
         else:
             calls.append(kvq.prepare_decode_step(c, k_rows if wl.n_new else None,
                                                  v_rows if wl.n_new else None, q, pt, sl, msl,
                                                  out, lse, ws, num_splits=args.splits,
-                                                 stream=stream))
+                                                 stream=stream, window=win))
 
     def step(i):
         calls[i % len(calls)]()
@@ -297,7 +309,7 @@ def main(argv=None):
     log(f"[bench] {args.steps} steps in {total_ms:.2f} ms (wall {wall * 1e3:.1f} ms): "
         f"{ms_per_step * 1e3:.1f} us per step")
 
-    dec_bytes = decode_algorithmic_bytes(wl, inp.seq_lens, vbits)
+    dec_bytes = decode_algorithmic_bytes(wl, inp.seq_lens, vbits, win)
     step_bytes = dec_bytes + (append_algorithmic_bytes(wl, vbits) if wl.n_new else 0)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = value  # the step is one call: the attention launch (with the append) + the merge
@@ -336,7 +348,8 @@ def main(argv=None):
         "dtype": "f16",
         "data": "synthetic",
         "config": {
-            "workload": name, "n_seq": wl.n_seq, "seq_len": wl.seq_len,
+            "workload": name + (f"_window{win}" if win else ""), "n_seq": wl.n_seq,
+            "seq_len": wl.seq_len, "window": win,
             "kv_heads": wl.num_kv_heads, "q_heads": wl.n_q_heads, "head_dim": D,
             "page_size": wl.page_size, "pool_pages": wl.pool_pages,
             "page_order": wl.page_order, "query_rows": wl.n_rows, "new_tokens_per_seq": wl.n_new,
@@ -369,7 +382,7 @@ def main(argv=None):
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline: oracle on full steps, about 10 s")
-        dt, n_cpu, cores = cpu_baseline(wl, inp)
+        dt, n_cpu, cores = cpu_baseline(wl, inp, window=win)
         res["cpu_baseline"] = {
             "value": round(step_bytes / dt / 1e9, 4),
             "unit": "GB/s",
@@ -377,7 +390,8 @@ def main(argv=None):
             "kind": "oracle",
             "sample": f"{n_cpu} full steps of {name} (each: append of {wl.n_seq * wl.n_new} "
                       f"tokens + attention of all {wl.n_seq * wl.n_rows * wl.n_q_heads} output rows "
-                      f"over {wl.seq_len} tokens each), fp64, {dt * n_cpu:.1f} s in all",
+                      f"over {min(wl.seq_len, win) if win else wl.seq_len} tokens each), fp64, "
+                      f"{dt * n_cpu:.1f} s in all",
             "s_per_step": round(dt, 3),
         }
     print(json.dumps(res), flush=True)
