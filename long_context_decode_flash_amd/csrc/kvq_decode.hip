@@ -476,9 +476,10 @@ __device__ __attribute__((always_inline)) inline void process_block(
 }
 
 // One workgroup (4 waves) per (unit, split); wave w takes the split's blocks w, w+4, w+8, ...
-// Each wave streams its blocks through three LDS stage buffers with direct-to-LDS loads, so two
-// blocks are in flight while it computes the third.  The waves merge through LDS into one
-// partial (the output itself when the context is a single piece).
+// Each wave streams its blocks through NSTAGE LDS stage buffers with direct-to-LDS loads, so
+// NSTAGE - 1 blocks are in flight while it computes one.  The waves merge through LDS into one
+// partial (the output itself when the context is a single piece).  WIN: a sliding window (the
+// pieces start at the first row's window start; pages may be a ring).
 template <int D, int NB, int VB, bool WIN>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   constexpr int DB = D / 16;
@@ -567,7 +568,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int mask_from = min(L - a.n_rows + 1, Lc);
   const int mask_below = WIN ? L - a.window : 0;
 
-  // ---- chunks of the split: page ids in lanes, blocks staged through three LDS buffers ----
+  // ---- chunks of the split: page ids in lanes, blocks staged through the LDS buffers ----
   // LDS byte address of this wave's stage buffers (wave-uniform, computed once)
   const uint32_t my_stage_lds =
       __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)&s_stage[w][0][0]);
@@ -588,9 +589,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
                     dst + (uint32_t)(tau * Stage<D, VB>::kTileBytes), lane16, sl);
     }
   };
-  // stage buffer of block k: k % 3, tracked incrementally
+  // stage buffer of block k: k % NSTAGE, tracked incrementally
   auto next_stage = [&](uint32_t x) { return x == my_stage_lds + (NSTAGE - 1) * BS ? my_stage_lds : x + BS; };
-  // chunk set-up: this wave's page ids into lanes, then the loads of its first two blocks
+  // chunk set-up: this wave's page ids into lanes, then the loads of its first NSTAGE - 1 blocks
   auto chunk_count = [&]() {
     const int c1 = min(c0 + CHUNK, g_blk1);
     n_my = first < c1 ? (c1 - first + kWavesPerGroup - 1) / kWavesPerGroup : 0;
