@@ -51,12 +51,20 @@ def _declare(lib):
     lib.kvq_oracle_append_fmt.restype = None
     lib.kvq_oracle_read_slot_fmt.argtypes = [P, I, I, I, I, I, I, I, P, P, P, P]
     lib.kvq_oracle_read_slot_fmt.restype = None
-    lib.kvq_oracle_decode_attn_win.argtypes = [P, I, I, I, I, I, I, I, P, P, P, I, I, I, I,
-                                               ctypes.c_double, P, I, P, P]
-    lib.kvq_oracle_decode_attn_win.restype = None
-    lib.kvq_oracle_attn_weights_win.argtypes = [P, I, I, I, I, I, I, I, P, P, P, I, I, I,
-                                                ctypes.c_double, I, I, I, P]
-    lib.kvq_oracle_attn_weights_win.restype = I
+    lib.kvq_oracle_append_kf.argtypes = [P, I, I, I, I, I, P, P, P, I]
+    lib.kvq_oracle_append_kf.restype = None
+    lib.kvq_oracle_decode_attn_kf.argtypes = [P, I, I, I, I, I, I, I, P, P, P, I, I, I, I,
+                                              ctypes.c_double, P, I, P, P]
+    lib.kvq_oracle_decode_attn_kf.restype = None
+    lib.kvq_oracle_attn_weights_kf.argtypes = [P, I, I, I, I, I, I, I, P, P, P, I, I, I,
+                                               ctypes.c_double, I, I, I, P]
+    lib.kvq_oracle_attn_weights_kf.restype = I
+    lib.kvq_oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
+    lib.kvq_oracle_e4m3_to_double.restype = ctypes.c_double
+    lib.kvq_oracle_e4m3_from_float.argtypes = [ctypes.c_float]
+    lib.kvq_oracle_e4m3_from_float.restype = ctypes.c_uint8
+    lib.kvq_oracle_quantize_group_f8.argtypes = [P, I, P, P]
+    lib.kvq_oracle_quantize_group_f8.restype = None
     lib.kvq_oracle_num_threads.argtypes = []
     lib.kvq_oracle_num_threads.restype = I
     return lib
@@ -68,6 +76,16 @@ def _ptr(a: np.ndarray):
 
 def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
+
+
+# KV formats as the library header numbers them: 0 K8/V4, 1 K8/V8, 2 fp8 (e4m3 K and V in the
+# K8/V8 layout).  Calls take either vbits (4 or 8: the integer formats) or kv_format.
+FMT_K8V4, FMT_K8V8, FMT_FP8 = 0, 1, 2
+
+
+def _fmt(vbits, kv_format):
+    kf = (1 if vbits == 8 else 0) if kv_format is None else int(kv_format)
+    return (4 if kf == 0 else 8), kf
 
 
 class Oracle:
@@ -94,7 +112,21 @@ class Oracle:
         self.lib.kvq_oracle_quantize_group(_ptr(x), x.size, int(qmax), _ptr(codes), _ptr(sb))
         return codes, int(sb[0])
 
-    # vbits: bits per V code, 4 (K8/V4, the default) or 8 (K8/V8)
+    def e4m3_to_double(self, code: int) -> float:
+        return self.lib.kvq_oracle_e4m3_to_double(int(code))
+
+    def e4m3_from_float(self, y: float) -> int:
+        return int(self.lib.kvq_oracle_e4m3_from_float(float(y)))
+
+    def quantize_group_f8(self, x):
+        """fp8 scale group (fp32 values). Returns (uint8 E4M3 codes, fp16 scale bits)."""
+        x = _c(x, np.float32)
+        codes = np.zeros(x.size, np.uint8)
+        sb = np.zeros(1, np.uint16)
+        self.lib.kvq_oracle_quantize_group_f8(_ptr(x), x.size, _ptr(codes), _ptr(sb))
+        return codes, int(sb[0])
+
+    # vbits: bits per V code, 4 (K8/V4, the default) or 8 (K8/V8 and fp8)
     def block_bytes(self, page_size: int, head_dim: int, vbits: int = 4) -> int:
         return int(self.lib.kvq_oracle_block_bytes_fmt(page_size, head_dim, vbits))
 
@@ -112,8 +144,9 @@ class Oracle:
         return int(off), int(aux.value)
 
     def append(self, pool: np.ndarray, num_pages: int, page_size: int, num_kv_heads: int,
-               head_dim: int, k, v, slot_mapping, vbits: int = 4) -> None:
+               head_dim: int, k, v, slot_mapping, vbits: int = 4, kv_format=None) -> None:
         """Quantize tokens k, v (fp32 [n_tok][Hkv][D]) into ``pool`` (uint8, in place)."""
+        vbits, kf = _fmt(vbits, kv_format)
         assert pool.dtype == np.uint8 and pool.flags.c_contiguous
         assert pool.size >= self.pool_bytes(num_pages, page_size, num_kv_heads, head_dim, vbits)
         k = _c(k, np.float32)
@@ -121,8 +154,8 @@ class Oracle:
         slots = _c(slot_mapping, np.int32)
         n_tok = slots.size
         assert k.size == n_tok * num_kv_heads * head_dim and v.size == k.size
-        self.lib.kvq_oracle_append_fmt(_ptr(pool), num_pages, page_size, num_kv_heads, head_dim,
-                                       vbits, _ptr(k), _ptr(v), _ptr(slots), n_tok)
+        self.lib.kvq_oracle_append_kf(_ptr(pool), num_pages, page_size, num_kv_heads, head_dim,
+                                      kf, _ptr(k), _ptr(v), _ptr(slots), n_tok)
 
     def new_pool(self, num_pages: int, page_size: int, num_kv_heads: int, head_dim: int,
                  vbits: int = 4):
@@ -143,7 +176,7 @@ class Oracle:
     def decode_attn(self, pool: np.ndarray, num_pages: int, page_size: int, num_kv_heads: int,
                     head_dim: int, q_bits, page_table, seq_lens, n_rows: int, n_q_heads: int,
                     softmax_scale: float = 0.0, select=None, vbits: int = 4, window: int = 0,
-                    ring_pages: int = 0):
+                    ring_pages: int = 0, kv_format=None):
         """fp64 attention. ``q_bits``: uint16 fp16 bits [n_seq][n_rows][Hq][D].
 
         Returns (out, lse): with ``select`` None, out is [n_seq][n_rows][Hq][D] and lse
@@ -151,6 +184,7 @@ class Oracle:
         ``window`` > 0: row i sees only the last ``window`` tokens up to its own position;
         ``ring_pages`` > 0: logical page n lives in page-table entry n mod ``ring_pages``.
         """
+        vbits, kf = _fmt(vbits, kv_format)
         q = _c(q_bits, np.uint16)
         pt = _c(page_table, np.int32)
         sl = _c(seq_lens, np.int32)
@@ -166,8 +200,8 @@ class Oracle:
             count = sel.shape[0]
         out = np.zeros((count, head_dim), np.float64)
         lse = np.zeros(count, np.float64)
-        self.lib.kvq_oracle_decode_attn_win(_ptr(pool), num_pages, page_size, num_kv_heads,
-                                            head_dim, vbits, window, ring_pages, _ptr(q), _ptr(pt),
+        self.lib.kvq_oracle_decode_attn_kf(_ptr(pool), num_pages, page_size, num_kv_heads,
+                                            head_dim, kf, window, ring_pages, _ptr(q), _ptr(pt),
                                             _ptr(sl), n_seq, n_rows, n_q_heads, max_pages,
                                             float(softmax_scale),
                                             None if sel is None else _ptr(sel), count, _ptr(out),
@@ -181,15 +215,16 @@ class Oracle:
                      num_kv_heads: int, head_dim: int, q_bits, page_table, seq_lens,
                      n_rows: int, n_q_heads: int, b: int, i: int, hq: int,
                      softmax_scale: float = 0.0, vbits: int = 4, window: int = 0,
-                     ring_pages: int = 0):
+                     ring_pages: int = 0, kv_format=None):
         """Softmax weights over the L tokens of sequence b for query row i, head hq."""
+        vbits, kf = _fmt(vbits, kv_format)
         q = _c(q_bits, np.uint16)
         pt = _c(page_table, np.int32)
         sl = _c(seq_lens, np.int32)
         max_pages = pt.size // sl.size
         w = np.zeros(max(int(sl[b]), 1), np.float64)
-        n = self.lib.kvq_oracle_attn_weights_win(_ptr(pool), num_pages, page_size, num_kv_heads,
-                                                 head_dim, vbits, window, ring_pages, _ptr(q),
+        n = self.lib.kvq_oracle_attn_weights_kf(_ptr(pool), num_pages, page_size, num_kv_heads,
+                                                 head_dim, kf, window, ring_pages, _ptr(q),
                                                  _ptr(pt), _ptr(sl), n_rows, n_q_heads, max_pages,
                                                  float(softmax_scale), b, i, hq, _ptr(w))
         return w, n

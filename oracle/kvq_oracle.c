@@ -10,7 +10,9 @@
  * up to fp32 rounding):
  *   - quantization of each new token's K row to int8 with one fp16 scale, and of its V row to
  *     int4 (vb = 4) or int8 (vb = 8) with one fp16 scale per 32 dims (the engine's "rk8v4"
- *     K8-V4 KV dtype, and the int8 KV it is compared with: forum post
+ *     K8-V4 KV dtype, and the int8 KV it is compared with; or K and V both as OCP fp8 e4m3
+ *     codes at the same scale granularity, the fp8 KV the same post finds missing on its card:
+ *     forum post
  *     "3090 单卡跑 Qwen3.8-27B：NInfer 上机实测（180K 上下文 / C2 并发 / 4bit KV）", section
  *     一、部署, launch-flag table; the pages leave the scale granularity open, the library
  *     header fixes it and this file follows that definition);
@@ -84,8 +86,7 @@ uint16_t kvq_oracle_fp16_from_double(double x) {
 /* One scale group: absmax -> scale = fp16_rne(absmax / qmax) (fp32 IEEE divide, saturated to
  * the largest finite fp16) -> code = clamp(rint_half_even(x / scale), -qmax, qmax) with the
  * divide in fp32 and the stored fp16 scale, all codes 0 when the scale is 0. */
-void kvq_oracle_quantize_group(const float* x, int n, int qmax, int8_t* codes,
-                               uint16_t* scale_bits) {
+static float group_scale(const float* x, int n, int qmax, uint16_t* scale_bits) {
   float a = 0.0f;
   for (int i = 0; i < n; ++i) {
     float m = fabsf(x[i]);
@@ -95,7 +96,12 @@ void kvq_oracle_quantize_group(const float* x, int n, int qmax, int8_t* codes,
   uint16_t sb = kvq_oracle_fp16_from_double((double)s32);
   if ((sb & 0x7FFF) == 0x7C00) sb = (uint16_t)((sb & 0x8000) | 0x7BFF);
   *scale_bits = sb;
-  float s = (float)kvq_oracle_fp16_to_double(sb);
+  return (float)kvq_oracle_fp16_to_double(sb); /* codes divide by the stored scale */
+}
+
+void kvq_oracle_quantize_group(const float* x, int n, int qmax, int8_t* codes,
+                               uint16_t* scale_bits) {
+  float s = group_scale(x, n, qmax, scale_bits);
   for (int i = 0; i < n; ++i) {
     if (s == 0.0f) {
       codes[i] = 0;
@@ -109,7 +115,60 @@ void kvq_oracle_quantize_group(const float* x, int n, int qmax, int8_t* codes,
   }
 }
 
+/* ---------------------------------------------------------------- OCP fp8 e4m3 ---------- */
+
+/* Value of an OCP 8-bit E4M3 code: sign bit 7, exponent bits 6..3 (bias 7), mantissa bits
+ * 2..0.  Exponent field 0 is subnormal, m * 2^-9; otherwise (8 + m) * 2^(e - 10).  The two
+ * codes with every exponent and mantissa bit set are NaN; there is no infinity. */
+double kvq_oracle_e4m3_to_double(uint8_t c) {
+  int sign = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return NAN;
+  double mag = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+  return sign ? -mag : mag;
+}
+
+/* Round y (|y| <= 448) to the nearest E4M3 value, ties to the even mantissa.  Near |y| the
+ * spacing of E4M3 values is 2^(E-3), E = max(floor(log2|y|), -6); rounding |y| to a multiple
+ * of it is the definition of round-to-nearest (a result of 2^(E+1) is the next binade's
+ * first value).  The sign bit is y's, zeros included. */
+uint8_t kvq_oracle_e4m3_from_float(float y) {
+  uint8_t sign = signbit(y) ? 0x80 : 0;
+  double a = fabs((double)y);
+  if (a > 448.0) a = 448.0;
+  if (a == 0.0) return sign;
+  int E = (int)floor(log2(a));
+  if (E < -6) E = -6;
+  double quantum = ldexp(1.0, E - 3);
+  double r = nearbyint(a / quantum) * quantum; /* the current rounding mode: to nearest even */
+  if (r == 0.0) return sign;
+  if (r < ldexp(1.0, -6)) return sign | (uint8_t)(r / ldexp(1.0, -9)); /* subnormal */
+  int Er = (int)floor(log2(r));
+  int mbits = (int)(ldexp(r, -Er) * 8.0 - 8.0);
+  return sign | (uint8_t)((Er + 7) << 3) | (uint8_t)mbits;
+}
+
+/* One fp8 scale group: scale = fp16_rne(absmax / 448) as for the integer codes; then
+ * code = e4m3_rne(clamp(x / scale, -448, 448)) with the divide in fp32 and the stored fp16
+ * scale, all codes 0 when the scale is 0. */
+void kvq_oracle_quantize_group_f8(const float* x, int n, uint8_t* codes, uint16_t* scale_bits) {
+  float s = group_scale(x, n, 448, scale_bits);
+  for (int i = 0; i < n; ++i) {
+    if (s == 0.0f) {
+      codes[i] = 0;
+      continue;
+    }
+    float y = x[i] / s;
+    if (y > 448.0f) y = 448.0f;
+    if (y < -448.0f) y = -448.0f;
+    codes[i] = kvq_oracle_e4m3_from_float(y);
+  }
+}
+
 /* ---------------------------------------------------------------- page format ------------ */
+
+/* KV formats, as the library header numbers them: 0 K8/V4, 1 K8/V8, 2 fp8 (K and V e4m3, the
+ * K8/V8 byte layout).  vb is the bits per V code the layout uses. */
+static int vb_of(int kf) { return kf == 0 ? 4 : 8; }
 
 /* vb = bits per V code: 4 (K8/V4, two codes per byte) or 8 (K8/V8, one per byte). */
 size_t kvq_oracle_block_bytes_fmt(int P, int D, int vb) {
@@ -166,9 +225,12 @@ static uint8_t* block_of(uint8_t* pool, int Hkv, int P, int D, int vb, int page,
   return pool + ((size_t)page * Hkv + h) * kvq_oracle_block_bytes_fmt(P, D, vb);
 }
 
-/* Quantize n_tok tokens and write them into their slots (slot < 0 or beyond the pool: skip). */
-void kvq_oracle_append_fmt(uint8_t* pool, int num_pages, int P, int Hkv, int D, int vb,
-                           const float* k, const float* v, const int32_t* slots, int n_tok) {
+/* Quantize n_tok tokens and write them into their slots (slot < 0 or beyond the pool: skip),
+ * in KV format kf. */
+void kvq_oracle_append_kf(uint8_t* pool, int num_pages, int P, int Hkv, int D, int kf,
+                          const float* k, const float* v, const int32_t* slots, int n_tok) {
+  const int vb = vb_of(kf);
+  const int f8 = kf == 2;
   const int vqmax = vb == 8 ? 127 : 7;
   int8_t* codes = (int8_t*)malloc((size_t)D);
   for (int n = 0; n < n_tok; ++n) {
@@ -180,13 +242,20 @@ void kvq_oracle_append_fmt(uint8_t* pool, int num_pages, int P, int Hkv, int D, 
       const float* krow = k + ((size_t)n * Hkv + h) * D;
       const float* vrow = v + ((size_t)n * Hkv + h) * D;
       uint16_t sb;
-      kvq_oracle_quantize_group(krow, D, 127, codes, &sb);
+      if (f8)
+        kvq_oracle_quantize_group_f8(krow, D, (uint8_t*)codes, &sb);
+      else
+        kvq_oracle_quantize_group(krow, D, 127, codes, &sb);
       for (int d = 0; d < D; ++d) blk[k_code_offset(D, s, d)] = (uint8_t)codes[d];
       size_t so = k_scale_offset(P, D, s);
       blk[so] = (uint8_t)(sb & 0xFF);
       blk[so + 1] = (uint8_t)(sb >> 8);
       for (int j = 0; j < D / 32; ++j) {
-        kvq_oracle_quantize_group(vrow + 32 * j, 32, vqmax, codes + 32 * j, &sb);
+        const float* vg = vrow + 32 * j; /* scale group j: 32 contiguous dims */
+        if (f8)
+          kvq_oracle_quantize_group_f8(vg, 32, (uint8_t*)codes + 32 * j, &sb);
+        else
+          kvq_oracle_quantize_group(vg, 32, vqmax, codes + 32 * j, &sb);
         size_t vo = v_scale_offset_fmt(P, D, vb, s, j);
         blk[vo] = (uint8_t)(sb & 0xFF);
         blk[vo + 1] = (uint8_t)(sb >> 8);
@@ -204,6 +273,10 @@ void kvq_oracle_append_fmt(uint8_t* pool, int num_pages, int P, int Hkv, int D, 
     }
   }
   free(codes);
+}
+void kvq_oracle_append_fmt(uint8_t* pool, int num_pages, int P, int Hkv, int D, int vb,
+                           const float* k, const float* v, const int32_t* slots, int n_tok) {
+  kvq_oracle_append_kf(pool, num_pages, P, Hkv, D, vb == 8 ? 1 : 0, k, v, slots, n_tok);
 }
 void kvq_oracle_append(uint8_t* pool, int num_pages, int P, int Hkv, int D, const float* k,
                        const float* v, const int32_t* slots, int n_tok) {
@@ -242,17 +315,25 @@ void kvq_oracle_read_slot(const uint8_t* pool, int P, int Hkv, int D, int page, 
 /* Dequantized K and V of logical token t of sequence b, head h (page-table entries clamped
  * into [0, num_pages) as the library header specifies).  ring > 0: logical page t / P sits in
  * entry (t / P) mod ring of the sequence's page-table row; ring = 0: in entry t / P. */
-static void token_kv(const uint8_t* pool, int num_pages, int P, int Hkv, int D, int vb, int ring,
+static void token_kv(const uint8_t* pool, int num_pages, int P, int Hkv, int D, int kf, int ring,
                      const int32_t* pt_row, int t, int h, double* kd, double* vd, int8_t* kc,
                      int8_t* vc, uint16_t* vs) {
+  const int vb = vb_of(kf);
   int page = pt_row[ring > 0 ? (t / P) % ring : t / P];
   if (page < 0) page = 0;
   if (page >= num_pages) page = num_pages - 1;
   uint16_t ks;
   kvq_oracle_read_slot_fmt(pool, P, Hkv, D, vb, page, t % P, h, kc, &ks, vc, vs);
   double sk = kvq_oracle_fp16_to_double(ks);
-  for (int d = 0; d < D; ++d) kd[d] = (double)kc[d] * sk;
-  for (int d = 0; d < D; ++d) vd[d] = (double)vc[d] * kvq_oracle_fp16_to_double(vs[d / 32]);
+  /* fp8 (kf 2): the code bytes are E4M3 values; otherwise two's complement integers */
+  for (int d = 0; d < D; ++d) {
+    double kcode = kf == 2 ? kvq_oracle_e4m3_to_double((uint8_t)kc[d]) : (double)kc[d];
+    kd[d] = kcode * sk;
+  }
+  for (int d = 0; d < D; ++d) {
+    double vcode = kf == 2 ? kvq_oracle_e4m3_to_double((uint8_t)vc[d]) : (double)vc[d];
+    vd[d] = vcode * kvq_oracle_fp16_to_double(vs[d / 32]);
+  }
 }
 
 /* First and last token row i of a sequence of L tokens sees: the causal mask of an MTP verify
@@ -267,7 +348,7 @@ static void row_range(int L, int R, int i, int window, int* first, int* last) {
 /* Softmax weights of one output row (sequence b, query row i, query head hq): w[t] for
  * t < L (0 where masked).  Returns the number of attended tokens; *m_out and *sum_out get the
  * max logit and sum of exp(z - max) for the log-sum-exp. */
-static int row_weights(const uint8_t* pool, int num_pages, int P, int Hkv, int D, int vb,
+static int row_weights(const uint8_t* pool, int num_pages, int P, int Hkv, int D, int kf,
                        int window, int ring, const uint16_t* q, const int32_t* page_table,
                        const int32_t* seq_lens, int R, int Hq, int max_pages, double scale, int b,
                        int i, int hq, double* w, double* m_out, double* sum_out) {
@@ -293,7 +374,7 @@ static int row_weights(const uint8_t* pool, int num_pages, int P, int Hkv, int D
   const int32_t* pt_row = page_table + (size_t)b * max_pages;
   double m = -INFINITY;
   for (int t = first; t <= last; ++t) {
-    token_kv(pool, num_pages, P, Hkv, D, vb, ring, pt_row, t, h, kd, vd, kc, vc, vs);
+    token_kv(pool, num_pages, P, Hkv, D, kf, ring, pt_row, t, h, kd, vd, kc, vc, vs);
     double dot = 0.0;
     for (int d = 0; d < D; ++d) dot += qd[d] * kd[d];
     w[t] = scale * dot; /* logit z_t, replaced by its weight below */
@@ -313,8 +394,8 @@ static int row_weights(const uint8_t* pool, int num_pages, int P, int Hkv, int D
 
 /* Attention outputs for a list of (b, i, hq) triples (sel, n_sel of them), or for every
  * output in [b][i][hq] order when sel is NULL.  out: [count][D] fp64, lse: [count] fp64. */
-void kvq_oracle_decode_attn_win(const uint8_t* pool, int num_pages, int P, int Hkv, int D, int vb,
-                                int window, int ring, const uint16_t* q, const int32_t* page_table,
+void kvq_oracle_decode_attn_kf(const uint8_t* pool, int num_pages, int P, int Hkv, int D, int kf,
+                               int window, int ring, const uint16_t* q, const int32_t* page_table,
                                 const int32_t* seq_lens, int n_seq, int R, int Hq, int max_pages,
                                 double scale, const int32_t* sel, int n_sel, double* out,
                                 double* lse) {
@@ -335,7 +416,7 @@ void kvq_oracle_decode_attn_win(const uint8_t* pool, int num_pages, int P, int H
     int L = seq_lens[b];
     double* w = (double*)malloc(sizeof(double) * (L > 0 ? (size_t)L : 1));
     double m, sum;
-    int n = row_weights(pool, num_pages, P, Hkv, D, vb, window, ring, q, page_table, seq_lens, R,
+    int n = row_weights(pool, num_pages, P, Hkv, D, kf, window, ring, q, page_table, seq_lens, R,
                         Hq, max_pages, scale, b, i, hq, w, &m, &sum);
     double* o_row = out + (size_t)o * D;
     for (int d = 0; d < D; ++d) o_row[d] = 0.0;
@@ -350,7 +431,7 @@ void kvq_oracle_decode_attn_win(const uint8_t* pool, int num_pages, int P, int H
       int first, last;
       row_range(L, R, i, window, &first, &last);
       for (int t = first; t <= last; ++t) {
-        token_kv(pool, num_pages, P, Hkv, D, vb, ring, pt_row, t, h, kd, vd, kc, vc, vs);
+        token_kv(pool, num_pages, P, Hkv, D, kf, ring, pt_row, t, h, kd, vd, kc, vc, vs);
         for (int d = 0; d < D; ++d) o_row[d] += w[t] * vd[d];
       }
       free(kd); free(vd); free(kc); free(vc); free(vs);
@@ -367,8 +448,8 @@ void kvq_oracle_decode_attn_fmt(const uint8_t* pool, int num_pages, int P, int H
                                 const int32_t* seq_lens, int n_seq, int R, int Hq, int max_pages,
                                 double scale, const int32_t* sel, int n_sel, double* out,
                                 double* lse) {
-  kvq_oracle_decode_attn_win(pool, num_pages, P, Hkv, D, vb, 0, 0, q, page_table, seq_lens, n_seq,
-                             R, Hq, max_pages, scale, sel, n_sel, out, lse);
+  kvq_oracle_decode_attn_kf(pool, num_pages, P, Hkv, D, vb == 8 ? 1 : 0, 0, 0, q, page_table,
+                            seq_lens, n_seq, R, Hq, max_pages, scale, sel, n_sel, out, lse);
 }
 
 void kvq_oracle_decode_attn(const uint8_t* pool, int num_pages, int P, int Hkv, int D,
@@ -381,23 +462,23 @@ void kvq_oracle_decode_attn(const uint8_t* pool, int num_pages, int P, int Hkv, 
 }
 
 /* Softmax weights of one output row, w[0..L-1] (0 where masked). Returns attended count. */
-int kvq_oracle_attn_weights_win(const uint8_t* pool, int num_pages, int P, int Hkv, int D, int vb,
-                                int window, int ring, const uint16_t* q,
+int kvq_oracle_attn_weights_kf(const uint8_t* pool, int num_pages, int P, int Hkv, int D, int kf,
+                               int window, int ring, const uint16_t* q,
                                 const int32_t* page_table, const int32_t* seq_lens, int R, int Hq,
                                 int max_pages, double scale, int b, int i, int hq, double* w) {
   if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
   int L = seq_lens[b];
   for (int t = 0; t < L; ++t) w[t] = 0.0;
   double m, sum;
-  return row_weights(pool, num_pages, P, Hkv, D, vb, window, ring, q, page_table, seq_lens, R, Hq,
+  return row_weights(pool, num_pages, P, Hkv, D, kf, window, ring, q, page_table, seq_lens, R, Hq,
                      max_pages, scale, b, i, hq, w, &m, &sum);
 }
 int kvq_oracle_attn_weights_fmt(const uint8_t* pool, int num_pages, int P, int Hkv, int D, int vb,
                                 const uint16_t* q, const int32_t* page_table,
                                 const int32_t* seq_lens, int R, int Hq, int max_pages, double scale,
                                 int b, int i, int hq, double* w) {
-  return kvq_oracle_attn_weights_win(pool, num_pages, P, Hkv, D, vb, 0, 0, q, page_table, seq_lens,
-                                     R, Hq, max_pages, scale, b, i, hq, w);
+  return kvq_oracle_attn_weights_kf(pool, num_pages, P, Hkv, D, vb == 8 ? 1 : 0, 0, 0, q,
+                                    page_table, seq_lens, R, Hq, max_pages, scale, b, i, hq, w);
 }
 int kvq_oracle_attn_weights(const uint8_t* pool, int num_pages, int P, int Hkv, int D,
                             const uint16_t* q, const int32_t* page_table,

@@ -38,8 +38,9 @@ def _brute_ref(i, vqmax=7, window=0):
     inp = _case(i)
     wl = inp.wl
     n, L, H, D = wl.n_seq, wl.seq_len, wl.num_kv_heads, wl.head_dim
-    kc = np.zeros((n, L, H, D), np.int8)
-    vc = np.zeros((n, L, H, D), np.int8)
+    f8 = vqmax == "fp8"
+    kc = np.zeros((n, L, H, D), np.uint8 if f8 else np.int8)
+    vc = np.zeros((n, L, H, D), np.uint8 if f8 else np.int8)
     ks = np.zeros((n, L, H), np.uint16)
     vs = np.zeros((n, L, H, D // 32), np.uint16)
     for b in range(n):
@@ -47,8 +48,10 @@ def _brute_ref(i, vqmax=7, window=0):
             for h in range(H):
                 kc[b, t, h], ks[b, t, h], vc[b, t, h], vs[b, t, h] = brute.quantize_token_np(
                     inp.k[b, t, h], inp.v[b, t, h], vqmax)
+    vals = brute.e4m3_values_torch() if f8 else None
     return brute.attention_brute(inp.q_bits, kc, ks, vc, vs, inp.seq_lens, wl.n_rows,
-                                 wl.n_q_heads, H, 1.0 / math.sqrt(D), window)
+                                 wl.n_q_heads, H, 1.0 / math.sqrt(D), window,
+                                 (lambda c: float(vals[int(c)])) if f8 else None)
 
 
 def _golden_lines(name):
@@ -123,27 +126,28 @@ def check_format_golden_v8(o):
     return _check_format_file(o, "format_offsets_v8.txt", 8)
 
 
-def _fill(o, inp, vbits=4):
+def _fill(o, inp, vbits=4, kv_format=None):
     wl = inp.wl
     pool = o.new_pool(wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim, vbits)
     k, v, slots = inp.all_tokens()
     o.append(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim, k, v, slots,
-             vbits=vbits)
+             vbits=vbits, kv_format=kv_format)
     return pool
 
 
-def _attend(o, inp, pool, scale=0.0, vbits=4):
+def _attend(o, inp, pool, scale=0.0, vbits=4, kv_format=None):
     wl = inp.wl
     return o.decode_attn(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
                          inp.q_bits, inp.page_table, inp.seq_lens, wl.n_rows, wl.n_q_heads,
-                         softmax_scale=scale, vbits=vbits)
+                         softmax_scale=scale, vbits=vbits, kv_format=kv_format)
 
 
-def _brute_force(o, vbits, cases):
+def _brute_force(o, vbits, cases, kv_format=None):
     for i in cases:
         inp = _case(i)
-        out, lse = _attend(o, inp, _fill(o, inp, vbits), vbits=vbits)
-        out_b, lse_b = _brute_ref(i, 127 if vbits == 8 else 7)
+        out, lse = _attend(o, inp, _fill(o, inp, vbits, kv_format), vbits=vbits,
+                           kv_format=kv_format)
+        out_b, lse_b = _brute_ref(i, "fp8" if kv_format == 2 else 127 if vbits == 8 else 7)
         if not (np.allclose(out, out_b, rtol=0, atol=1e-12) and
                 np.allclose(lse, lse_b, rtol=0, atol=1e-11)):
             return False
@@ -157,6 +161,46 @@ def check_brute_force(o):
 def check_brute_force_v8(o):
     """K8/V8: the same brute force with 8-bit V codes (qmax 127)."""
     return _brute_force(o, 8, range(2))
+
+
+def check_brute_force_f8(o):
+    """fp8: the same brute force with E4M3 codes (PyTorch's conversion) for K and V."""
+    return _brute_force(o, 8, range(2), kv_format=2)
+
+
+def check_e4m3(o):
+    """The E4M3 value of every code, and the encoding of a sweep holding every tie between
+    neighbouring values (subnormal, normal, the top of the range), signed zeros and the range
+    ends: against PyTorch's float8_e4m3fn and an argmin over all codes."""
+    vals = brute.e4m3_values_torch()
+    for c in range(256):
+        got = o.e4m3_to_double(c)
+        if not (np.isnan(vals[c]) and np.isnan(got)) and not (got == vals[c] and
+                                                              math.copysign(1, got) == math.copysign(1, vals[c])):
+            return False
+    finite = np.unique(vals[~np.isnan(vals)])
+    mids = (finite[:-1] + finite[1:]) / 2
+    ys = np.concatenate([finite, mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9),
+                         [0.0, -0.0, 448.0, -448.0, 2.0 ** -12, -2.0 ** -12]]).astype(np.float32)
+    ys = ys[np.abs(ys) <= 448]
+    ref = brute.e4m3_codes_torch(ys)
+    got = np.array([o.e4m3_from_float(float(y)) for y in ys], np.uint8)
+    if not np.array_equal(got, ref):
+        return False
+    rng = np.random.default_rng(31)
+    for y in list(rng.choice(ys, 60, replace=False)) + [float(np.float32(-0.0))]:
+        if o.e4m3_from_float(float(y)) != brute.e4m3_argmin(float(y)):
+            return False
+    # the group quantizer: numpy scale and PyTorch codes, zeros and a zero group included
+    for seed in range(4):
+        x = np.random.default_rng(40 + seed).standard_normal(32).astype(np.float32) * 3
+        x[seed] = -0.0
+        codes, sb = o.quantize_group_f8(x)
+        rc, rsb = brute.quantize_group_f8_np(x)
+        if sb != rsb or not np.array_equal(codes, rc):
+            return False
+    codes, sb = o.quantize_group_f8(np.zeros(32, np.float32))
+    return sb == 0 and not codes.any()
 
 
 def check_closed_forms(o):
@@ -242,7 +286,7 @@ def check_window_ring(o):
 
 CHECKS = [check_window_ring, check_fp16, check_quantizer_golden, check_quantizer_argmin, check_format_golden,
           check_brute_force, check_closed_forms, check_large_logits, check_format_golden_v8,
-          check_brute_force_v8]
+          check_brute_force_v8, check_e4m3, check_brute_force_f8]
 
 
 def run(o):

@@ -15,14 +15,22 @@ MUTATIONS = {
     "scale_divisor": ("float s32 = a / (float)qmax;", "float s32 = a / (float)(qmax + 1);"),
     "truncate_not_round": ("float c = nearbyintf(y);", "float c = truncf(y);"),
     "no_clamp": ("if (c > (float)qmax) c = (float)qmax;", ""),
-    "unrounded_scale": ("float s = (float)kvq_oracle_fp16_to_double(sb);", "float s = s32;"),
+    "unrounded_scale": ("return (float)kvq_oracle_fp16_to_double(sb);", "return s32;"),
     "fp16_ties_away": ("double n = nearbyint(a / quantum);", "double n = round(a / quantum);"),
     "fp16_subnormal_floor": ("if (e < -14) e = -14;", "if (e < -15) e = -15;"),
     "v_group_stride": ("vrow + 32 * j", "vrow + 16 * j"),
     "v_nibble_unsigned": ("(int8_t)(nib >= 8 ? nib - 16 : nib)", "(int8_t)(nib)"),
-    "k_scale_dropped": ("kd[d] = (double)kc[d] * sk;", "kd[d] = (double)kc[d];"),
+    "k_scale_dropped": ("kd[d] = kcode * sk;", "kd[d] = kcode;"),
     "v_scale_group": ("kvq_oracle_fp16_to_double(vs[d / 32])", "kvq_oracle_fp16_to_double(vs[d / 64])"),
     "mask_off_by_one": ("*last = L - R + i;", "*last = L - R + i - 1;"),
+    # fp8 (OCP E4M3 codes)
+    "f8_fnuz_max": ("float s = group_scale(x, n, 448, scale_bits);",
+                    "float s = group_scale(x, n, 240, scale_bits);"),
+    "f8_bias_8": ("ldexp((double)(8 + m), e - 10)", "ldexp((double)(8 + m), e - 11)"),
+    "f8_subnormal_step": ("ldexp((double)m, -9)", "ldexp((double)m, -10)"),
+    "f8_ties_away": ("double r = nearbyint(a / quantum) * quantum;",
+                     "double r = round(a / quantum) * quantum;"),
+    "f8_zero_sign": ("uint8_t sign = signbit(y) ? 0x80 : 0;", "uint8_t sign = y < 0 ? 0x80 : 0;"),
     # sliding window over ring pages
     "window_off_by_one": ("*first = window > 0 ? *last - window + 1 : 0;",
                           "*first = window > 0 ? *last - window : 0;"),
