@@ -75,24 +75,25 @@ def append_algorithmic_bytes(wl, vbits: int = 4) -> int:
     return n * wl.num_kv_heads * (2 * wl.head_dim * 4 + token_bytes(wl.head_dim, vbits)) + n * 4
 
 
-def cpu_baseline(wl, inp, min_seconds=10.0, window=0):
+def cpu_baseline(wl, inp, min_seconds=10.0, window=0, kv_format=0):
     """The oracle, as it is, on full steps of the workload on the host cores, repeated until
     min_seconds have passed (the step's append writes the same slots each time).  Returns the
     mean seconds per step, the steps run and the threads used."""
     import oracle
-    pool = oracle.new_pool(wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim)
+    pool = oracle.new_pool(wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
+                           4 if kv_format == 0 else 8)
     t0 = time.perf_counter()
     oracle.append(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
-                  *inp.prefill())
+                  *inp.prefill(), kv_format=kv_format)
     log(f"[cpu] oracle prefill {time.perf_counter() - t0:.1f}s (not timed)")
     steps = 0
     t0 = time.perf_counter()
     while True:
         oracle.append(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
-                      *inp.step_tokens())
+                      *inp.step_tokens(), kv_format=kv_format)
         oracle.decode_attn(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
                            inp.q_bits, inp.page_table, inp.seq_lens, wl.n_rows, wl.n_q_heads,
-                           window=window)
+                           window=window, kv_format=kv_format)
         steps += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds:
@@ -158,7 +159,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=None, help="name in workloads.WORKLOADS")
-    ap.add_argument("--kv-format", default="k8v4", choices=["k8v4", "k8v8"],
+    ap.add_argument("--kv-format", default="k8v4", choices=["k8v4", "k8v8", "fp8"],
                     help="KV cache format: 4-bit (the headline) or 8-bit V codes")
     ap.add_argument("--copies", type=int, default=8, help="pool copies rotated for a cold cache")
     ap.add_argument("--splits", type=int, default=0, help="0 = automatic split plan")
@@ -217,7 +218,7 @@ def main(argv=None):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     fmt = kvq.FORMATS[args.kv_format]
-    vbits = 8 if fmt == kvq.KVQ_FORMAT_K8V8 else 4
+    vbits = 4 if fmt == kvq.KVQ_FORMAT_K8V4 else 8  # fp8 codes use the 8-bit V layout
     caches = [kvq.PagedCache.allocate(wl.pool_pages, wl.page_size, wl.num_kv_heads, D, dev,
                                       kv_format=fmt)]
     k_pre, v_pre, s_pre = (dev_t(x) for x in inp.prefill())
@@ -353,8 +354,10 @@ def main(argv=None):
             "kv_heads": wl.num_kv_heads, "q_heads": wl.n_q_heads, "head_dim": D,
             "page_size": wl.page_size, "pool_pages": wl.pool_pages,
             "page_order": wl.page_order, "query_rows": wl.n_rows, "new_tokens_per_seq": wl.n_new,
-            "kv_format": ("K int8/token scale, V int8/32-dim scale" if vbits == 8 else
-                          "K int8/token scale, V int4/32-dim scale"), "splits": splits,
+            "kv_format": {kvq.KVQ_FORMAT_K8V4: "K int8/token scale, V int4/32-dim scale",
+                          kvq.KVQ_FORMAT_K8V8: "K int8/token scale, V int8/32-dim scale",
+                          kvq.KVQ_FORMAT_FP8: "K e4m3/token scale, V e4m3/32-dim scale"}[fmt],
+            "splits": splits,
             "pool_copies": len(caches), "parallelism": "single GPU",
         },
         "roofline": {
@@ -382,7 +385,7 @@ def main(argv=None):
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline: oracle on full steps, about 10 s")
-        dt, n_cpu, cores = cpu_baseline(wl, inp, window=win)
+        dt, n_cpu, cores = cpu_baseline(wl, inp, window=win, kv_format=fmt)
         res["cpu_baseline"] = {
             "value": round(step_bytes / dt / 1e9, 4),
             "unit": "GB/s",

@@ -102,9 +102,22 @@ size_t kvq_block_bytes(int32_t page_size, int32_t head_dim);
  *                      V code (t, d):  byte  16*D*tile + 512*w*(j/w) + 8*w*lane + 8*(j%w)
  *                                            + 4*((d/16)%2) + t%4   (int8)
  *                    (the two nibbles of a 4-bit byte become two bytes, 4 apart).
+ *   KVQ_FORMAT_FP8   K and V as 8-bit floating-point codes: the fp8 KV the replies to the same
+ *                    forum post find missing on their card.  Codes are OCP FP8 E4M3 (sign bit 7,
+ *                    exponent bits 6..3 with bias 7, mantissa bits 2..0; exponent 0 is
+ *                    subnormal, m * 2^-9; largest finite value 448; 0x7F and 0xFF are NaN and
+ *                    never produced).  The scale granularity is that of K8/V8 (one fp16 scale per
+ *                    token and KV head for K, one per 32 dims for V), with 448 in place of qmax:
+ *                    s = fp16_rne(absmax / 448.0f) (fp32 IEEE divide, saturated at 65504), and
+ *                    code = e4m3_rne(clamp(x / s, -448, 448)) with the divide in fp32 and the
+ *                    stored scale, rounded to the nearest E4M3 value, ties to the even
+ *                    mantissa; the sign bit is the quotient's (a negative value that rounds to
+ *                    zero is 0x80).  s == 0 gives code 0 for every element.  Dequantized:
+ *                    value(code) * s.  The byte layout and block_bytes are those of K8/V8.
  * kvq_decode_num_splits and kvq_decode_workspace_bytes do not depend on the format. */
 #define KVQ_FORMAT_K8V4 0
 #define KVQ_FORMAT_K8V8 1
+#define KVQ_FORMAT_FP8 2
 
 /* Block bytes of a format (0 for an unknown format or unsupported shape).  Host only. */
 size_t kvq_block_bytes_fmt(int32_t kv_format, int32_t page_size, int32_t head_dim);

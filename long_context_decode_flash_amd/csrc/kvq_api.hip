@@ -10,9 +10,12 @@ namespace {
 
 bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
 bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
-// bits per V code of a KV format, or 0 for an unknown format
+// bits per V code of a KV format (the fp8 format uses the 8-bit V layout), or 0 for an unknown
+// format
 int vbits_of(int32_t kv_format) {
-  return kv_format == KVQ_FORMAT_K8V4 ? 4 : kv_format == KVQ_FORMAT_K8V8 ? 8 : 0;
+  return kv_format == KVQ_FORMAT_K8V4 ? 4
+         : (kv_format == KVQ_FORMAT_K8V8 || kv_format == KVQ_FORMAT_FP8) ? 8
+                                                                          : 0;
 }
 
 // Workgroups (4 waves each) the decode grid aims for: one per CU of the 256.
@@ -124,7 +127,8 @@ int kvq_append_fmt(int32_t kv_format, void* pool, int32_t num_pages, int32_t pag
   if (n_tok == 0) return KVQ_OK;
   if (!k || !v || !slot_mapping) return KVQ_ERR_ARG;
   if ((long long)n_tok * num_kv_heads > (1LL << 33)) return KVQ_ERR_ARG;
-  kvq::AppendArgs a{(uint8_t*)pool, num_pages, page_size, num_kv_heads, vb, k, v, slot_mapping, n_tok};
+  kvq::AppendArgs a{(uint8_t*)pool, num_pages,    page_size, num_kv_heads, vb,
+                    kv_format == KVQ_FORMAT_FP8, k, v,         slot_mapping, n_tok};
   (void)hipGetLastError();  // start from a clean error state
   return kvq::launch_append(head_dim, a, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
@@ -199,6 +203,7 @@ int decode_impl(int32_t kv_format, const void* pool, int32_t num_pages, int32_t 
   a.page_size = page_size;
   a.num_kv_heads = num_kv_heads;
   a.vbits = vb;
+  a.fp8 = kv_format == KVQ_FORMAT_FP8;
   a.log2_page = __builtin_ctz((unsigned)page_size);
   a.q = q;
   a.page_table = page_table;

@@ -20,7 +20,7 @@ __device__ inline void copy16(uint8_t* dst, const uint8_t* src, int bytes, int l
   for (int o = 16 * lane; o < bytes; o += 16 * kWave) *(uint4*)(dst + o) = *(const uint4*)(src + o);
 }
 
-template <int D, int VB>
+template <int D, int VB, bool F8>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   constexpr int TB = (int)block_bytes(kTile, D, VB);  // one tile as a one-tile page
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[4][TB];
@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   if (whole) {
     uint8_t* st = s_tile[wv];
 #pragma unroll
-    for (int i = 0; i < kTokensPerWave; ++i) store_row<D, VB>(st, kTile, i, rv[i], lane);
+    for (int i = 0; i < kTokensPerWave; ++i) store_row<D, VB, F8>(st, kTile, i, rv[i], lane);
     const int page = (int)(s0 / P), tile = (int)(s0 % P) / kTile;
     uint8_t* blk = a.pool + ((size_t)page * a.num_kv_heads + h) * block_bytes(P, D, VB);
     copy16<D>(blk + (size_t)kTile * D * tile, st, kTile * D, lane);                                 // K codes
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     const long long slot = __builtin_amdgcn_readlane((int)my_slot, i);
     if (i < cnt && slot >= 0 && slot < pool_slots) {  // padding / out of pool: skip
       const int page = (int)(slot / P), s = (int)(slot % P);
-      store_row<D, VB>(a.pool + ((size_t)page * a.num_kv_heads + h) * block_bytes(P, D, VB), P, s, rv[i], lane);
+      store_row<D, VB, F8>(a.pool + ((size_t)page * a.num_kv_heads + h) * block_bytes(P, D, VB), P, s, rv[i], lane);
     }
   }
 }
@@ -76,21 +76,17 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 hipError_t launch_append(int head_dim, const AppendArgs& a, hipStream_t stream) {
   const long long groups = ((long long)a.n_tok + kTokensPerWave - 1) / kTokensPerWave;
   const long long items = groups * a.num_kv_heads;
-  const unsigned grid = (unsigned)((items + 3) / 4);
-  const bool v8 = a.vbits == 8;
-  switch (head_dim) {
-    case 64:
-      if (v8) hipLaunchKernelGGL((append_kernel<64, 8>), dim3(grid), dim3(256), 0, stream, a);
-      else hipLaunchKernelGGL((append_kernel<64, 4>), dim3(grid), dim3(256), 0, stream, a);
-      break;
-    case 128:
-      if (v8) hipLaunchKernelGGL((append_kernel<128, 8>), dim3(grid), dim3(256), 0, stream, a);
-      else hipLaunchKernelGGL((append_kernel<128, 4>), dim3(grid), dim3(256), 0, stream, a);
-      break;
-    case 256:
-      if (v8) hipLaunchKernelGGL((append_kernel<256, 8>), dim3(grid), dim3(256), 0, stream, a);
-      else hipLaunchKernelGGL((append_kernel<256, 4>), dim3(grid), dim3(256), 0, stream, a);
-      break;
+  const dim3 grid((unsigned)((items + 3) / 4)), block(256);
+  const int kind = a.fp8 ? 2 : a.vbits == 8 ? 1 : 0;  // fp8 / 8-bit / 4-bit V codes
+  switch (head_dim * 4 + kind) {
+#define KVQ_APPEND_CASE(D)                                                                      \
+  case 4 * D + 0: hipLaunchKernelGGL((append_kernel<D, 4, false>), grid, block, 0, stream, a); break; \
+  case 4 * D + 1: hipLaunchKernelGGL((append_kernel<D, 8, false>), grid, block, 0, stream, a); break; \
+  case 4 * D + 2: hipLaunchKernelGGL((append_kernel<D, 8, true>), grid, block, 0, stream, a); break;
+    KVQ_APPEND_CASE(64)
+    KVQ_APPEND_CASE(128)
+    KVQ_APPEND_CASE(256)
+#undef KVQ_APPEND_CASE
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -73,6 +73,23 @@ __device__ inline void i8x8_to_h2x4(uint32_t lo_w, uint32_t hi_w, uint32_t& lo02
   hi13 = as_u32(as_h2(((hi_w >> 8) & 0x00FF00FFu) ^ 0x64806480u) + off);
 }
 
+// The E4M3 form: lo_w / hi_w as for i8x8_to_h2x4, each byte an OCP E4M3 code.  Every E4M3
+// value (magnitudes 2^-9 .. 448) is an fp16 value, so the gfx950 converter (scale 1) is exact; a
+// byte permute first pairs tokens (0, 2) and (1, 3).
+template <bool HI_WORD>
+__device__ inline uint32_t e4m3x2_to_h2(uint32_t x) {
+  return as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, HI_WORD));
+}
+__device__ inline void f8x8_to_h2x4(uint32_t lo_w, uint32_t hi_w, uint32_t& lo02, uint32_t& lo13,
+                                    uint32_t& hi02, uint32_t& hi13) {
+  const uint32_t l = __builtin_amdgcn_perm(lo_w, lo_w, 0x03010200u);  // bytes (0, 2, 1, 3)
+  const uint32_t h = __builtin_amdgcn_perm(hi_w, hi_w, 0x03010200u);
+  lo02 = e4m3x2_to_h2<false>(l);
+  lo13 = e4m3x2_to_h2<true>(l);
+  hi02 = e4m3x2_to_h2<false>(h);
+  hi13 = e4m3x2_to_h2<true>(h);
+}
+
 // p0 * s0 and p1 * s1 (p fp32, s an fp16 half of sw0 / sw1 selected by SH) as fp16 hi + lo pairs:
 // hi = rne(p * s) and lo = rne(p * s - hi) straight from the exact products (v_fma_mix*), so the
 // two halves always belong together and hi + lo = p * s to about 2^-22.
@@ -329,31 +346,57 @@ __device__ inline void read_tile(TileRaw<D, VB>& r, const uint8_t* src, int lane
 //          sums of 2^(z - base) * (1, v);  it only moves up, in whole powers of two, when a block's
 //          largest logit and V scale would push p * v_scale past 2^15 (fp16 headroom), so most
 //          blocks rescale nothing and every rescale is exact.
-template <int D, int NB, int VB, bool WIN>
+template <int D, int NB, int VB, bool WIN, bool F8>
 __device__ __attribute__((always_inline)) inline void process_block(
-    TileRaw<D, VB> (&raw)[2], int blk, bool masked, float e5, const i32x4 (&qd)[NB][3][D / 64], const float (&cz)[NB],
+    TileRaw<D, VB> (&raw)[2], int blk, bool masked, float e5, const i32x4 (&qd)[NB][3][D / 64],
+    const u32x4 (&qw)[NB][D / 64][2], const float (&cz)[NB],
     const int (&first_tok)[NB], const int (&last_tok)[NB], int g, floatx4 (&acc)[NB][D / 16], float (&base)[NB],
     float (&l_run)[NB]) {
   constexpr int DB = D / 16;
   constexpr int NG = D / 32;
-  // ---- S^T = K Q^T on the int8 matrix cores, three digit planes of Q ----
+  // ---- S^T = K Q^T: int8 codes on the int8 matrix cores with three digit planes of Q; E4M3
+  // codes widened to fp16 (exactly) on the f16 matrix cores with Q's own fp16 values ----
   i32x4 sd[2][NB][3];
+  floatx4 sf[2][NB];
 #pragma unroll
   for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+    for (int nb = 0; nb < NB; ++nb) {
+      sf[tau][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int pc = 0; pc < 3; ++pc) sd[tau][nb][pc] = i32x4{0, 0, 0, 0};
+    }
 #pragma unroll
   for (int jj = 0; jj < D / 64; ++jj)
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
-      const i32x4 ka = __builtin_bit_cast(i32x4, raw[tau].k[jj]);
+      if constexpr (F8) {
+        // dword i of the lane's 16 codes holds dims 4i .. 4i+3: halves 0..7 and 8..15 pair with
+        // the query's two fp16 words of the same 16 dims
+        const u32x4 kc = raw[tau].k[jj];
+        uint32_t kh[8];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+        for (int i = 0; i < 4; ++i) {
+          kh[2 * i] = e4m3x2_to_h2<false>(kc[i]);
+          kh[2 * i + 1] = e4m3x2_to_h2<true>(kc[i]);
+        }
+        const half8 k0 = __builtin_bit_cast(half8, u32x4{kh[0], kh[1], kh[2], kh[3]});
+        const half8 k1 = __builtin_bit_cast(half8, u32x4{kh[4], kh[5], kh[6], kh[7]});
 #pragma unroll
-        for (int pc = 0; pc < 3; ++pc)
-          sd[tau][nb][pc] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka, qd[nb][pc][jj], sd[tau][nb][pc], 0, 0, 0);
+        for (int nb = 0; nb < NB; ++nb) {
+          sf[tau][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, __builtin_bit_cast(half8, qw[nb][jj][0]),
+                                                               sf[tau][nb], 0, 0, 0);
+          sf[tau][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, __builtin_bit_cast(half8, qw[nb][jj][1]),
+                                                               sf[tau][nb], 0, 0, 0);
+        }
+      } else {
+        const i32x4 ka = __builtin_bit_cast(i32x4, raw[tau].k[jj]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int pc = 0; pc < 3; ++pc)
+            sd[tau][nb][pc] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka, qd[nb][pc][jj], sd[tau][nb][pc], 0, 0, 0);
+      }
     }
   float ks[2][4];
 #pragma unroll
@@ -373,8 +416,13 @@ __device__ __attribute__((always_inline)) inline void process_block(
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int hm = (sd[tau][nb][0][e] << 8) + sd[tau][nb][1][e];  // |.| < 2^30: exact
-        const float sc = __builtin_fmaf((float)hm, 256.0f, (float)sd[tau][nb][2][e]);
+        float sc;
+        if constexpr (F8) {
+          sc = sf[tau][nb][e];
+        } else {
+          const int hm = (sd[tau][nb][0][e] << 8) + sd[tau][nb][1][e];  // |.| < 2^30: exact
+          sc = __builtin_fmaf((float)hm, 256.0f, (float)sd[tau][nb][2][e]);
+        }
         z[tau][e] = sc * (ks[tau][e] * cz[nb]);
       }
     if (masked) {  // wave-uniform: only the blocks at the end of a context
@@ -430,7 +478,9 @@ __device__ __attribute__((always_inline)) inline void process_block(
     uint32_t l02[2], l13[2], h02[2], h13[2];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
-      if constexpr (VB == 8)
+      if constexpr (F8)
+        f8x8_to_h2x4(raw[tau].v[2 * j], raw[tau].v[2 * j + 1], l02[tau], l13[tau], h02[tau], h13[tau]);
+      else if constexpr (VB == 8)
         i8x8_to_h2x4(raw[tau].v[2 * j], raw[tau].v[2 * j + 1], l02[tau], l13[tau], h02[tau], h13[tau]);
       else
         i4x8_to_h2x4(raw[tau].v[j], l02[tau], l13[tau], h02[tau], h13[tau]);
@@ -480,7 +530,7 @@ __device__ __attribute__((always_inline)) inline void process_block(
 // NSTAGE - 1 blocks are in flight while it computes one.  The waves merge through LDS into one
 // partial (the output itself when the context is a single piece).  WIN: a sliding window (the
 // pieces start at the first row's window start; pages may be a ring).
-template <int D, int NB, int VB, bool WIN>
+template <int D, int NB, int VB, bool WIN, bool F8>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   constexpr int DB = D / 16;
   constexpr int ROWS = 16 * NB;
@@ -618,7 +668,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     if (t < 0 || blk < g_blk0 || blk >= g_blk1 || ((blk - g_blk0) & (kWavesPerGroup - 1)) != w) continue;
     const int page = min(max(pt[entry(t >> lgP)], 0), a.num_pages - 1);
     const size_t row = (((size_t)b * a.n_new + j) * a.num_kv_heads + h) * D;
-    append_row<D, VB>(a.pool_rw + ((size_t)page * a.num_kv_heads + h) * bb, P, t & (P - 1), a.k_new + row,
+    append_row<D, VB, F8>(a.pool_rw + ((size_t)page * a.num_kv_heads + h) * bb, P, t & (P - 1), a.k_new + row,
                   a.v_new + row, lane);
   }
   chunk_count();
@@ -633,9 +683,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // balanced digits in [-128, 127] and |q * 2^F| < 2^22 for the row's largest |q|; exact for every
   // element within 2^12 of it, the rest rounded to the 2^-F grid. ----
   i32x4 qd[NB][3][D / 64];
-  float cz[NB];  // 2^-F * softmax_scale * log2(e)
+  float cz[NB];  // 2^-F * softmax_scale * log2(e); E4M3 keys: softmax_scale * log2(e)
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
+    if constexpr (F8) {  // the fp16 query words are the B operands as they are
+      cz[nb] = a.scale_log2;
+      continue;
+    }
     float amax = 0.0f;
 #pragma unroll
     for (int jj = 0; jj < D / 64; ++jj)
@@ -744,7 +798,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             __builtin_bit_cast(u16x2, vsw[0]), __builtin_bit_cast(u16x2, vsw[Stage<D, VB>::kTileBytes / 4]))));
         e5 = (float)((m >> 10) & 31);
       }
-      process_block<D, NB, VB, WIN>(raw, blk, masked, e5, qd, cz, first_tok, last_tok, g, acc, base, l_run);
+      process_block<D, NB, VB, WIN, F8>(raw, blk, masked, e5, qd, qw, cz, first_tok, last_tok, g, acc, base,
+                                        l_run);
     }
     c0 += CHUNK;
     if (c0 < g_blk1) {
@@ -857,19 +912,22 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a) {
   if (q == 0 && a.lse) a.lse[o] = den > 0.0f ? (mx + log2f(den)) * 0.69314718055994530942f : kNegInf;
 }
 
+template <int D, bool WIN, int VB, bool F8>
+void launch_attn_f(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t stream) {
+  if (a.rows <= 16)
+    hipLaunchKernelGGL((decode_kernel<D, 1, VB, WIN, F8>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<D, 2, VB, WIN, F8>), grid, block, 0, stream, a);
+}
+
 template <int D, bool WIN>
 void launch_attn(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t stream) {
-  if (a.vbits == 8) {
-    if (a.rows <= 16)
-      hipLaunchKernelGGL((decode_kernel<D, 1, 8, WIN>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((decode_kernel<D, 2, 8, WIN>), grid, block, 0, stream, a);
-  } else {
-    if (a.rows <= 16)
-      hipLaunchKernelGGL((decode_kernel<D, 1, 4, WIN>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((decode_kernel<D, 2, 4, WIN>), grid, block, 0, stream, a);
-  }
+  if (a.fp8)
+    launch_attn_f<D, WIN, 8, true>(a, grid, block, stream);
+  else if (a.vbits == 8)
+    launch_attn_f<D, WIN, 8, false>(a, grid, block, stream);
+  else
+    launch_attn_f<D, WIN, 4, false>(a, grid, block, stream);
 }
 
 template <int D>

@@ -34,6 +34,7 @@ struct AppendArgs {
   uint8_t* pool;
   int num_pages, page_size, num_kv_heads;
   int vbits;  // 4 or 8
+  int fp8;    // 1: K and V as OCP e4m3 codes (8-bit V layout)
   const float* k;
   const float* v;
   const int32_t* slots;
@@ -44,6 +45,7 @@ struct DecodeArgs {
   const uint8_t* pool;
   int num_pages, page_size, num_kv_heads;
   int vbits;  // 4 or 8
+  int fp8;    // 1: K and V as OCP e4m3 codes (8-bit V layout)
   int log2_page;  // page_size = 1 << log2_page
   const uint16_t* q;
   const int32_t* page_table;

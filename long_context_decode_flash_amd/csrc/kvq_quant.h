@@ -1,4 +1,4 @@
-// kvq_quant.h — the K8/V4 (and K8/V8) quantizer of one (token, KV head) row, written into its
+// kvq_quant.h — the K8/V4 (and K8/V8, fp8) quantizer of one (token, KV head) row, written into its
 // cache slot by one 64-lane wave.  Shared by the append kernel and the decode kernel's fused
 // append, so both write the same bytes.
 //
@@ -37,6 +37,29 @@ __device__ inline int quantize_one(float x, float s, float qmax) {
   return (int)c;
 }
 
+// OCP FP8 E4M3 code of y, |y| <= 448, rounded to the nearest E4M3 value with ties to the even
+// mantissa.  Below 2^-6 the values are the multiples of 2^-9 (code = y * 2^9, exact scaling,
+// then rint); from 2^-6 on the code is the fp32 exponent and top three mantissa bits, rounded to
+// nearest even on the 20 dropped bits (a carry moves into the exponent), rebased from bias 127 to
+// bias 7.  The sign bit is y's.
+__device__ inline uint32_t e4m3_rne(float y) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t mag;
+  if (a < 0x3C800000u)  // |y| < 2^-6: subnormal codes 0..7, and 8 (= 2^-6) when rounding up
+    mag = (uint32_t)__builtin_rintf(__builtin_bit_cast(float, a) * 512.0f);
+  else
+    mag = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
+  return sign | mag;
+}
+
+__device__ inline uint32_t quantize_one_f8(float x, float s) {
+  if (s == 0.0f) return 0u;
+  const float y = x / s;  // IEEE divide
+  return e4m3_rne(fminf(fmaxf(y, -448.0f), 448.0f));
+}
+
 // A wave's share of one token's K and V rows: lane l holds dims E*l .. E*l + E-1.
 template <int D>
 struct RowVals {
@@ -57,9 +80,11 @@ __device__ __attribute__((always_inline)) inline RowVals<D> load_row(const float
 }
 
 // Quantize one token's K and V rows (already in the wave's registers) into slot s of the
-// (page, KV head) block at blk, with VB-bit V codes.  Called by all 64 lanes of a wave.
-template <int D, int VB = 4>
+// (page, KV head) block at blk, with VB-bit V codes; F8 (with VB = 8): K and V as E4M3 codes
+// at 448 in place of qmax.  Called by all 64 lanes of a wave.
+template <int D, int VB = 4, bool F8 = false>
 __device__ __attribute__((always_inline)) inline void store_row(uint8_t* blk, int P, int s, const RowVals<D>& r, int lane) {
+  static_assert(!F8 || VB == 8, "fp8 codes use the 8-bit layout");
   constexpr int E = RowVals<D>::E;
   const int tile = s / kTile, t = s % kTile;
   const int d0 = lane * E;
@@ -72,10 +97,11 @@ __device__ __attribute__((always_inline)) inline void store_row(uint8_t* blk, in
   for (int e = 0; e < E; ++e) ka = fmaxf(ka, fabsf(kx[e]));
   ka = wave_max(ka, kWave);
   float ks;
-  const uint16_t ks_bits = group_scale(ka, 127.0f, &ks);
+  const uint16_t ks_bits = group_scale(ka, F8 ? 448.0f : 127.0f, &ks);
   uint32_t kpacked = 0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) kpacked |= (uint32_t)(quantize_one(kx[e], ks, 127.0f) & 0xFF) << (8 * e);
+  for (int e = 0; e < E; ++e)
+    kpacked |= (F8 ? quantize_one_f8(kx[e], ks) : (uint32_t)(quantize_one(kx[e], ks, 127.0f) & 0xFF)) << (8 * e);
   // K code (t, d) at 16*D*tile + 256*(d/16) + 16*t + d%16; E consecutive dims stay in one chunk
   uint8_t* kdst = blk + (size_t)16 * D * tile + 256 * (d0 / 16) + 16 * t + d0 % 16;
   if constexpr (E == 4) {
@@ -88,7 +114,7 @@ __device__ __attribute__((always_inline)) inline void store_row(uint8_t* blk, in
   if (lane == 0) *(uint16_t*)(blk + k_scales_at(P, D) + 2 * s) = ks_bits;
 
   // ---- V: one scale per 32 dims (qmax 7, or 127 for 8-bit codes), 32/E lanes per group ----
-  constexpr float vqmax = VB == 8 ? 127.0f : 7.0f;
+  constexpr float vqmax = F8 ? 448.0f : VB == 8 ? 127.0f : 7.0f;
   float va = 0.0f;
 #pragma unroll
   for (int e = 0; e < E; ++e) va = fmaxf(va, fabsf(vx[e]));
@@ -106,7 +132,7 @@ __device__ __attribute__((always_inline)) inline void store_row(uint8_t* blk, in
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int vlane = 16 * (t / 4) + (d0 + e) % 16;
-      vbase[8 * w * vlane] = (uint8_t)(quantize_one(vx[e], vsc, vqmax) & 0xFF);
+      vbase[8 * w * vlane] = F8 ? (uint8_t)quantize_one_f8(vx[e], vsc) : (uint8_t)(quantize_one(vx[e], vsc, vqmax) & 0xFF);
     }
     return;
   }
@@ -132,10 +158,10 @@ __device__ __attribute__((always_inline)) inline void store_row(uint8_t* blk, in
 }
 
 // Load and quantize one token's rows (krow/vrow point at the rows' first values) into slot s.
-template <int D, int VB = 4>
+template <int D, int VB = 4, bool F8 = false>
 __device__ inline void append_row(uint8_t* blk, int P, int s, const float* krow_base,
                                   const float* vrow_base, int lane) {
-  store_row<D, VB>(blk, P, s, load_row<D>(krow_base, vrow_base, lane), lane);
+  store_row<D, VB, F8>(blk, P, s, load_row<D>(krow_base, vrow_base, lane), lane);
 }
 
 }  // namespace kvq

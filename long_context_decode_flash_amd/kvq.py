@@ -23,7 +23,8 @@ KVQ_ERR_HIP = -4
 KVQ_MAX_STEP_TOKENS = 64
 KVQ_FORMAT_K8V4 = 0  # 4-bit V codes
 KVQ_FORMAT_K8V8 = 1  # 8-bit V codes
-FORMATS = {"k8v4": KVQ_FORMAT_K8V4, "k8v8": KVQ_FORMAT_K8V8}
+KVQ_FORMAT_FP8 = 2   # K and V as OCP e4m3 codes, the 8-bit V layout
+FORMATS = {"k8v4": KVQ_FORMAT_K8V4, "k8v8": KVQ_FORMAT_K8V8, "fp8": KVQ_FORMAT_FP8}
 
 _lock = threading.Lock()
 _lib = None

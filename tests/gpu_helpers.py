@@ -33,8 +33,10 @@ def to_dev(a: np.ndarray):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-# KV formats: the library's format code and the oracle's bits per V code
-VBITS = {0: 4, 1: 8}
+# KV formats: the library's format code and the oracle's bits per V code (fp8 codes use the
+# 8-bit V layout)
+VBITS = {0: 4, 1: 8, 2: 8}
+FORMAT_IDS = {0: "k8v4", 1: "k8v8", 2: "fp8"}
 
 
 def gpu_cache(inp: W.Inputs, kv_format=0):
@@ -80,12 +82,12 @@ def oracle_fill(inp: W.Inputs, kv_format=0):
     pool = oracle.new_pool(wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim, vb)
     if wl.n_new and np.all(inp.seq_lens == wl.seq_len):
         oracle.append(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
-                      *inp.prefill(), vbits=vb)
+                      *inp.prefill(), kv_format=kv_format)
         oracle.append(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
-                      *inp.step_tokens(), vbits=vb)
+                      *inp.step_tokens(), kv_format=kv_format)
     else:
         oracle.append(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
-                      *inp.all_tokens(), vbits=vb)
+                      *inp.all_tokens(), kv_format=kv_format)
     return pool
 
 
@@ -94,7 +96,7 @@ def oracle_decode(inp: W.Inputs, pool, select=None, softmax_scale=0.0, kv_format
     return oracle.decode_attn(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
                               inp.q_bits, inp.page_table, inp.seq_lens, wl.n_rows,
                               wl.n_q_heads, softmax_scale=softmax_scale, select=select,
-                              vbits=VBITS[kv_format])
+                              kv_format=kv_format)
 
 
 @functools.lru_cache(maxsize=2)

@@ -111,15 +111,21 @@ def test_append_validation(lib):
 
 
 def test_kv_formats(lib):
-    """K8/V4 and K8/V8 block sizes; an unknown format is refused before any HIP call."""
+    """K8/V4, K8/V8 and fp8 block sizes (fp8 has the K8/V8 layout); an unknown format is
+    refused before any HIP call."""
     assert lib.kvq_block_bytes_fmt(kvq.KVQ_FORMAT_K8V4, 64, 256) == 64 * (256 + 2 + 128 + 16)
     assert lib.kvq_block_bytes_fmt(kvq.KVQ_FORMAT_K8V8, 64, 256) == 64 * (2 * 256 + 2 + 16)
     assert lib.kvq_block_bytes_fmt(kvq.KVQ_FORMAT_K8V8, 16, 64) == 16 * (2 * 64 + 2 + 4)
     assert lib.kvq_block_bytes(64, 256) == lib.kvq_block_bytes_fmt(kvq.KVQ_FORMAT_K8V4, 64, 256)
-    assert lib.kvq_block_bytes_fmt(2, 64, 256) == 0
+    for P, D in ((64, 256), (16, 64), (32, 128)):
+        assert lib.kvq_block_bytes_fmt(kvq.KVQ_FORMAT_FP8, P, D) == \
+            lib.kvq_block_bytes_fmt(kvq.KVQ_FORMAT_K8V8, P, D)
+    assert lib.kvq_block_bytes_fmt(3, 64, 256) == 0
     assert lib.kvq_block_bytes_fmt(-1, 64, 256) == 0
-    assert lib.kvq_append_fmt(2, FAKE, 4, 16, 1, 64, FAKE, FAKE, FAKE, 1, None) == \
+    assert lib.kvq_append_fmt(3, FAKE, 4, 16, 1, 64, FAKE, FAKE, FAKE, 1, None) == \
         kvq.KVQ_ERR_UNSUPPORTED
+    assert lib.kvq_append_fmt(kvq.KVQ_FORMAT_FP8, FAKE, 4, 16, 1, 64, FAKE, FAKE, FAKE, 0,
+                              None) == kvq.KVQ_OK
     assert lib.kvq_append_fmt(kvq.KVQ_FORMAT_K8V8, FAKE, 4, 16, 1, 64, FAKE, FAKE, FAKE, 0,
                               None) == kvq.KVQ_OK
     assert lib.kvq_decode_attn_fmt(7, FAKE, 8, 16, 2, 64, FAKE, FAKE, FAKE, 1, 1, 4, 8, 100,

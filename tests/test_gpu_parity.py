@@ -57,7 +57,46 @@ def test_append_edge_rows_bit_exact():
         assert np.array_equal(got, inp_pool), (P, D, Hkv, np.flatnonzero(got != inp_pool)[:8])
 
 
-@pytest.mark.parametrize("kv_format", [0, 1], ids=["k8v4", "k8v8"])
+def test_append_fp8_rounding_edges_bit_exact():
+    """fp8 codes at the edges of E4M3 rounding, against the oracle's encoder: with a K row's
+    absmax 448 the scale is exactly 1, so each value is its own quotient: exact midpoints
+    between normal neighbours (ties go to the even mantissa), midpoints between subnormals and
+    at the subnormal/normal edge, negative values that round to zero (code 0x80), the largest
+    value; plus zero, tiny and huge rows and V groups of mixed magnitudes."""
+    H.say("[append fp8 edges]")
+    rng = np.random.default_rng(79)
+    ties = np.array([1.0625, 1.1875, 1.3125, 3.75 + 0.125, 0.5 * 2.0 ** -9, 1.5 * 2.0 ** -9,
+                     7.5 * 2.0 ** -9, 2.0 ** -6 + 2.0 ** -10, 2.0 ** -6 + 3 * 2.0 ** -10, 240.0 + 8.0,
+                     416.0 + 8.0, 448.0, 0.25 * 2.0 ** -9, 0.75 * 2.0 ** -9], np.float64)
+    for P, D, Hkv in ((16, 64, 2), (64, 256, 1), (32, 128, 3)):
+        pages = 6
+        n = 12
+        k = rng.standard_normal((n, Hkv, D)).astype(np.float32)
+        v = rng.standard_normal((n, Hkv, D)).astype(np.float32)
+        k[0] = 0.0
+        v[0] = 0.0
+        k[1] *= np.float32(1e-6)
+        v[1] *= np.float32(1e-7)
+        k[2] *= np.float32(1e7)
+        v[2] *= np.float32(1e6)
+        row = np.resize(np.concatenate([ties, -ties]), D).astype(np.float32)
+        row[0] = 448.0
+        k[3] = row
+        v[3] = row
+        v[4, :, :] = np.float32(3.5)
+        v[4, :, ::32] = np.float32(448.0)
+        slots = rng.choice(pages * P, n, replace=False).astype(np.int32)
+        slots[5] = -1
+        slots[6] = pages * P + 3
+        ref = H.oracle.new_pool(pages, P, Hkv, D, 8)
+        H.oracle.append(ref, pages, P, Hkv, D, k, v, slots, kv_format=2)
+        cache = H.kvq().PagedCache.allocate(pages, P, Hkv, D, kv_format=2)
+        H.gpu_append(cache, k, v, slots)
+        got = cache.pool.cpu().numpy()
+        assert np.array_equal(got, ref), (P, D, Hkv, np.flatnonzero(got != ref)[:8])
+
+
+@pytest.mark.parametrize("kv_format", [0, 1, 2], ids=["k8v4", "k8v8", "fp8"])
 def test_append_tile_and_row_paths_bit_exact(kv_format):
     """Groups of 16 tokens that fill one tile in order are written as whole tiles; any other
     group token by token.  One call mixes both: whole tiles, a run starting mid-tile, a tile with
@@ -86,7 +125,7 @@ def test_append_tile_and_row_paths_bit_exact(kv_format):
         k[2] = 0.0
         v[50] *= np.float32(1e-6)
         ref = H.oracle.new_pool(pages, P, Hkv, D, vb)
-        H.oracle.append(ref, pages, P, Hkv, D, k, v, slots, vbits=vb)
+        H.oracle.append(ref, pages, P, Hkv, D, k, v, slots, kv_format=kv_format)
         cache = H.kvq().PagedCache.allocate(pages, P, Hkv, D, kv_format=kv_format)
         H.gpu_append(cache, k, v, slots)
         got = cache.pool.cpu().numpy()
@@ -231,45 +270,65 @@ def test_decode_batch_equals_each_sequence_alone():
         assert np.array_equal(o1[0], out[b]) and np.array_equal(l1[0], lse[b])
 
 
-# ------------------------------------------------------------------ K8/V8 ---------------
-# 8-bit V codes (KVQ_FORMAT_K8V8): the same bar, pool bytes bit-exact and outputs within 2e-3.
+# ------------------------------------------------------------------ K8/V8 and fp8 ----------
+# 8-bit V codes (KVQ_FORMAT_K8V8) and E4M3 K and V codes (KVQ_FORMAT_FP8): the same bar, pool
+# bytes bit-exact and outputs within 2e-3.
 
 V8_SMALL = SMALL + [W.custom(n_seq=2, seq_lens=(700, 333), num_kv_heads=2, n_q_heads=12,
                              head_dim=128, page_size=32, n_rows=2, seed=61, name="d128").wl,
                     W.custom(n_seq=1, seq_lens=(300,), num_kv_heads=1, n_q_heads=4,
                              head_dim=64, page_size=16, n_rows=1, seed=300, name="d64_ragged").wl]
+FMT8 = pytest.mark.parametrize("kv_format", [1, 2], ids=["k8v8", "fp8"])
 
 
+@FMT8
 @pytest.mark.parametrize("wl", V8_SMALL, ids=lambda w: w.name)
-def test_v8_decode_small_every_output(wl):
-    H.say(f"[k8v8 small] {wl.name} L={wl.seq_len}")
+def test_v8_decode_small_every_output(wl, kv_format):
+    H.say(f"[{H.FORMAT_IDS[kv_format]} small] {wl.name} L={wl.seq_len}")
     inp = W.generate(wl)
-    cache = H.gpu_fill(inp, kv_format=1)
-    pool_ref = H.oracle_fill(inp, 1)
+    cache = H.gpu_fill(inp, kv_format=kv_format)
+    pool_ref = H.oracle_fill(inp, kv_format)
     assert np.array_equal(cache.pool.cpu().numpy(), pool_ref)
     for splits in (0, 3):
         out, lse = H.gpu_decode(inp, cache, num_splits=splits)
-        out_r, lse_r = H.oracle_decode(inp, pool_ref, kv_format=1)
+        out_r, lse_r = H.oracle_decode(inp, pool_ref, kv_format=kv_format)
         assert H.report(f"  out (splits {splits})", out, out_r) <= H.TOL_ABS
+        assert H.report(f"  out rel (splits {splits})", out, out_r) <= 1e-3 * np.max(np.abs(out_r))
         np.testing.assert_allclose(lse, lse_r, rtol=0, atol=1e-4)
 
 
-def test_v8_step_equals_append_then_decode():
-    """kvq_decode_step in K8/V8: the same pool bytes and outputs as kvq_append followed by
-    kvq_decode_attn, and the oracle's."""
+@FMT8
+def test_v8_peaked_attention(kv_format):
+    """Queries scaled up so the softmax concentrates on few tokens and outputs are O(1)."""
+    wl = W.scaled(W.WORKLOADS["ctx184k_c2"], 611, name="c2_611_peaked", q_scale=8.0)
+    H.say(f"[{H.FORMAT_IDS[kv_format]} peaked] {wl.name}")
+    inp = W.generate(wl)
+    cache = H.gpu_fill(inp, kv_format=kv_format)
+    pool_ref = H.oracle_fill(inp, kv_format)
+    out, lse = H.gpu_decode(inp, cache)
+    out_r, lse_r = H.oracle_decode(inp, pool_ref, kv_format=kv_format)
+    mx = H.report("  out", out, out_r)
+    assert mx <= H.TOL_ABS and mx <= 1e-3 * np.max(np.abs(out_r))
+    np.testing.assert_allclose(lse, lse_r, rtol=0, atol=1e-4)
+
+
+@FMT8
+def test_v8_step_equals_append_then_decode(kv_format):
+    """kvq_decode_step in an 8-bit format: the same pool bytes and outputs as kvq_append
+    followed by kvq_decode_attn, and the oracle's."""
     import torch
-    H.say("[k8v8 step]")
+    H.say(f"[{H.FORMAT_IDS[kv_format]} step]")
     kvq = H.kvq()
     inp = W.custom(n_seq=1, seq_lens=(1154,), num_kv_heads=4, n_q_heads=24, head_dim=256,
                    page_size=64, n_rows=4, seed=62)
     wl = inp.wl
     n_new = 4
     pre, new_flat, k_new, v_new = inp.ragged_split(n_new)
-    a = H.gpu_cache(inp, 1)
+    a = H.gpu_cache(inp, kv_format)
     H.gpu_append(a, *pre)
     H.gpu_append(a, *new_flat)
     out_a, lse_a = H.gpu_decode(inp, a, num_splits=7)
-    b = H.gpu_cache(inp, 1)
+    b = H.gpu_cache(inp, kv_format)
     H.gpu_append(b, *pre)
     q = H.to_dev(inp.q_bits).view(torch.float16)
     out_b, lse_b = kvq.decode_step(b, H.to_dev(k_new), H.to_dev(v_new), q, H.to_dev(inp.page_table),
@@ -277,23 +336,23 @@ def test_v8_step_equals_append_then_decode():
     torch.cuda.synchronize()
     assert np.array_equal(a.pool.cpu().numpy(), b.pool.cpu().numpy())
     assert np.array_equal(out_a, out_b.cpu().numpy()) and np.array_equal(lse_a, lse_b.cpu().numpy())
-    out_r, _ = H.oracle_decode(inp, H.oracle_fill(inp, 1), kv_format=1)
+    out_r, _ = H.oracle_decode(inp, H.oracle_fill(inp, kv_format), kv_format=kv_format)
     assert H.report("  out", out_a, out_r) <= H.TOL_ABS
 
 
-def test_v8_full_size_headline():
-    """The 184K-token two-sequence workload in K8/V8 with the automatic plan: the whole pool
-    bit-exact, sampled rows against the oracle."""
-    H.say("[k8v8 full] ctx184k_c2")
+@FMT8
+def test_v8_full_size_headline(kv_format):
+    """The 184K-token two-sequence workload in an 8-bit format with the automatic plan: the
+    whole pool bit-exact, sampled rows against the oracle."""
+    H.say(f"[{H.FORMAT_IDS[kv_format]} full] ctx184k_c2")
     inp = W.generate(W.WORKLOADS["ctx184k_c2"])
-    wl = inp.wl
-    pool_ref = H.oracle_fill(inp, 1)
-    cache = H.gpu_fill(inp, kv_format=1)
+    pool_ref = H.oracle_fill(inp, kv_format)
+    cache = H.gpu_fill(inp, kv_format=kv_format)
     got = cache.pool.cpu().numpy()
     assert np.array_equal(got, pool_ref), np.flatnonzero(got != pool_ref)[:8]
     out, lse = H.gpu_decode(inp, cache)
     sel = [(0, 0, 0), (1, 0, 23), (0, 0, 11), (1, 0, 6)]
-    out_r, lse_r = H.oracle_decode(inp, pool_ref, select=sel, kv_format=1)
+    out_r, lse_r = H.oracle_decode(inp, pool_ref, select=sel, kv_format=kv_format)
     got = np.stack([out[b, i, hq] for b, i, hq in sel])
     assert H.report("  out", got, out_r) <= H.TOL_ABS
     np.testing.assert_allclose(np.array([lse[b, i, hq] for b, i, hq in sel]), lse_r, rtol=0, atol=1e-4)

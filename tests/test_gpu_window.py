@@ -13,11 +13,11 @@ from tests.gpu_helpers import (TOL_ABS, gpu_append, gpu_cache, kvq, oracle, repo
 pytestmark = pytest.mark.gpu
 
 
-def _oracle_pool(inp, k, v, slots, vb):
+def _oracle_pool(inp, k, v, slots, kf):
     wl = inp.wl
-    pool = oracle.new_pool(wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim, vb)
+    pool = oracle.new_pool(wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim, VBITS[kf])
     oracle.append(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim, k, v, slots,
-                  vbits=vb)
+                  kv_format=kf)
     return pool
 
 
@@ -31,11 +31,11 @@ def _run(inp, cache, table, window, ring, num_splits=0, msl=None, kv_format=0):
     return out.cpu().numpy(), lse.cpu().numpy()
 
 
-def _ref(inp, pool, table, window, ring, vb, select=None):
+def _ref(inp, pool, table, window, ring, kf, select=None):
     wl = inp.wl
     return oracle.decode_attn(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
                               inp.q_bits, table, inp.seq_lens, wl.n_rows, wl.n_q_heads,
-                              select=select, vbits=vb, window=window, ring_pages=ring)
+                              select=select, kv_format=kf, window=window, ring_pages=ring)
 
 
 def _check(tag, out, lse, ref_out, ref_lse):
@@ -55,20 +55,20 @@ LINEAR_CASES = [
 ]
 
 
-@pytest.mark.parametrize("kv_format", [0, 1])
+@pytest.mark.parametrize("kv_format", [0, 1, 2], ids=["k8v4", "k8v8", "fp8"])
 @pytest.mark.parametrize("case", range(len(LINEAR_CASES)))
 def test_window_linear_table_every_output(case, kv_format):
     n_seq, lens, hkv, hq, D, P, R, windows = LINEAR_CASES[case]
-    vb = VBITS[kv_format]
+    kf = kv_format
     say(f"[window linear] case {case} fmt {kv_format}: lens {lens} D {D} P {P} R {R}")
     inp = W.custom(n_seq=n_seq, seq_lens=lens, num_kv_heads=hkv, n_q_heads=hq, head_dim=D,
                    page_size=P, n_rows=R, seed=300 + case)
     k, v, slots = inp.all_tokens()
-    pool = _oracle_pool(inp, k, v, slots, vb)
+    pool = _oracle_pool(inp, k, v, slots, kf)
     cache = gpu_cache(inp, kv_format)
     gpu_append(cache, k, v, slots)
     for window in windows:
-        ref_out, ref_lse = _ref(inp, pool, inp.page_table, window, 0, vb)
+        ref_out, ref_lse = _ref(inp, pool, inp.page_table, window, 0, kf)
         for splits in (0, 1, 3):
             out, lse = _run(inp, cache, inp.page_table, window, 0, splits)
             _check(f"case {case} fmt {kv_format} W {window} splits {splits}", out, lse,
@@ -84,11 +84,11 @@ RING_CASES = [
 ]
 
 
-@pytest.mark.parametrize("kv_format", [0, 1])
+@pytest.mark.parametrize("kv_format", [0, 1, 2], ids=["k8v4", "k8v8", "fp8"])
 @pytest.mark.parametrize("case", range(len(RING_CASES)))
 def test_window_ring_every_output(case, kv_format):
     n_seq, lens, hkv, hq, D, P, R, window, ring = RING_CASES[case]
-    vb = VBITS[kv_format]
+    kf = kv_format
     say(f"[window ring] case {case} fmt {kv_format}: lens {lens} D {D} P {P} R {R} W {window} "
         f"ring {ring}")
     # the pool holds only the rings; positions run far past the ring table
@@ -96,22 +96,22 @@ def test_window_ring_every_output(case, kv_format):
                    page_size=P, n_rows=R, seed=400 + case)
     table, (k, v, slots) = inp.ring(ring)
     assert int(inp.seq_lens.max()) > table.shape[1] * P
-    pool = _oracle_pool(inp, k, v, slots, vb)
+    pool = _oracle_pool(inp, k, v, slots, kf)
     cache = gpu_cache(inp, kv_format)
     gpu_append(cache, k, v, slots)
-    ref_out, ref_lse = _ref(inp, pool, table, window, ring, vb)
+    ref_out, ref_lse = _ref(inp, pool, table, window, ring, kf)
     for splits in (0, 1, 2):
         out, lse = _run(inp, cache, table, window, ring, splits)
         _check(f"ring case {case} fmt {kv_format} splits {splits}", out, lse, ref_out, ref_lse)
 
 
-@pytest.mark.parametrize("kv_format", [0, 1])
+@pytest.mark.parametrize("kv_format", [0, 1, 2], ids=["k8v4", "k8v8", "fp8"])
 def test_window_ring_fused_step(kv_format):
     """kvq_decode_step_win on a ring: the step's tokens overwrite the ring slots of tokens a
     ring length earlier; the pool bytes match the oracle's append of the same history, and the
     outputs its windowed attention."""
     torch = torch_mod()
-    vb = VBITS[kv_format]
+    kf = kv_format
     R, n_new, window, ring, P = 4, 4, 200, 6, 64
     inp = W.custom(n_seq=2, seq_lens=(4099, 1090), num_kv_heads=4, n_q_heads=24, head_dim=256,
                    page_size=P, n_rows=R, seed=511)
@@ -128,10 +128,10 @@ def test_window_ring_fused_step(kv_format):
         ks.append(inp.k[b, L - n_new:L])
         vs.append(inp.v[b, L - n_new:L])
         ss.append(inp.ring_slots(table, ring, b, L - n_new, L))
-    pool = _oracle_pool(inp, k0, v0, s0, vb)
+    pool = _oracle_pool(inp, k0, v0, s0, kf)
     oracle.append(pool, wl.pool_pages, P, 4, 256, np.concatenate(ks), np.concatenate(vs),
-                  np.concatenate(ss), vbits=vb)
-    ref_out, ref_lse = _ref(inp, pool, table, window, ring, vb)
+                  np.concatenate(ss), kv_format=kf)
+    ref_out, ref_lse = _ref(inp, pool, table, window, ring, kf)
     for splits in (0, 1, 3):
         say(f"[window ring step] fmt {kv_format} splits {splits}")
         cache = gpu_cache(inp, kv_format)
@@ -159,7 +159,7 @@ def test_window_full_size_sampled_rows():
     out, lse = _run(inp, cache, inp.page_table, window, 0, msl=wl.seq_len)
     rng = np.random.default_rng(5)
     sel = [(b, 0, int(h)) for b in range(wl.n_seq) for h in rng.choice(wl.n_q_heads, 3, False)]
-    ref_out, ref_lse = _ref(inp, pool, inp.page_table, window, 0, 4, select=sel)
+    ref_out, ref_lse = _ref(inp, pool, inp.page_table, window, 0, 0, select=sel)
     got = np.stack([out[b, i, h] for b, i, h in sel])
     got_lse = np.array([lse[b, i, h] for b, i, h in sel])
     _check("ctx184k_c2 window 65536 sampled", got, got_lse, ref_out, ref_lse)
