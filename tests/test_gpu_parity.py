@@ -358,6 +358,46 @@ def test_v8_full_size_headline(kv_format):
     np.testing.assert_allclose(np.array([lse[b, i, hq] for b, i, hq in sel]), lse_r, rtol=0, atol=1e-4)
 
 
+@pytest.mark.parametrize("kv_format", [0, 1, 2], ids=["k8v4", "k8v8", "fp8"])
+def test_decode_unwritten_slots_hold_junk(kv_format):
+    """Slots no token was appended to hold 0xFF bytes (NaN scales, NaN E4M3 codes): the ragged
+    ends of the contexts and the slots before a window start read such bytes into the staged
+    blocks, and the outputs must still match the oracle's."""
+    import torch
+    H.say(f"[junk slots] {H.FORMAT_IDS[kv_format]}")
+    for lens, D, P, R, hkv, hq in (((300, 77), 256, 64, 4, 4, 24), ((333,), 64, 16, 1, 1, 4),
+                                   ((515, 100), 128, 32, 2, 2, 12)):
+        inp = W.custom(n_seq=len(lens), seq_lens=lens, num_kv_heads=hkv, n_q_heads=hq,
+                       head_dim=D, page_size=P, n_rows=R, seed=90 + D)
+        cache = H.gpu_cache(inp, kv_format)
+        cache.pool.fill_(0xFF)
+        torch.cuda.synchronize()
+        k, v, slots = inp.all_tokens()
+        H.gpu_append(cache, k, v, slots)
+        pool_ref = H.oracle_fill(inp, kv_format)
+        for splits in (0, 3):
+            out, lse = H.gpu_decode(inp, cache, num_splits=splits)
+            out_r, lse_r = H.oracle_decode(inp, pool_ref, kv_format=kv_format)
+            assert np.all(np.isfinite(out)), "non-finite output"
+            assert H.report(f"  D {D} splits {splits}", out, out_r) <= H.TOL_ABS
+            np.testing.assert_allclose(lse, lse_r, rtol=0, atol=1e-4)
+        # a window whose start falls inside a block: the slots before it are real tokens here,
+        # and the junk beyond the ends is read as above
+        q = H.to_dev(inp.q_bits).view(torch.float16)
+        for window in (45, 200):
+            out, lse = H.kvq().decode_attn(cache, q, H.to_dev(inp.page_table),
+                                           H.to_dev(inp.seq_lens), int(max(lens)),
+                                           window=window)
+            torch.cuda.synchronize()
+            wl = inp.wl
+            out_r, lse_r = H.oracle.decode_attn(pool_ref, wl.pool_pages, P, hkv, D, inp.q_bits,
+                                                inp.page_table, inp.seq_lens, R, hq,
+                                                kv_format=kv_format, window=window)
+            got = out.cpu().numpy()
+            assert np.all(np.isfinite(got)), "non-finite output"
+            assert H.report(f"  D {D} window {window}", got, out_r) <= H.TOL_ABS
+
+
 # ------------------------------------------------------------------ decode, full size ----
 
 @pytest.mark.parametrize("name", list(W.WORKLOADS))
