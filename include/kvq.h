@@ -50,6 +50,9 @@ extern "C" {
 #define KVQ_MAX_ROWS_PER_KV 32
 #define KVQ_MAX_N_ROWS      4
 #define KVQ_MAX_STEP_TOKENS 64
+/* chunked prefill (kvq_prefill_attn): chunk positions per sequence, and chunk * G rows per KV head */
+#define KVQ_MAX_CHUNK        8192
+#define KVQ_MAX_PREFILL_ROWS 65536
 
 /* ---- quantization (defined by this library; the pages give only "K8/V4") ---------------
  * Per token and KV head, with inputs in fp32:
@@ -282,6 +285,41 @@ int32_t kvq_decode_num_splits_win(int32_t n_seq, int32_t num_kv_heads, int32_t m
 size_t kvq_decode_workspace_bytes_win(int32_t n_seq, int32_t n_rows, int32_t n_q_heads,
                                       int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
                                       int32_t window, int32_t num_splits_request);
+
+/* ---- kvq_prefill_attn: chunked-prefill attention -------------------------------------------
+ * The forum post's engine prefills prompts in chunks of 1,024 tokens (一、部署, launch-flag table,
+ * --prefill-chunk 1024) and names prefill as the cost behind the time to first token (二、测评).
+ * After a chunk's tokens are appended (kvq_append), every position of the chunk attends
+ * causally to the cache up to itself.  For sequence b with L = seq_lens[b] tokens, the last
+ * `chunk` of them being the chunk, position i (0 <= i < chunk) sees tokens 0 .. L - chunk + i:
+ * the definition of kvq_decode_attn with n_rows = chunk, for any chunk up to KVQ_MAX_CHUNK.
+ *   q             fp16 bits [n_seq][chunk][n_q_heads][head_dim], 16-byte aligned.
+ *   out           fp32 [n_seq][chunk][n_q_heads][head_dim], 16-byte aligned; lse (nullable) fp32
+ *                 [n_seq][chunk][n_q_heads], natural log, of the scaled logits.  A position that
+ *                 sees no token (L - chunk + i < 0) gets out = 0 and lse = -inf.
+ *   chunk         1 .. KVQ_MAX_CHUNK, and chunk * n_q_heads / num_kv_heads <= KVQ_MAX_PREFILL_ROWS.
+ *   num_splits    0 = automatic; otherwise pieces per (sequence, KV head, 128-row tile).
+ *   workspace     device memory of at least kvq_prefill_workspace_bytes(...) bytes, 16-byte
+ *                 aligned, never initialized by the caller; its contents after the call are
+ *                 unspecified.
+ * Other arguments, the KV formats, the page table and the device-data contract are those of
+ * kvq_decode_attn_fmt.  Stream-ordered, allocates nothing, never synchronizes.  Returns KVQ_OK,
+ * KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE or KVQ_ERR_HIP; every argument error is
+ * found on the host before any launch. */
+int kvq_prefill_attn(int32_t kv_format, const void* pool, int32_t num_pages, int32_t page_size,
+                     int32_t num_kv_heads, int32_t head_dim, const uint16_t* q,
+                     const int32_t* page_table, const int32_t* seq_lens, int32_t n_seq,
+                     int32_t chunk, int32_t n_q_heads, int32_t max_pages_per_seq,
+                     int32_t max_seq_len, float softmax_scale, int32_t num_splits, float* out,
+                     float* lse, void* workspace, size_t workspace_bytes, void* stream);
+/* Pieces per (sequence, KV head, row tile) the call above would use (negative: an error code). */
+int32_t kvq_prefill_num_splits(int32_t n_seq, int32_t chunk, int32_t n_q_heads,
+                               int32_t num_kv_heads, int32_t max_seq_len,
+                               int32_t num_splits_request);
+/* Workspace bytes kvq_prefill_attn needs (0 for invalid arguments).  Host only. */
+size_t kvq_prefill_workspace_bytes(int32_t n_seq, int32_t chunk, int32_t n_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
+                                   int32_t num_splits_request);
 
 /* Static description of a return code. */
 const char* kvq_strerror(int code);

@@ -4,6 +4,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 #include "kvq_internal.h"
 
 namespace {
@@ -197,7 +199,7 @@ int decode_impl(int32_t kv_format, const void* pool, int32_t num_pages, int32_t 
     return KVQ_ERR_WORKSPACE;
   const double scale = softmax_scale > 0.0f ? (double)softmax_scale : 1.0 / sqrt((double)head_dim);
 
-  kvq::DecodeArgs a;
+  kvq::DecodeArgs a{};
   a.pool = (const uint8_t*)pool;
   a.num_pages = num_pages;
   a.page_size = page_size;
@@ -332,6 +334,141 @@ int kvq_decode_step_win(int32_t kv_format, void* pool, int32_t num_pages, int32_
                      q, page_table, seq_lens, n_seq, n_rows, n_q_heads, max_pages_per_seq,
                      max_seq_len, window, ring_pages, softmax_scale, num_splits, out, lse,
                      workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---- chunked prefill ------------------------------------------------------------------------
+
+namespace {
+
+// Pieces per (sequence, KV head, row tile) for the prefill: the count whose grid fills the 256
+// CUs in the fewest rounds per unit of work (one workgroup per CU), each piece keeping at least
+// 8 blocks, the smallest such count on ties (fewer partials to merge).
+int plan_prefill(int n_seq, int num_kv_heads, int rows, int max_seq_len, int request, Plan* plan,
+                 int* row_tiles) {
+  if (n_seq <= 0 || num_kv_heads <= 0 || rows <= 0 || max_seq_len <= 0 || request < 0)
+    return KVQ_ERR_ARG;
+  const long long nblk = ceil_div(max_seq_len, kvq::kBlock);
+  const long long tiles = ceil_div(rows, kvq::kPrefillRowsPerTile);
+  const long long work = (long long)n_seq * num_kv_heads * tiles;
+  long long s = 1;
+  if (request > 0) {
+    s = request;
+  } else {
+    const long long s_max = std::max(1LL, std::min(16LL, nblk / 8));
+    double best = 0.0;
+    for (long long c = 1; c <= s_max; ++c) {
+      const double eff = (double)(work * c) / (double)(kTargetGroups * ceil_div(work * c, kTargetGroups));
+      if (eff > best + 0.02) {
+        best = eff;
+        s = c;
+      }
+    }
+  }
+  if (s > nblk) s = nblk;
+  if (s > kvq::kMaxSplits) s = kvq::kMaxSplits;
+  const long long bps = ceil_div(nblk, s);
+  s = ceil_div(nblk, bps);
+  if (work * s >= (1LL << 31)) return KVQ_ERR_ARG;
+  plan->splits = (int)s;
+  plan->blocks_per_split = (int)bps;
+  *row_tiles = (int)tiles;
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvq_prefill_num_splits(int32_t n_seq, int32_t chunk, int32_t n_q_heads,
+                               int32_t num_kv_heads, int32_t max_seq_len,
+                               int32_t num_splits_request) {
+  if (chunk < 1 || chunk > KVQ_MAX_CHUNK || num_kv_heads <= 0 || n_q_heads <= 0 ||
+      n_q_heads % num_kv_heads != 0)
+    return KVQ_ERR_ARG;
+  Plan p;
+  int tiles;
+  const int rc = plan_prefill(n_seq, num_kv_heads, chunk * (n_q_heads / num_kv_heads), max_seq_len,
+                              num_splits_request, &p, &tiles);
+  return rc == KVQ_OK ? p.splits : rc;
+}
+
+size_t kvq_prefill_workspace_bytes(int32_t n_seq, int32_t chunk, int32_t n_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
+                                   int32_t num_splits_request) {
+  if (chunk < 1 || chunk > KVQ_MAX_CHUNK || num_kv_heads <= 0 || n_q_heads <= 0 ||
+      n_q_heads % num_kv_heads != 0 || !head_dim_ok(head_dim))
+    return 0;
+  const int rows = chunk * (n_q_heads / num_kv_heads);
+  Plan p;
+  int tiles;
+  if (plan_prefill(n_seq, num_kv_heads, rows, max_seq_len, num_splits_request, &p, &tiles) != KVQ_OK)
+    return 0;
+  return workspace_for((long long)n_seq * num_kv_heads, p.splits, rows, head_dim);
+}
+
+int kvq_prefill_attn(int32_t kv_format, const void* pool, int32_t num_pages, int32_t page_size,
+                     int32_t num_kv_heads, int32_t head_dim, const uint16_t* q,
+                     const int32_t* page_table, const int32_t* seq_lens, int32_t n_seq,
+                     int32_t chunk, int32_t n_q_heads, int32_t max_pages_per_seq,
+                     int32_t max_seq_len, float softmax_scale, int32_t num_splits, float* out,
+                     float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  const int vb = vbits_of(kv_format);
+  int rc = pool_args_ok(pool, num_pages, page_size, num_kv_heads, head_dim, vb);
+  if (rc != KVQ_OK) return rc;
+  if (!q || !page_table || !seq_lens || !out) return KVQ_ERR_ARG;
+  if (n_seq <= 0 || n_q_heads <= 0 || max_pages_per_seq <= 0 || max_seq_len <= 0 ||
+      num_splits < 0 || chunk < 1)
+    return KVQ_ERR_ARG;
+  if (chunk > KVQ_MAX_CHUNK) return KVQ_ERR_UNSUPPORTED;
+  if (n_q_heads % num_kv_heads != 0) return KVQ_ERR_ARG;
+  const int group = n_q_heads / num_kv_heads;
+  if ((long long)group * chunk > KVQ_MAX_PREFILL_ROWS) return KVQ_ERR_UNSUPPORTED;
+  if ((long long)max_seq_len > (long long)max_pages_per_seq * page_size) return KVQ_ERR_ARG;
+  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return KVQ_ERR_ARG;
+  if (((uintptr_t)q & 15) != 0 || ((uintptr_t)out & 15) != 0) return KVQ_ERR_ARG;
+  const int rows = group * chunk;
+  Plan plan;
+  int tiles;
+  rc = plan_prefill(n_seq, num_kv_heads, rows, max_seq_len, num_splits, &plan, &tiles);
+  if (rc != KVQ_OK) return rc;
+  const long long units = (long long)n_seq * num_kv_heads;
+  const size_t need = workspace_for(units, plan.splits, rows, head_dim);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15) != 0)
+    return KVQ_ERR_WORKSPACE;
+  const double scale = softmax_scale > 0.0f ? (double)softmax_scale : 1.0 / sqrt((double)head_dim);
+
+  kvq::DecodeArgs a{};
+  a.pool = (const uint8_t*)pool;
+  a.num_pages = num_pages;
+  a.page_size = page_size;
+  a.num_kv_heads = num_kv_heads;
+  a.vbits = vb;
+  a.fp8 = kv_format == KVQ_FORMAT_FP8;
+  a.log2_page = __builtin_ctz((unsigned)page_size);
+  a.q = q;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.n_seq = n_seq;
+  a.n_rows = chunk;
+  a.n_q_heads = n_q_heads;
+  a.group = group;
+  a.rows = rows;
+  a.max_pages = max_pages_per_seq;
+  a.max_seq_len = max_seq_len;
+  a.splits = plan.splits;
+  a.blocks_per_split = plan.blocks_per_split;
+  a.row_tiles = tiles;
+  a.scale_log2 = (float)(scale * 1.4426950408889634074);
+  a.ws_acc = (float*)workspace;
+  a.ws_ml = plan.splits > 1
+                ? (float2*)((char*)a.ws_acc + (size_t)units * plan.splits * rows * head_dim * sizeof(float))
+                : nullptr;
+  a.out = out;
+  a.lse = lse;
+  (void)hipGetLastError();
+  return kvq::launch_prefill(head_dim, a, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
 }  // extern "C"

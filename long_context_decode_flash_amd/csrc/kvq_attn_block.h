@@ -521,6 +521,70 @@ __device__ __attribute__((always_inline)) inline void process_block(
   }
 }
 
+// The query rows' B operands of Q K^T, from the raw fp16 words qw (lane: query row 16*nb + m16
+// and the 16 dims 16*(4*jj + g) .. +15 of each 64-dim step jj).  cz[nb] receives the factor
+// that turns a row's dot products into log2-unit logits (before the K scale).
+template <int D, int NB, bool F8>
+__device__ __attribute__((always_inline)) inline void prepare_queries(
+    const u32x4 (&qw)[NB][D / 64][2], float scale_log2, i32x4 (&qd)[NB][3][D / 64], float (&cz)[NB]) {
+  // Q^T as three int8 digit planes (B of QK^T).  Per row, q * 2^F = h*2^16 + m*2^8 + l with
+  // balanced digits in [-128, 127] and |q * 2^F| < 2^22 for the row's largest |q|; exact for every
+  // element within 2^12 of it, the rest rounded to the 2^-F grid.  E4M3 keys
+  // use the fp16 words as they are (cz = softmax_scale * log2(e)); qd is then left unset.
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    if constexpr (F8) {  // the fp16 query words are the B operands as they are
+      cz[nb] = scale_log2;
+      continue;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int jj = 0; jj < D / 64; ++jj)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const half8 h8 = __builtin_bit_cast(half8, qw[nb][jj][hf]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)h8[e]));
+      }
+    amax = max_over_rows(amax);
+    int E = 0;
+    if (amax > 0.0f) (void)__builtin_frexpf(amax, &E);  // amax < 2^E
+    const int F = amax > 0.0f ? 22 - E : 0;
+    const float scale_f = __builtin_ldexpf(1.0f, F);
+    cz[nb] = __builtin_ldexpf(scale_log2, -F);
+#pragma unroll
+    for (int jj = 0; jj < D / 64; ++jj) {
+      uint32_t wd[3][4];
+#pragma unroll
+      for (int w4 = 0; w4 < 4; ++w4) {
+        // x + 1.5 * 2^23 rounds x to an integer (ties to even) in the low mantissa bits; adding
+        // 128 * (1 + 2^8 + 2^16) then makes byte k of the word digit k + 128, so xor 0x80 per byte
+        // leaves the balanced digits as int8
+        uint32_t wq[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int el = 4 * w4 + e;
+          const half8 h8 = __builtin_bit_cast(half8, qw[nb][jj][el >> 3]);
+          const float x = (float)h8[el & 7];
+          const uint32_t y = __builtin_bit_cast(uint32_t, __builtin_fmaf(x, scale_f, 12582912.0f));
+          wq[e] = (y - (0x4B400000u - 0x808080u)) ^ 0x808080u;
+        }
+        // 4x3 byte transpose: plane k gets byte k of the four words
+        const uint32_t t01 = __builtin_amdgcn_perm(wq[1], wq[0], 0x05010400u);
+        const uint32_t t23 = __builtin_amdgcn_perm(wq[3], wq[2], 0x05010400u);
+        const uint32_t u01 = __builtin_amdgcn_perm(wq[1], wq[0], 0x0C0C0602u);
+        const uint32_t u23 = __builtin_amdgcn_perm(wq[3], wq[2], 0x0C0C0602u);
+        wd[2][w4] = __builtin_amdgcn_perm(t23, t01, 0x05040100u);  // low digits
+        wd[1][w4] = __builtin_amdgcn_perm(t23, t01, 0x07060302u);
+        wd[0][w4] = __builtin_amdgcn_perm(u23, u01, 0x05040100u);  // high digits
+      }
+#pragma unroll
+      for (int pc = 0; pc < 3; ++pc)
+        qd[nb][pc][jj] = __builtin_bit_cast(i32x4, u32x4{wd[pc][0], wd[pc][1], wd[pc][2], wd[pc][3]});
+    }
+  }
+}
+
 // The log-sum-exp merge of the splits.  One wave per 64 (unit, query row, 4 dims) items: each
 // lane takes one item over every split, with an online max, so the merge needs no LDS and no
 // barrier and all of a lane's loads of a batch are in flight at once.  The partials come from

@@ -57,6 +57,7 @@ struct DecodeArgs {
   // page-table entry n % ring.  0 and 0: the whole context through a linear page table.
   int window, ring;
   int splits, blocks_per_split;  // workgroups per (sequence, KV head), 32-token blocks each
+  int row_tiles;  // prefill: tiles of 128 query rows per (sequence, KV head)
   float scale_log2;  // softmax_scale * log2(e)
   float* ws_acc;     // [units][splits][rows][D] partial numerators
   float2* ws_ml;     // [units][ml_stride(splits, rows)] (max in log2 units, sum of exp2)
@@ -72,5 +73,8 @@ struct DecodeArgs {
 
 hipError_t launch_append(int head_dim, const AppendArgs& a, hipStream_t stream);
 hipError_t launch_decode(int head_dim, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_prefill(int head_dim, const DecodeArgs& a, hipStream_t stream);
+
+constexpr int kPrefillRowsPerTile = 128;  // query rows of one prefill workgroup (32 per wave)
 
 }  // namespace kvq

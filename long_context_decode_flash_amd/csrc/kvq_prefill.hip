@@ -1,0 +1,242 @@
+// kvq_prefill.hip — chunked-prefill attention over the paged cache.
+//
+// The forum post "3090 单卡跑 Qwen3.8-27B：NInfer 上机实测（180K 上下文 / C2 并发 / 4bit KV）"
+// (一、部署, launch-flag table) prefills prompts in chunks of 1,024 tokens and names prefill as
+// the cost behind the time to first token (二、测评).  Once a chunk's tokens are appended to the
+// cache, each position of the chunk attends causally to the cache up to itself: position i of a
+// chunk of C at the end of a context of L tokens sees tokens 0 .. L - C + i.  That is the
+// decode's multi-row attention with C rows; what changes is the shape.  Every cached byte now
+// meets thousands of query rows, so the work is dense matrix-core work, not a byte stream:
+//
+//   * one workgroup of 4 waves per (sequence, KV head, tile of 128 query rows, piece of the
+//     context); the rows of a KV head are (chunk position, query head of its group) pairs in
+//     position-major order, and wave w owns rows 32w .. 32w + 31 of the tile as the two 16-row
+//     blocks of the decode's matrix-core step (int8 Q K^T on three exact digit planes of the
+//     query, or fp16 for E4M3 keys; online softmax; P V with the V scale folded into P);
+//   * waves 0 and 1 stage tiles 0 and 1 of each 32-token block into one of three LDS buffers
+//     shared by all four waves, so two blocks are in flight while the workgroup computes one,
+//     with one barrier per block;
+//   * blocks past the tile's last position are never loaded; a wave skips blocks past its last
+//     row's position and masks the blocks that cross its rows' positions;
+//   * each wave writes its rows: the output itself (one piece per context) or a partial that the
+//     decode's log-sum-exp merge launch combines.
+#include "kvq_attn_block.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kRowsPerWave = kPrefillRowsPerTile / kWavesPerGroup;  // 32
+constexpr int kIdsPerChunk = kWave;  // blocks whose page ids a staging wave keeps in its lanes
+
+template <int D, int VB, bool F8>
+__global__ __launch_bounds__(256) void prefill_kernel(DecodeArgs a) {
+  constexpr int NB = kRowsPerWave / 16;
+  constexpr int DB = D / 16;
+  constexpr int NSTAGE = 3;
+  constexpr int BS = Stage<D, VB>::kBlockBytes;
+  constexpr int TB = Stage<D, VB>::kTileBytes;
+  constexpr int NLT = Stage<D, VB>::kLoads / 2;  // direct-to-LDS loads of one tile
+  static_assert(NLT <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) uint8_t s_stage[NSTAGE][BS];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int split = blockIdx.x % a.splits;
+  const int ut = blockIdx.x / a.splits;
+  const int tile = ut % a.row_tiles, unit = ut / a.row_tiles;
+  const int b = unit / a.num_kv_heads, h = unit % a.num_kv_heads;
+  const int P = a.page_size;
+  const int L = a.seq_lens[b];
+  const int Lc = min(L, a.max_seq_len);  // tokens past max_seq_len are not attended
+  const int m16 = lane & 15, g = lane >> 4;
+  const int C = a.n_rows;  // chunk positions
+
+  // ---- the tile's and the wave's rows (position i = n / group of row n) ----
+  const int n_tile0 = tile * kPrefillRowsPerTile;
+  const int n_tile1 = min(n_tile0 + kPrefillRowsPerTile, a.rows) - 1;
+  const int t_hi = min(L - C + n_tile1 / a.group, Lc - 1);  // last token a row of the tile sees
+  const int nblk = t_hi >= 0 ? t_hi / kBlock + 1 : 0;
+  const int g_blk0 = split * a.blocks_per_split;
+  const int n_blocks = max(min(g_blk0 + a.blocks_per_split, nblk) - g_blk0, 0);
+  const int nw0 = n_tile0 + kRowsPerWave * w;
+  const int nw1 = min(nw0 + kRowsPerWave, a.rows) - 1;  // below nw0: the wave holds only padding
+  // last token every row of the wave sees, and last token some row of it sees
+  const int w_all = nw1 >= nw0 ? min(L - C + nw0 / a.group, Lc - 1) : -1;
+  const int w_any = nw1 >= nw0 ? min(L - C + nw1 / a.group, Lc - 1) : -1;
+
+  const size_t bb = block_bytes(P, D, VB);
+  const uint32_t page_stride32 = (uint32_t)(a.num_kv_heads * bb);  // < 2^32, checked on the host
+  const uint8_t* pool_h = a.pool + (size_t)h * bb;
+  const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
+  const int lgP = a.log2_page;
+
+  // ---- raw query words (the decode's B-operand layout); padding rows: q = 0, see nothing ----
+  u32x4 qw[NB][D / 64][2];
+  int last_tok[NB], first_tok[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = nw0 + 16 * nb + m16;
+    const bool real = n < a.rows;
+    const int i = real ? n / a.group : 0;
+    const int hq = h * a.group + (real ? n % a.group : 0);
+    last_tok[nb] = real ? min(L - C + i, Lc - 1) : -1;
+    first_tok[nb] = 0;
+    const uint16_t* qrow = a.q + (((size_t)b * C + i) * a.n_q_heads + hq) * D;
+#pragma unroll
+    for (int jj = 0; jj < D / 64; ++jj)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        qw[nb][jj][hf] = real ? *(const u32x4*)(qrow + 16 * (4 * jj + g) + 8 * hf) : u32x4{0, 0, 0, 0};
+  }
+
+  // ---- staging: wave tau (0 or 1) loads tile tau of every block; lane k holds the physical page
+  // of that tile for block k of the current group of kIdsPerChunk blocks ----
+  const uint32_t stage0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)&s_stage[0][0]);
+  const uint32_t lane16 = 16u * lane;
+  const ScaleLane sl = scale_lane<D, VB>(P, lane);
+  const bool stager = w < 2;
+  int my_pid = 0;
+  auto load_ids = [&](int k0) {
+    const int blk = g_blk0 + k0 + lane;
+    int tok0 = blk * kBlock + kTile * w;
+    if (tok0 >= Lc) tok0 = blk * kBlock;  // a tile past the end stages tile 0 again, all masked
+    const int id = pt[k0 + lane < n_blocks ? (tok0 >> lgP) : 0];  // entry 0 always exists
+    my_pid = min(max(id, 0), a.num_pages - 1);  // out-of-range ids are clamped, never followed
+  };
+  auto issue = [&](int k) {
+    const int blk = g_blk0 + k;
+    int tok0 = blk * kBlock + kTile * w;
+    if (tok0 >= Lc) tok0 = blk * kBlock;
+    const int phys = __builtin_amdgcn_readlane(my_pid, k % kIdsPerChunk);
+    stage_tile<D, VB>(pool_h + (uint64_t)(uint32_t)phys * page_stride32, P, tok0 & (P - 1),
+                      stage0 + (uint32_t)((k % NSTAGE) * BS + w * TB), lane16, sl);
+  };
+  if (stager) {
+    load_ids(0);
+    // the query words are used here, so the compiler's wait for them (one round trip with the
+    // page ids) is not placed after the block loads
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int jj = 0; jj < D / 64; ++jj) asm volatile("" ::"v"(qw[nb][jj][0]), "v"(qw[nb][jj][1]));
+    asm volatile("" ::"v"(my_pid));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the DMA counting starts here
+    if (n_blocks > 0) issue(0);
+    if (n_blocks > 1) issue(1);
+  }
+
+  i32x4 qd[NB][3][D / 64];
+  float cz[NB];
+  prepare_queries<D, NB, F8>(qw, a.scale_log2, qd, cz);
+
+  floatx4 acc[NB][DB];
+  float base[NB], l_run[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[nb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
+    base[nb] = kNegInf;
+    l_run[nb] = 0.0f;
+  }
+
+  for (int k = 0; k < n_blocks; ++k) {
+    const int blk = g_blk0 + k;
+    const uint8_t* src = &s_stage[k % NSTAGE][0];
+    if (stager) {
+      if (k + 1 < n_blocks)
+        wait_vmcnt<NLT>();  // this tile of block k is in; block k + 1's may still be in flight
+      else
+        wait_vmcnt<0>();
+      // slots at or past the context end may hold junk scale bits, and 0 * Inf is no zero:
+      // clear their V scales in the staged copy before any wave reads it
+      const int t = blk * kBlock + kTile * w + lane;
+      if (lane < kTile && t >= Lc) {
+        uint8_t* vs = (uint8_t*)src + w * TB + Stage<D, VB>::kVs + lane * (D / 16);
+        if constexpr (D == 256) *(u32x4*)vs = u32x4{0, 0, 0, 0};
+        else if constexpr (D == 128) *(u32x2*)vs = u32x2{0, 0};
+        else *(uint32_t*)vs = 0u;
+      }
+    }
+    // block k staged for every wave (the stagers waited for their loads above), and every
+    // wave's reads of block k - 1's buffer are complete, so it may be refilled; the loads of
+    // block k + 1 stay in flight across the barrier
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (stager && k + 2 < n_blocks) {
+      if ((k + 2) % kIdsPerChunk == 0) load_ids(k + 2);  // the compiler waits for the ids (and all loads)
+      issue(k + 2);
+    }
+    if (blk * kBlock > w_any) continue;  // no row of this wave sees the block (wave-uniform)
+    const bool masked = blk * kBlock + kBlock - 1 > w_all;
+    TileRaw<D, VB> raw[2];
+    read_tile<D, VB>(raw[0], src, lane);
+    read_tile<D, VB>(raw[1], src + TB, lane);
+    if constexpr (F8) {
+      if (masked) {
+        clear_unseen_v<D, VB>(raw[0], blk * kBlock, g, 0, Lc);
+        clear_unseen_v<D, VB>(raw[1], blk * kBlock + kTile, g, 0, Lc);
+      }
+    }
+    float e5;  // binary exponent of the block's largest V scale
+    {
+      const uint32_t* vsw = (const uint32_t*)(src + Stage<D, VB>::kVs) + (lane & (D / 4 - 1));
+      const uint32_t m = wave_max_u16x2(__builtin_bit_cast(uint32_t, __builtin_elementwise_max(
+          __builtin_bit_cast(u16x2, vsw[0]), __builtin_bit_cast(u16x2, vsw[TB / 4]))));
+      e5 = (float)((m >> 10) & 31);
+    }
+    process_block<D, NB, VB, false, F8>(raw, blk, masked, e5, qd, qw, cz, first_tok, last_tok, g, acc, base,
+                                        l_run);
+  }
+
+  // ---- each wave writes its own rows: the output (one piece) or this piece's partial ----
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const float l = sum_over_rows(l_run[nb]);
+    const int n = nw0 + 16 * nb + m16;
+    if (n >= a.rows) continue;
+    if (a.splits == 1) {
+      const int i = n / a.group, hq = h * a.group + n % a.group;
+      const size_t o = ((size_t)b * C + i) * a.n_q_heads + hq;
+      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) *(floatx4*)(a.out + o * D + 16 * db + 4 * g) = acc[nb][db] * inv;
+      if (g == 0 && a.lse) a.lse[o] = l > 0.0f ? (base[nb] + log2f(l)) * 0.69314718055994530942f : kNegInf;
+    } else {
+      const size_t prow = ((size_t)unit * a.splits + split) * a.rows + n;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) *(floatx4*)(a.ws_acc + prow * D + 16 * db + 4 * g) = acc[nb][db];
+      if (g == 0) a.ws_ml[(size_t)unit * ml_stride(a.splits, a.rows) + (size_t)split * a.rows + n] = float2{base[nb], l};
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_prefill_d(const DecodeArgs& a, hipStream_t stream) {
+  const unsigned units = (unsigned)((long long)a.n_seq * a.num_kv_heads);
+  const dim3 grid(units * (unsigned)a.row_tiles * (unsigned)a.splits), block(kWave * kWavesPerGroup);
+  if (a.fp8)
+    hipLaunchKernelGGL((prefill_kernel<D, 8, true>), grid, block, 0, stream, a);
+  else if (a.vbits == 8)
+    hipLaunchKernelGGL((prefill_kernel<D, 8, false>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<D, 4, false>), grid, block, 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits == 1) return e;
+  const unsigned per_unit = (unsigned)(((long long)a.rows * (D / 4) + kWave - 1) / kWave);
+  hipLaunchKernelGGL((merge_kernel<D>), dim3(units * per_unit), dim3(kWave), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(int head_dim, const DecodeArgs& a, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_prefill_d<64>(a, stream);
+    case 128: return launch_prefill_d<128>(a, stream);
+    case 256: return launch_prefill_d<256>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvq

@@ -24,6 +24,7 @@ KVQ_MAX_STEP_TOKENS = 64
 KVQ_FORMAT_K8V4 = 0  # 4-bit V codes
 KVQ_FORMAT_K8V8 = 1  # 8-bit V codes
 KVQ_FORMAT_FP8 = 2   # K and V as OCP e4m3 codes, the 8-bit V layout
+KVQ_MAX_CHUNK = 8192  # chunked prefill: positions per chunk
 FORMATS = {"k8v4": KVQ_FORMAT_K8V4, "k8v8": KVQ_FORMAT_K8V8, "fp8": KVQ_FORMAT_FP8}
 
 _lock = threading.Lock()
@@ -84,6 +85,13 @@ def lib():
         L.kvq_decode_num_splits_win.restype = I
         L.kvq_decode_workspace_bytes_win.argtypes = [I, I, I, I, I, I, I, I]
         L.kvq_decode_workspace_bytes_win.restype = ctypes.c_size_t
+        # chunked prefill: the decode_attn_fmt arguments with chunk in place of n_rows
+        L.kvq_prefill_attn.argtypes = L.kvq_decode_attn_fmt.argtypes
+        L.kvq_prefill_attn.restype = ctypes.c_int
+        L.kvq_prefill_num_splits.argtypes = [I, I, I, I, I, I]
+        L.kvq_prefill_num_splits.restype = I
+        L.kvq_prefill_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+        L.kvq_prefill_workspace_bytes.restype = ctypes.c_size_t
         _lib = L
         return L
 
@@ -234,6 +242,80 @@ def decode_attn(cache: PagedCache, q: torch.Tensor, page_table: torch.Tensor,
     if rc != KVQ_OK:
         raise KVQError(rc, "kvq_decode_attn")
     return out, lse
+
+
+def prefill_num_splits(n_seq: int, chunk: int, n_q_heads: int, num_kv_heads: int,
+                       max_seq_len: int, num_splits: int = 0) -> int:
+    r = int(lib().kvq_prefill_num_splits(n_seq, chunk, n_q_heads, num_kv_heads, max_seq_len,
+                                         num_splits))
+    if r < 0:
+        raise KVQError(r, "kvq_prefill_num_splits")
+    return r
+
+
+def prefill_workspace_bytes(n_seq: int, chunk: int, n_q_heads: int, num_kv_heads: int,
+                            head_dim: int, max_seq_len: int, num_splits: int = 0) -> int:
+    return int(lib().kvq_prefill_workspace_bytes(n_seq, chunk, n_q_heads, num_kv_heads, head_dim,
+                                                 max_seq_len, num_splits))
+
+
+def _prefill_args(cache, q, page_table, seq_lens, max_seq_len, out, lse, workspace,
+                  softmax_scale, num_splits, stream):
+    if q.dim() != 4 or q.shape[3] != cache.head_dim:
+        raise ValueError("q must be [n_seq][chunk][n_q_heads][head_dim]")
+    n_seq, chunk, n_q_heads, D = (int(x) for x in q.shape)
+    if tuple(out.shape) != (n_seq, chunk, n_q_heads, D):
+        raise ValueError("out must be [n_seq][chunk][n_q_heads][head_dim]")
+    if page_table.dim() != 2 or page_table.shape[0] != n_seq or seq_lens.numel() != n_seq:
+        raise ValueError("page_table must be [n_seq][max_pages_per_seq], seq_lens [n_seq]")
+    return (cache.kv_format, _dev(cache.pool, "pool", torch.uint8), cache.num_pages,
+            cache.page_size, cache.num_kv_heads, D, _dev(q, "q", torch.float16),
+            _dev(page_table, "page_table", torch.int32), _dev(seq_lens, "seq_lens", torch.int32),
+            n_seq, chunk, n_q_heads, int(page_table.shape[1]), int(max_seq_len),
+            float(softmax_scale), int(num_splits), _dev(out, "out", torch.float32),
+            _dev(lse, "lse", torch.float32) if lse is not None else None,
+            _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream_ptr(stream))
+
+
+def prefill_attn(cache: PagedCache, q: torch.Tensor, page_table: torch.Tensor,
+                 seq_lens: torch.Tensor, max_seq_len: int, *, softmax_scale: float = 0.0,
+                 num_splits: int = 0, out: torch.Tensor | None = None, want_lse: bool = True,
+                 lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                 stream=None):
+    """kvq_prefill_attn: the chunk (the last ``chunk`` tokens of each sequence, already
+    appended) attends causally to the cache. q: fp16 [n_seq][chunk][Hq][D]. Returns (out fp32
+    [n_seq][chunk][Hq][D], lse or None)."""
+    n_seq, chunk, n_q_heads, D = (int(x) for x in q.shape)
+    dev = q.device
+    if out is None:
+        out = torch.empty((n_seq, chunk, n_q_heads, D), dtype=torch.float32, device=dev)
+    if want_lse and lse is None:
+        lse = torch.empty((n_seq, chunk, n_q_heads), dtype=torch.float32, device=dev)
+    if workspace is None:
+        need = prefill_workspace_bytes(n_seq, chunk, n_q_heads, cache.num_kv_heads, D,
+                                       max_seq_len, num_splits)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    rc = lib().kvq_prefill_attn(*_prefill_args(cache, q, page_table, seq_lens, max_seq_len, out,
+                                               lse, workspace, softmax_scale, num_splits, stream))
+    if rc != KVQ_OK:
+        raise KVQError(rc, "kvq_prefill_attn")
+    return out, lse
+
+
+def prepare_prefill(cache: PagedCache, q: torch.Tensor, page_table: torch.Tensor,
+                    seq_lens: torch.Tensor, max_seq_len: int, out: torch.Tensor,
+                    lse: torch.Tensor | None, workspace: torch.Tensor, *,
+                    softmax_scale: float = 0.0, num_splits: int = 0, stream=None):
+    """Marshal the arguments of one kvq_prefill_attn once; the returned callable re-issues it."""
+    args = _prefill_args(cache, q, page_table, seq_lens, max_seq_len, out, lse, workspace,
+                         softmax_scale, num_splits, stream)
+    fn = lib().kvq_prefill_attn
+
+    def call():
+        rc = fn(*args)
+        if rc != KVQ_OK:
+            raise KVQError(rc, "kvq_prefill_attn")
+    return call
 
 
 def _step_args(cache, k_new, v_new, q, page_table, seq_lens, max_seq_len, out, lse, workspace,

@@ -255,3 +255,55 @@ def test_window_split_plan(lib):
             kvq.decode_workspace_bytes(2, n_rows, 24, 4, 256, span)
     assert lib.kvq_decode_num_splits_win(1, 4, 1000, 1, -1, 0) == kvq.KVQ_ERR_ARG
     assert lib.kvq_decode_workspace_bytes_win(1, 1, 4, 4, 64, 1000, -1, 0) == 0
+
+
+def prefill_rc(lib, **kw):
+    a = dict(fmt=0, pool=FAKE, num_pages=8, page_size=16, hkv=2, d=64, q=FAKE, pt=FAKE, sl=FAKE,
+             n_seq=1, chunk=10, hq=4, max_pages=8, max_seq_len=100, scale=0.0, splits=0,
+             out=FAKE, lse=None, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return lib.kvq_prefill_attn(a["fmt"], a["pool"], a["num_pages"], a["page_size"], a["hkv"],
+                                a["d"], a["q"], a["pt"], a["sl"], a["n_seq"], a["chunk"], a["hq"],
+                                a["max_pages"], a["max_seq_len"], a["scale"], a["splits"],
+                                a["out"], a["lse"], a["ws"], a["ws_bytes"], None)
+
+
+def test_prefill_validation(lib):
+    """Every argument error of kvq_prefill_attn is found on the host (FAKE pointers are never
+    dereferenced)."""
+    E = kvq
+    assert prefill_rc(lib, pool=None) == E.KVQ_ERR_ARG
+    assert prefill_rc(lib, q=None) == E.KVQ_ERR_ARG
+    assert prefill_rc(lib, out=None) == E.KVQ_ERR_ARG
+    assert prefill_rc(lib, fmt=3) == E.KVQ_ERR_UNSUPPORTED
+    assert prefill_rc(lib, d=96) == E.KVQ_ERR_UNSUPPORTED
+    assert prefill_rc(lib, chunk=0) == E.KVQ_ERR_ARG
+    assert prefill_rc(lib, chunk=E.KVQ_MAX_CHUNK + 1) == E.KVQ_ERR_UNSUPPORTED
+    assert prefill_rc(lib, hq=5) == E.KVQ_ERR_ARG
+    assert prefill_rc(lib, hkv=1, hq=16, chunk=8192) == E.KVQ_ERR_UNSUPPORTED  # 131072 rows
+    assert prefill_rc(lib, max_seq_len=129) == E.KVQ_ERR_ARG
+    assert prefill_rc(lib, splits=-1) == E.KVQ_ERR_ARG
+    assert prefill_rc(lib, scale=float("nan")) == E.KVQ_ERR_ARG
+    assert prefill_rc(lib, ws=None) == E.KVQ_ERR_WORKSPACE
+    need = kvq.prefill_workspace_bytes(1, 10, 4, 2, 64, 100)
+    assert need > 0
+    assert prefill_rc(lib, ws_bytes=need - 1) == E.KVQ_ERR_WORKSPACE
+    assert prefill_rc(lib, q=ctypes.c_void_p(0x100002)) == E.KVQ_ERR_ARG
+    assert prefill_rc(lib, out=ctypes.c_void_p(0x100004)) == E.KVQ_ERR_ARG
+
+
+def test_prefill_split_plan(lib):
+    """The prefill plan fills the 256 CUs in whole rounds where it can: the 1,024-position chunk
+    of two 92,160-token sequences (4 KV heads, 6 query heads each) has 2 x 4 x 48 row tiles, and
+    two pieces per tile make 768 workgroups (3 rounds); the workspace holds each piece's
+    partials."""
+    s = kvq.prefill_num_splits(2, 1024, 24, 4, 92160)
+    assert s == 2 and (2 * 4 * 48 * s) % 256 == 0
+    nblk = 92160 // 32
+    assert kvq.prefill_num_splits(1, 1024, 24, 4, 92160, 3) == 3
+    assert kvq.prefill_num_splits(1, 1, 1, 1, 64) == 1  # too few blocks to split
+    ws = kvq.prefill_workspace_bytes(2, 1024, 24, 4, 256, 92160)
+    rows = 1024 * 6
+    assert ws >= 8 * s * rows * 256 * 4 + 8 * s * rows * 8
+    assert kvq.prefill_workspace_bytes(1, 0, 4, 2, 64, 100) == 0
+    assert nblk > 0

@@ -390,8 +390,10 @@ def test_gqa_equals_mha_with_repeated_kv_heads():
     assert np.array_equal(out_g, out_m) and np.array_equal(lse_g, lse_m)
 
 
-def test_mtp_row_equals_single_row_decode_at_shorter_length():
-    R, L = 4, 75
+@pytest.mark.parametrize("R,L", [(4, 75), (40, 100)], ids=["mtp4", "chunk40"])
+def test_mtp_row_equals_single_row_decode_at_shorter_length(R, L):
+    """Row i of n_rows = R sees exactly what a one-row decode of length L - R + 1 + i sees: the
+    MTP verify step (R = 4) and a prefill chunk (R = 40, the chunk's positions)."""
     mtp = W.custom(n_seq=1, seq_lens=(L,), num_kv_heads=1, n_q_heads=2, head_dim=64,
                    page_size=16, n_rows=R, seed=29)
     o = oracle.default()
