@@ -70,6 +70,17 @@ def decode_algorithmic_bytes(wl, seq_lens, vbits: int = 4, window: int = 0) -> i
     return kv + q + pt + out
 
 
+def prefill_attn_flops(seq_lens, chunk: int, n_q_heads: int, head_dim: int) -> int:
+    """FLOPs of one chunked-prefill call: position i of a chunk at the end of a context of L
+    tokens attends L - chunk + i + 1 tokens (none below zero), each costing 2D for Q K^T and 2D
+    for P V per query head."""
+    seen = 0
+    for L in seq_lens:
+        lo = int(L) - chunk + 1
+        seen += sum(max(lo + i, 0) for i in range(chunk))
+    return seen * n_q_heads * 4 * head_dim
+
+
 def append_algorithmic_bytes(wl, vbits: int = 4) -> int:
     n = wl.n_seq * wl.n_new
     return n * wl.num_kv_heads * (2 * wl.head_dim * 4 + token_bytes(wl.head_dim, vbits)) + n * 4
@@ -153,6 +164,50 @@ def ingest_trace(stats_csv, command, bench_log=None):
     return "\n".join(lines) + "\n"
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix-core peak
+
+
+def bench_prefill(kvq, torch, wl, inp, caches, stream, chunk, reps=5):
+    """The chunked-prefill attention of the last `chunk` positions of every sequence of the
+    workload (their tokens are already in the pool), event-timed over `reps` calls rotating the
+    pool copies, against the fp16 matrix-core peak."""
+    dev = caches[0].pool.device
+    rng = np.random.default_rng(2024)
+    q = torch.from_numpy(rng.standard_normal((wl.n_seq, chunk, wl.n_q_heads, wl.head_dim),
+                                             dtype=np.float32).astype(np.float16)).to(dev)
+    pt = torch.from_numpy(np.ascontiguousarray(inp.page_table)).to(dev)
+    sl = torch.from_numpy(np.ascontiguousarray(inp.seq_lens)).to(dev)
+    msl = int(wl.seq_len)
+    splits = kvq.prefill_num_splits(wl.n_seq, chunk, wl.n_q_heads, wl.num_kv_heads, msl)
+    ws = torch.empty(kvq.prefill_workspace_bytes(wl.n_seq, chunk, wl.n_q_heads, wl.num_kv_heads,
+                                                 wl.head_dim, msl), dtype=torch.uint8, device=dev)
+    out = torch.empty((wl.n_seq, chunk, wl.n_q_heads, wl.head_dim), dtype=torch.float32,
+                      device=dev)
+    lse = torch.empty((wl.n_seq, chunk, wl.n_q_heads), dtype=torch.float32, device=dev)
+    calls = [kvq.prepare_prefill(c, q, pt, sl, msl, out, lse, ws, stream=stream) for c in caches]
+    calls[0]()  # warm-up
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for r in range(reps):
+        calls[(r + 1) % len(calls)]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    flops = prefill_attn_flops(inp.seq_lens, chunk, wl.n_q_heads, wl.head_dim)
+    tflops = flops / (us * 1e-6) / 1e12
+    log(f"[bench] prefill attention, chunk {chunk}: {us:.1f} us, {tflops:.1f} TFLOP/s")
+    return {
+        "chunk": chunk,
+        "us": round(us, 1),
+        "flops": flops,
+        "splits": splits,
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)},
+        "kernel": "kvq_prefill_attn: prefill_kernel (128-row tiles x context pieces) + merge_kernel",
+    }
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,6 +221,8 @@ def main(argv=None):
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window: each row sees only its last W tokens (0 = all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-chunk", type=int, default=1024,
+                    help="positions of the chunked-prefill measurement (0: skip it)")
     ap.add_argument("--unfused", action="store_true",
                     help="time kvq_append + kvq_decode_attn instead of kvq_decode_step")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -374,6 +431,9 @@ def main(argv=None):
             "launch_us_mean": round(ms_per_step * 1e3, 2),
         },
     }
+
+    if args.prefill_chunk > 0 and not win:
+        res["prefill_attn"] = bench_prefill(kvq, torch, wl, inp, caches, stream, args.prefill_chunk)
 
     res["prefill_append"] = {
         "tokens": n_pre,

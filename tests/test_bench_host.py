@@ -39,6 +39,17 @@ def test_window_bytes():
     assert bench.attended_range(262144, 4, 1000) == (262144 - 4 - 1000 + 1, 262144)
 
 
+def test_prefill_flops():
+    # position i of a chunk of C at the end of L tokens attends L - C + i + 1 tokens; 4D flops
+    # per token per query head (2D for Q K^T, 2D for P V)
+    assert bench.prefill_attn_flops([5], 3, 1, 64) == (3 + 4 + 5) * 4 * 64
+    # a chunk longer than the context: positions below zero see nothing
+    assert bench.prefill_attn_flops([2], 4, 1, 64) == (1 + 2) * 4 * 64
+    # the last 1,024-position chunk of both 92,160-token sequences, 24 query heads, D = 256
+    per_seq = 1024 * (92160 - 1024) + 1024 * 1025 // 2
+    assert bench.prefill_attn_flops([92160, 92160], 1024, 24, 256) == 2 * per_seq * 24 * 1024
+
+
 def test_more_than_one_gpu_is_refused(capsys):
     assert bench.main(["--gpus", "2"]) == 2
     assert "one GPU" in capsys.readouterr().err
