@@ -151,16 +151,26 @@ def ingest_trace(stats_csv, command, bench_log=None):
         lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{float(r['Percentage']):.2f} |")
-    step_us = sum(float(r["AverageNs"]) / 1e3 for r in rows
-                  if "decode_kernel" in r["Name"] or "merge_kernel" in r["Name"])
-    lines += ["", f"Sum of the step's kernel averages (decode_kernel + merge_kernel): {step_us:.2f} us."]
+    js = []
     if bench_log:
         with open(bench_log) as f:
             js = [json.loads(x) for x in f if x.startswith("{")]
-        if js:
-            lines.append(f"bench.py's own line in the same profiled run: {js[-1]['ms_per_step'] * 1e3:.2f} us "
-                         "per step (the profiler slows every launch; the unprofiled step time is the "
-                         "bench line's ms_per_step).")
+    pre = [r for r in rows if "prefill_kernel" in r["Name"]]
+    if pre:
+        # the merge launches of this run belong to both the decode steps and the prefill calls
+        pre_us = sum(float(r["TotalDurationNs"]) for r in pre) / sum(int(r["Calls"]) for r in pre) / 1e3
+        lines += ["", f"prefill_kernel average: {pre_us:.1f} us per call."]
+        if js and "prefill_attn" in js[-1]:
+            lines.append(f"bench.py's prefill_attn in the same profiled run: {js[-1]['prefill_attn']['us']:.1f} "
+                         "us per call (prefill_kernel and its merge launch, event-timed).")
+        return "\n".join(lines) + "\n"
+    step_us = sum(float(r["AverageNs"]) / 1e3 for r in rows
+                  if "decode_kernel" in r["Name"] or "merge_kernel" in r["Name"])
+    lines += ["", f"Sum of the step's kernel averages (decode_kernel + merge_kernel): {step_us:.2f} us."]
+    if js:
+        lines.append(f"bench.py's own line in the same profiled run: {js[-1]['ms_per_step'] * 1e3:.2f} us "
+                     "per step (the profiler slows every launch; the unprofiled step time is the "
+                     "bench line's ms_per_step).")
     return "\n".join(lines) + "\n"
 
 
@@ -208,11 +218,41 @@ def bench_prefill(kvq, torch, wl, inp, caches, stream, chunk, reps=5):
     }
 
 
+def ingest_settling(trace_csv, command, group=100):
+    """Markdown summary of a rocprofv3 --kernel-trace run of many steps: the decode kernel's
+    duration and the call period per group of calls, showing how the rate settles."""
+    rows = _counter_rows(trace_csv)
+    d = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows
+               if "decode_kernel" in r["Kernel_Name"])
+    m = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows
+               if "merge_kernel" in r["Kernel_Name"])
+    durs = [(e - s) / 1e3 for s, e in d]
+    lines = ["# Decode kernel duration over a sustained run", "", "Command:", "", "```", command, "```", "",
+             f"{len(d)} back-to-back decode steps. Per group of {group} calls: the decode kernel's mean, "
+             "min and max duration, and the call period (start to start).", "",
+             "| calls | t at first call (ms) | decode_kernel mean us | min us | max us | call period us |",
+             "|---|---:|---:|---:|---:|---:|"]
+    for i in range(0, len(d) - 1, group):
+        ch = durs[i:i + group]
+        j = min(i + group, len(d) - 1)
+        per = (d[j][0] - d[i][0]) / 1e3 / (j - i)
+        lines.append(f"| {i}-{i + len(ch) - 1} | {(d[i][0] - d[0][0]) / 1e6:.1f} | {sum(ch) / len(ch):.2f} | "
+                     f"{min(ch):.2f} | {max(ch):.2f} | {per:.2f} |")
+    settled = durs[len(durs) // 10:]
+    mm = [(e - s) / 1e3 for s, e in m[len(m) // 10:]]
+    lines += ["", f"After the first tenth of the calls: decode_kernel mean {sum(settled) / len(settled):.2f} us, "
+              f"merge_kernel mean {sum(mm) / max(len(mm), 1):.2f} us (both under the profiler)."]
+    return "\n".join(lines) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=50)
+    # 400 warm-up steps (about 22 ms): the decode kernel runs about 6 us slower for the first
+    # ~12 ms of a sustained run on this GPU, then settles (a kernel trace of 3,000 steps shows
+    # it); the timed steps measure the settled rate
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--workload", default=None, help="name in workloads.WORKLOADS")
     ap.add_argument("--kv-format", default="k8v4", choices=["k8v4", "k8v8", "fp8"],
                     help="KV cache format: 4-bit (the headline) or 8-bit V codes")
@@ -232,9 +272,22 @@ def main(argv=None):
     ap.add_argument("--ingest-trace", metavar="KERNEL_STATS_CSV",
                     help="write a markdown summary of a rocprofv3 kernel-stats CSV to profiles/")
     ap.add_argument("--command", default="", help="command line recorded with an ingested profile")
+    ap.add_argument("--ingest-settling", metavar="KERNEL_TRACE_CSV",
+                    help="summarize a long --kernel-trace run: decode duration per group of calls")
+    ap.add_argument("--ingest-out", default=None,
+                    help="file name under profiles/ for --ingest-trace (default: the decode trace)")
     ap.add_argument("--bench-log", default=None,
                     help="stdout of bench.py in the profiled run (its JSON line), for --ingest-trace")
     args = ap.parse_args(argv)
+
+    if args.ingest_settling:
+        from long_context_decode_flash_amd import workloads as W
+        path = os.path.join(ROOT, "profiles", args.ingest_out or
+                            f"decode_{args.workload or W.HEADLINE}_settling_trace.md")
+        with open(path, "w") as f:
+            f.write(ingest_settling(args.ingest_settling, args.command))
+        print(path)
+        return 0
 
     if args.ingest_pmc or args.ingest_trace:
         from long_context_decode_flash_amd import workloads as W
@@ -247,7 +300,7 @@ def main(argv=None):
             with open(path, "w") as f:
                 json.dump(res, f, indent=1)
         else:
-            path = os.path.join(ROOT, "profiles", f"decode_{name}_kernel_trace.md")
+            path = os.path.join(ROOT, "profiles", args.ingest_out or f"decode_{name}_kernel_trace.md")
             with open(path, "w") as f:
                 f.write(ingest_trace(args.ingest_trace, args.command, args.bench_log))
         print(path)
