@@ -342,14 +342,15 @@ __device__ inline void clear_unseen_v(TileRaw<D, VB>& r, int tok0, int g, int lo
 //          sums of 2^(z - base) * (1, v);  it only moves up, in whole powers of two, when a block's
 //          largest logit and V scale would push p * v_scale past 2^15 (fp16 headroom), so most
 //          blocks rescale nothing and every rescale is exact.
+// The first half: Q K^T and the online softmax, leaving the block's p = 2^(z - base) per row and
+// token in pexp (the acc rescale included).
 template <int D, int NB, int VB, bool WIN, bool F8>
-__device__ __attribute__((always_inline)) inline void process_block(
+__device__ __attribute__((always_inline)) inline void block_softmax(
     TileRaw<D, VB> (&raw)[2], int blk, bool masked, float e5, const i32x4 (&qd)[NB][3][D / 64],
     const u32x4 (&qw)[NB][D / 64][2], const float (&cz)[NB],
     const int (&first_tok)[NB], const int (&last_tok)[NB], int g, floatx4 (&acc)[NB][D / 16], float (&base)[NB],
-    float (&l_run)[NB]) {
+    float (&l_run)[NB], float (&pexp)[NB][2][4]) {
   constexpr int DB = D / 16;
-  constexpr int NG = D / 32;
   // ---- S^T = K Q^T: int8 codes on the int8 matrix cores with three digit planes of Q; E4M3
   // codes widened to fp16 (exactly) on the f16 matrix cores with Q's own fp16 values ----
   i32x4 sd[2][NB][3];
@@ -401,7 +402,6 @@ __device__ __attribute__((always_inline)) inline void process_block(
     for (int e = 0; e < 4; ++e) ks[tau][e] = h_at(raw[tau].ks, e);
 
   // ---- logits and the online softmax (log2 units) ----
-  float pexp[NB][2][4];
   bool rescale = false;
   float alpha[NB];
 #pragma unroll
@@ -468,7 +468,15 @@ __device__ __attribute__((always_inline)) inline void process_block(
         for (int e = 0; e < 4; ++e) acc[nb][db][e] *= alpha[nb];
   }
 
-  // ---- O^T += V^T P^T, one 32-dim scale group at a time ----
+}
+
+// The second half: O^T += V^T P^T, one 32-dim scale group at a time, with the V scale folded
+// into P.
+template <int D, int NB, int VB, bool F8>
+__device__ __attribute__((always_inline)) inline void block_pv_folded(TileRaw<D, VB> (&raw)[2],
+                                                                      const float (&pexp)[NB][2][4],
+                                                                      floatx4 (&acc)[NB][D / 16]) {
+  constexpr int NG = D / 32;
 #pragma unroll
   for (int j = 0; j < NG; ++j) {
     uint32_t l02[2], l13[2], h02[2], h13[2];
@@ -519,6 +527,18 @@ __device__ __attribute__((always_inline)) inline void process_block(
       acc[nb][2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vhi, plo, acc[nb][2 * j + 1], 0, 0, 0);
     }
   }
+}
+
+template <int D, int NB, int VB, bool WIN, bool F8>
+__device__ __attribute__((always_inline)) inline void process_block(
+    TileRaw<D, VB> (&raw)[2], int blk, bool masked, float e5, const i32x4 (&qd)[NB][3][D / 64],
+    const u32x4 (&qw)[NB][D / 64][2], const float (&cz)[NB],
+    const int (&first_tok)[NB], const int (&last_tok)[NB], int g, floatx4 (&acc)[NB][D / 16], float (&base)[NB],
+    float (&l_run)[NB]) {
+  float pexp[NB][2][4];
+  block_softmax<D, NB, VB, WIN, F8>(raw, blk, masked, e5, qd, qw, cz, first_tok, last_tok, g, acc, base, l_run,
+                                    pexp);
+  block_pv_folded<D, NB, VB, F8>(raw, pexp, acc);
 }
 
 // The query rows' B operands of Q K^T, from the raw fp16 words qw (lane: query row 16*nb + m16

@@ -10,9 +10,12 @@
 //
 //   * one workgroup of 8 waves per (sequence, KV head, tile of 128 query rows, piece of the
 //     context); the rows of a KV head are (chunk position, query head of its group) pairs in
-//     position-major order, and wave w owns rows 16w .. 16w + 15 of the tile as one 16-row
-//     block of the decode's matrix-core step (int8 Q K^T on three exact digit planes of the
-//     query, or fp16 for E4M3 keys; online softmax; P V with the V scale folded into P);
+//     position-major order, and wave w owns rows 16w .. 16w + 15 of the tile: the decode's
+//     Q K^T (int8 on three exact digit planes of the query, or fp16 for E4M3 keys) and online
+//     softmax for one 16-row block;
+//   * P V takes its V operands from LDS, built once per block for all eight waves: codes times
+//     V scale as exact fp16 hi + lo pairs (the decode instead folds the scale into each row's P,
+//     which costs per row what this costs once);
 //   * waves 0 and 1 stage tiles 0 and 1 of each 32-token block into one of three LDS buffers
 //     shared by all eight waves, so two blocks are in flight while the workgroup computes one,
 //     with one barrier per block;
@@ -27,6 +30,125 @@ namespace {
 
 constexpr int kIdsPerChunk = kWave;  // blocks whose page ids a staging wave keeps in its lanes
 
+// ---- V of a staged block as scaled fp16 operands, built once per workgroup ----
+// For 32-dim group j and half dh (dims 32j + 16dh .. + 15), lane l holds the A operand of the
+// P V product for dim 32j + 16dh + l%16 and the eight tokens of its lane group in the order the
+// P operand uses (tokens 0, 2, 1, 3 of the group's four in tile 0, then in tile 1), as an fp16
+// hi and lo pair: v = code * v_scale * 2^(15 - e5) is exact in fp32, hi = rne16(v) and
+// lo = rne16(v - hi).  e5 is the block's largest V-scale exponent field, so |v| < 2^9 and
+// nothing overflows; the P operand carries the 2^(e5 - 15).  One copy serves every wave, in
+// place of each wave widening the codes and folding the scale into its own rows' P.
+template <int NG>
+struct VHat {
+  u32x4 w[NG][2][2][kWave];  // [group][dim half][hi, lo][lane]
+};
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// hi = rne16(c * s), lo = rne16(c * s - hi) for both fp16 halves of c and s (v_fma_mix forms
+// the exact product in fp32 and rounds once).
+__device__ inline void mul16_hi_lo(uint32_t c, uint32_t s, uint32_t& hi, uint32_t& lo) {
+  uint32_t h, l;
+  asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel:[0,0,0] op_sel_hi:[1,1,0]" : "=v"(h) : "v"(c), "v"(s));
+  asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[1,1,0] op_sel_hi:[1,1,0]" : "+v"(h) : "v"(c), "v"(s));
+  asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel:[0,0,0] op_sel_hi:[1,1,1]" : "=&v"(l) : "v"(c), "v"(s), "v"(h));
+  asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[1,1,1] op_sel_hi:[1,1,1]" : "+v"(l) : "v"(c), "v"(s), "v"(h));
+  hi = h;
+  lo = l;
+}
+#pragma clang diagnostic pop
+
+// The code dword of V word index x of a staged tile, for this lane (the read_tile layout).
+template <int D, int VB>
+__device__ inline uint32_t v_word(const uint8_t* tile, int x, int lane) {
+  using S = Stage<D, VB>;
+  if constexpr (VB == 4 && D == 64) return *(const uint32_t*)(tile + S::kV + 8 * lane + 4 * x);
+  return *(const uint32_t*)(tile + S::kV + 1024 * (x / 4) + 16 * lane + 4 * (x % 4));
+}
+
+// Item it = (group j, dim half dh) of the block staged at src: codes of slots at or past lc are
+// taken as 0 (never-written slots may hold NaN codes), scales times vfac = 2^(15 - e5).
+template <int D, int VB, bool F8>
+__device__ inline void build_vhat(const uint8_t* src, VHat<D / 32>& vh, int it, int lane, int tok0, int lc,
+                                  half2v vfac) {
+  constexpr int NG = D / 32;
+  using S = Stage<D, VB>;
+  const int j = it >> 1, dh = it & 1, g = lane >> 4;
+  uint32_t hi[4], lo[4];
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) {
+    const uint8_t* tile = src + tau * S::kTileBytes;
+    uint32_t keep = 0;  // byte r of a code word is slot 4g + r of the tile
+#pragma unroll
+    for (int e = 0; e < 4; ++e) keep |= (tok0 + kTile * tau + 4 * g + e < lc) ? 0xFFu << (8 * e) : 0u;
+    uint32_t l02, l13, h02, h13;
+    if constexpr (VB == 4) {
+      i4x8_to_h2x4(v_word<D, VB>(tile, j, lane) & keep, l02, l13, h02, h13);
+    } else {
+      const uint32_t lw = v_word<D, VB>(tile, 2 * j, lane) & keep, hw = v_word<D, VB>(tile, 2 * j + 1, lane) & keep;
+      if constexpr (F8)
+        f8x8_to_h2x4(lw, hw, l02, l13, h02, h13);
+      else
+        i8x8_to_h2x4(lw, hw, l02, l13, h02, h13);
+    }
+    // scales of the lane group's tokens e = 0, 2 and 1, 3 for group j, times vfac
+    const uint16_t* vs = (const uint16_t*)(tile + S::kVs + g * (D / 4)) + j;
+    const half2v s02 = __builtin_bit_cast(half2v, (uint32_t)vs[0] | ((uint32_t)vs[2 * NG] << 16)) * vfac;
+    const half2v s13 = __builtin_bit_cast(half2v, (uint32_t)vs[NG] | ((uint32_t)vs[3 * NG] << 16)) * vfac;
+    mul16_hi_lo(dh ? h02 : l02, as_u32(s02), hi[2 * tau], lo[2 * tau]);
+    mul16_hi_lo(dh ? h13 : l13, as_u32(s13), hi[2 * tau + 1], lo[2 * tau + 1]);
+  }
+  vh.w[j][dh][0][lane] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+  vh.w[j][dh][1][lane] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+}
+
+// The K codes and K scales of a staged tile for this lane (the K part of read_tile).
+template <int D, int VB>
+__device__ inline void read_tile_k(TileRaw<D, VB>& r, const uint8_t* src, int lane) {
+  using S = Stage<D, VB>;
+#pragma unroll
+  for (int jj = 0; jj < TileRaw<D, VB>::kLoadsK; ++jj) r.k[jj] = *(const u32x4*)(src + S::kK + 1024 * jj + 16 * lane);
+  const u32x2 ks = *(const u32x2*)(src + S::kKs + 8 * (lane >> 4));
+  r.ks[0] = ks[0];
+  r.ks[1] = ks[1];
+}
+
+// O^T += V^T P^T from the shared operands: P as fp16 hi + lo with 2^(e5 - 15) applied, three
+// products per operand pair (hi*hi, hi*lo, lo*hi; lo*lo is below 2^-22 of the product).
+template <int D, int NB>
+__device__ __attribute__((always_inline)) inline void block_pv_vhat(const VHat<D / 32>& vh, int lane,
+                                                                    const float (&pexp)[NB][2][4], float pf,
+                                                                    floatx4 (&acc)[NB][D / 16]) {
+  constexpr int NG = D / 32;
+  constexpr uint32_t kOne = 0x3C003C00u;  // fp16 1.0 in both halves
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      mix_hi_lo<0>(pexp[nb][tau][0] * pf, kOne, pexp[nb][tau][2] * pf, kOne, hw[2 * tau], lw[2 * tau]);
+      mix_hi_lo<0>(pexp[nb][tau][1] * pf, kOne, pexp[nb][tau][3] * pf, kOne, hw[2 * tau + 1], lw[2 * tau + 1]);
+    }
+    // two wait states between the inline-asm writes of P and the matrix-core reads (the
+    // compiler's hazard tracking does not see inline-asm results)
+    asm("s_nop 1" : "+v"(hw[0]), "+v"(hw[1]), "+v"(hw[2]), "+v"(hw[3]), "+v"(lw[0]), "+v"(lw[1]), "+v"(lw[2]),
+        "+v"(lw[3]));
+    const half8 phi = __builtin_bit_cast(half8, u32x4{hw[0], hw[1], hw[2], hw[3]});
+    const half8 plo = __builtin_bit_cast(half8, u32x4{lw[0], lw[1], lw[2], lw[3]});
+#pragma unroll
+    for (int j = 0; j < NG; ++j)
+#pragma unroll
+      for (int dh = 0; dh < 2; ++dh) {
+        const half8 vhi = __builtin_bit_cast(half8, vh.w[j][dh][0][lane]);
+        const half8 vlo = __builtin_bit_cast(half8, vh.w[j][dh][1][lane]);
+        floatx4& c = acc[nb][2 * j + dh];
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(vhi, phi, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(vhi, plo, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(vlo, phi, c, 0, 0, 0);
+      }
+  }
+}
+
 // NB: 16-row blocks per wave; the 128 rows of a tile take 128 / (16 NB) waves.
 template <int D, int VB, bool F8, int NB>
 __global__ __launch_bounds__(kPrefillRowsPerTile / 16 / NB * kWave) void prefill_kernel(DecodeArgs a) {
@@ -37,7 +159,9 @@ __global__ __launch_bounds__(kPrefillRowsPerTile / 16 / NB * kWave) void prefill
   constexpr int TB = Stage<D, VB>::kTileBytes;
   constexpr int NLT = Stage<D, VB>::kLoads / 2;  // direct-to-LDS loads of one tile
   static_assert(NLT <= 63, "vmcnt range");
+  constexpr int NWAVES = kPrefillRowsPerTile / kRowsPerWave;
   __shared__ __attribute__((aligned(16))) uint8_t s_stage[NSTAGE][BS];
+  __shared__ VHat<D / 32> s_vh;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -167,26 +291,33 @@ __global__ __launch_bounds__(kPrefillRowsPerTile / 16 / NB * kWave) void prefill
       if ((k + 2) % kIdsPerChunk == 0) load_ids(k + 2);  // the compiler waits for the ids (and all loads)
       issue(k + 2);
     }
-    if (blk * kBlock > w_any) continue;  // no row of this wave sees the block (wave-uniform)
-    const bool masked = blk * kBlock + kBlock - 1 > w_all;
-    TileRaw<D, VB> raw[2];
-    read_tile<D, VB>(raw[0], src, lane);
-    read_tile<D, VB>(raw[1], src + TB, lane);
-    if constexpr (F8) {
-      if (masked) {
-        clear_unseen_v<D, VB>(raw[0], blk * kBlock, g, 0, Lc);
-        clear_unseen_v<D, VB>(raw[1], blk * kBlock + kTile, g, 0, Lc);
-      }
-    }
-    float e5;  // binary exponent of the block's largest V scale
+    // the block's largest V-scale exponent field (every wave reads the same staged scales)
+    float e5;
     {
       const uint32_t* vsw = (const uint32_t*)(src + Stage<D, VB>::kVs) + (lane & (D / 4 - 1));
       const uint32_t m = wave_max_u16x2(__builtin_bit_cast(uint32_t, __builtin_elementwise_max(
           __builtin_bit_cast(u16x2, vsw[0]), __builtin_bit_cast(u16x2, vsw[TB / 4]))));
       e5 = (float)((m >> 10) & 31);
     }
-    process_block<D, NB, VB, false, F8>(raw, blk, masked, e5, qd, qw, cz, first_tok, last_tok, g, acc, base,
-                                        l_run);
+    // the block's scaled V operands, each wave building its share of the (group, half) items
+    {
+      const _Float16 f = (_Float16)__builtin_ldexpf(1.0f, 15 - (int)e5);  // a power of two, exact
+      const half2v vfac = {f, f};
+#pragma unroll
+      for (int it = w; it < 2 * (D / 32); it += NWAVES) build_vhat<D, VB, F8>(src, s_vh, it, lane, blk * kBlock, Lc, vfac);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();  // the operands are complete
+    asm volatile("" ::: "memory");
+    if (blk * kBlock > w_any) continue;  // no row of this wave sees the block (wave-uniform)
+    const bool masked = blk * kBlock + kBlock - 1 > w_all;
+    TileRaw<D, VB> raw[2];
+    read_tile_k<D, VB>(raw[0], src, lane);
+    read_tile_k<D, VB>(raw[1], src + TB, lane);
+    float pexp[NB][2][4];
+    block_softmax<D, NB, VB, false, F8>(raw, blk, masked, e5, qd, qw, cz, first_tok, last_tok, g, acc, base, l_run,
+                                        pexp);
+    block_pv_vhat<D, NB>(s_vh, lane, pexp, __builtin_ldexpf(1.0f, (int)e5 - 15), acc);
   }
 
   // ---- each wave writes its own rows: the output (one piece) or this piece's partial ----
