@@ -21,6 +21,9 @@ CASES = [
     (1, (1500,), 4, 24, 256, 64, 100),      # 600 rows, 5 tiles
     (1, (130,), 2, 12, 256, 64, 130),       # the whole prompt as one chunk
     (2, (20, 61), 1, 4, 64, 16, 30),        # a chunk longer than the first context
+    (1, (700,), 2, 16, 128, 128, 33),       # 128-token pages, 8 query heads per KV head
+    (1, (1030,), 1, 2, 256, 256, 200),      # 256-token pages, a ragged last page
+    (2, (97, 160), 4, 8, 64, 32, 64),       # 32-token pages, two sequences sharing the pool
 ]
 
 
