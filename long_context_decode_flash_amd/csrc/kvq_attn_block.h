@@ -605,39 +605,50 @@ __device__ __attribute__((always_inline)) inline void prepare_queries(
   }
 }
 
-// The log-sum-exp merge of the splits.  One wave per 64 (unit, query row, 4 dims) items: each
-// lane takes one item over every split, with an online max, so the merge needs no LDS and no
-// barrier and all of a lane's loads of a batch are in flight at once.  The partials come from
-// the previous launch on the stream.
+// The log-sum-exp merge of the splits.  Eight lanes per (unit, query row, 4 dims) item, 8 items
+// per wave: lane p of an item takes the splits p, p + 8, p + 16, ... with an online max (all of
+// a batch's loads in flight at once), and the eight lanes combine through DPP moves within each
+// row of 16 lanes, so the merge needs no LDS and no barrier.  The partials come from the
+// previous launch on the stream.  On the 184K-token step (32 splits) one lane per item took
+// about 1 us longer per step than 4 lanes, and 8 and 16 lanes measured 0.3-0.6 us below 4.
+constexpr int kMergeLanes = 8;                       // lanes per output item (4, 8 or 16)
+constexpr int kMergeItems = kWave / kMergeLanes;     // items per wave
+
+__host__ __device__ constexpr unsigned merge_groups(int rows, int head_dim) {
+  return (unsigned)(((long long)rows * (head_dim / 4) + kMergeItems - 1) / kMergeItems);
+}
+
 template <int D>
 __global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a) {
   constexpr int NQ = D / 4;
-  constexpr int U = 32;  // splits per batch
+  constexpr int U = 32 / kMergeLanes;  // splits per lane per batch
   const int S = a.splits, R = a.rows;
   const int items = R * NQ;
-  const int per_unit = (items + kWave - 1) / kWave;
+  const int per_unit = (int)merge_groups(R, D);
   const int unit = blockIdx.x / per_unit;
-  const int it = (blockIdx.x % per_unit) * kWave + (int)threadIdx.x;
-  if (it >= items) return;
+  const int part = threadIdx.x & (kMergeLanes - 1);
+  const int it0 = (blockIdx.x % per_unit) * kMergeItems + (int)(threadIdx.x / kMergeLanes);
+  const bool live = it0 < items;  // the same for every lane of an item
+  const int it = live ? it0 : items - 1;
   const int n = it / NQ, q = it % NQ;
   const int b = unit / a.num_kv_heads, h = unit % a.num_kv_heads;
   const float2* ml = a.ws_ml + (size_t)unit * ml_stride(S, R) + n;
-  const float* part = a.ws_acc + ((size_t)unit * S * R + n) * D + 4 * q;
+  const float* prt = a.ws_acc + ((size_t)unit * S * R + n) * D + 4 * q;
   float mx = kNegInf, den = 0.0f;
   floatx4 num = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < S; s0 += U) {
+  for (int s0 = part; s0 < S; s0 += kMergeLanes * U) {
     float2 mv[U];
     floatx4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {  // indices clamped into range: all loads issued at once
-      const int sp = min(s0 + u, S - 1);
+      const int sp = min(s0 + kMergeLanes * u, S - 1);
       mv[u] = ml[(size_t)sp * R];
-      v[u] = *(const floatx4*)(part + (size_t)sp * R * D);
+      v[u] = *(const floatx4*)(prt + (size_t)sp * R * D);
     }
     // the batch's largest max; the running sums move to it (once per batch, exactly)
     float bm = kNegInf;
 #pragma unroll
-    for (int u = 0; u < U; ++u) bm = s0 + u < S ? fmaxf(bm, mv[u].x) : bm;
+    for (int u = 0; u < U; ++u) bm = s0 + kMergeLanes * u < S ? fmaxf(bm, mv[u].x) : bm;
     if (bm > mx) {
       const float f = __builtin_amdgcn_exp2f(mx - bm);  // 0 while mx is -inf
       num *= f;
@@ -648,15 +659,43 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       // a split that saw nothing has max -inf and weight 0
-      const float wgt = s0 + u < S ? __builtin_amdgcn_exp2f(mv[u].x - m_use) : 0.0f;
+      const float wgt = s0 + kMergeLanes * u < S ? __builtin_amdgcn_exp2f(mv[u].x - m_use) : 0.0f;
       num += wgt * v[u];
       den += wgt * mv[u].y;
     }
   }
+  // the lanes of the item: common max, then sums (quad_perm [1,0,3,2] and [2,3,0,1], then
+  // row_half_mirror and row_mirror for groups of 8 and 16)
+#define KVQ_QUAD(v, ctrl) \
+  __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, 0xF, 0xF, false))
+  float M = fmaxf(mx, KVQ_QUAD(mx, 0xB1));
+  M = fmaxf(M, KVQ_QUAD(M, 0x4E));
+  if constexpr (kMergeLanes >= 8) M = fmaxf(M, KVQ_QUAD(M, 0x141));
+  if constexpr (kMergeLanes >= 16) M = fmaxf(M, KVQ_QUAD(M, 0x140));
+  const float f = mx == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mx - M);
+  den *= f;
+  num *= f;
+  den += KVQ_QUAD(den, 0xB1);
+  den += KVQ_QUAD(den, 0x4E);
+  if constexpr (kMergeLanes >= 8) den += KVQ_QUAD(den, 0x141);
+  if constexpr (kMergeLanes >= 16) den += KVQ_QUAD(den, 0x140);
+  // (elements are copied to scalars first: a bit cast of a vector element reads element 0 with
+  // this compiler)
+  float nv[4] = {num[0], num[1], num[2], num[3]};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    nv[e] += KVQ_QUAD(nv[e], 0xB1);
+    nv[e] += KVQ_QUAD(nv[e], 0x4E);
+    if constexpr (kMergeLanes >= 8) nv[e] += KVQ_QUAD(nv[e], 0x141);
+    if constexpr (kMergeLanes >= 16) nv[e] += KVQ_QUAD(nv[e], 0x140);
+  }
+  num = floatx4{nv[0], nv[1], nv[2], nv[3]};
+#undef KVQ_QUAD
+  if (!live || part != 0) return;
   const int i = n / a.group, hq = h * a.group + n % a.group;
   const size_t o = ((size_t)b * a.n_rows + i) * a.n_q_heads + hq;
   *(floatx4*)(a.out + o * D + 4 * q) = num * (den > 0.0f ? 1.0f / den : 0.0f);
-  if (q == 0 && a.lse) a.lse[o] = den > 0.0f ? (mx + log2f(den)) * 0.69314718055994530942f : kNegInf;
+  if (q == 0 && a.lse) a.lse[o] = den > 0.0f ? (M + log2f(den)) * 0.69314718055994530942f : kNegInf;
 }
 
 }  // namespace

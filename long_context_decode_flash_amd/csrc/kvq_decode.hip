@@ -343,7 +343,7 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
     launch_attn<D, false>(a, dim3(grid), block, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
-  const unsigned per_unit = (unsigned)((a.rows * (D / 4) + kWave - 1) / kWave);
+  const unsigned per_unit = merge_groups(a.rows, D);
   hipLaunchKernelGGL((merge_kernel<D>), dim3(units * per_unit), dim3(kWave), 0, stream, a);
   return hipGetLastError();
 }

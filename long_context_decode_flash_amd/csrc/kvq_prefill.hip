@@ -361,7 +361,7 @@ hipError_t launch_prefill_d(const DecodeArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((prefill_kernel<D, 4, false, kPrefillNB>), grid, block, 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
-  const unsigned per_unit = (unsigned)(((long long)a.rows * (D / 4) + kWave - 1) / kWave);
+  const unsigned per_unit = merge_groups(a.rows, D);
   hipLaunchKernelGGL((merge_kernel<D>), dim3(units * per_unit), dim3(kWave), 0, stream, a);
   return hipGetLastError();
 }
