@@ -17,8 +17,8 @@
 //     V scale as exact fp16 hi + lo pairs (the decode instead folds the scale into each row's P,
 //     which costs per row what this costs once);
 //   * waves 0 and 1 stage tiles 0 and 1 of each 32-token block into one of three LDS buffers
-//     shared by all eight waves, so two blocks are in flight while the workgroup computes one,
-//     with one barrier per block;
+//     shared by all eight waves, so two blocks are in flight while the workgroup computes one;
+//     one barrier per block publishes the staged block, a second its V operands;
 //   * blocks past the tile's last position are never loaded; a wave skips blocks past its last
 //     row's position and masks the blocks that cross its rows' positions;
 //   * each wave writes its rows: the output itself (one piece per context) or a partial that the
