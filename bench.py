@@ -227,7 +227,7 @@ def bench_prefill(kvq, torch, wl, inp, caches, stream, chunk, reps=5):
         "splits": splits,
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)},
-        "kernel": "kvq_prefill_attn: prefill_kernel (128-row tiles x context pieces) + merge_kernel",
+        "kernel": "kvq_prefill_attn: prefill_kernel (256-row tiles x context pieces) + merge_kernel",
     }
 
 

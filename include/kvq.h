@@ -298,7 +298,7 @@ size_t kvq_decode_workspace_bytes_win(int32_t n_seq, int32_t n_rows, int32_t n_q
  *                 [n_seq][chunk][n_q_heads], natural log, of the scaled logits.  A position that
  *                 sees no token (L - chunk + i < 0) gets out = 0 and lse = -inf.
  *   chunk         1 .. KVQ_MAX_CHUNK, and chunk * n_q_heads / num_kv_heads <= KVQ_MAX_PREFILL_ROWS.
- *   num_splits    0 = automatic; otherwise pieces per (sequence, KV head, 128-row tile).
+ *   num_splits    0 = automatic; otherwise pieces per (sequence, KV head, 256-row tile).
  *   workspace     device memory of at least kvq_prefill_workspace_bytes(...) bytes, 16-byte
  *                 aligned, never initialized by the caller; its contents after the call are
  *                 unspecified.

@@ -342,15 +342,13 @@ __device__ inline void clear_unseen_v(TileRaw<D, VB>& r, int tok0, int g, int lo
 //          sums of 2^(z - base) * (1, v);  it only moves up, in whole powers of two, when a block's
 //          largest logit and V scale would push p * v_scale past 2^15 (fp16 headroom), so most
 //          blocks rescale nothing and every rescale is exact.
-// The first half: Q K^T and the online softmax, leaving the block's p = 2^(z - base) per row and
-// token in pexp (the acc rescale included).
-template <int D, int NB, int VB, bool WIN, bool F8>
-__device__ __attribute__((always_inline)) inline void block_softmax(
-    TileRaw<D, VB> (&raw)[2], int blk, bool masked, float e5, const i32x4 (&qd)[NB][3][D / 64],
-    const u32x4 (&qw)[NB][D / 64][2], const float (&cz)[NB],
-    const int (&first_tok)[NB], const int (&last_tok)[NB], int g, floatx4 (&acc)[NB][D / 16], float (&base)[NB],
-    float (&l_run)[NB], float (&pexp)[NB][2][4]) {
-  constexpr int DB = D / 16;
+// Q K^T of one block: sc[tau][nb][e] is the dot product of the lane's query row with token
+// 4g + e of tile tau, in units of the query scale (before the K scale and cz).
+template <int D, int NB, int VB, bool F8>
+__device__ __attribute__((always_inline)) inline void block_scores(TileRaw<D, VB> (&raw)[2],
+                                                                   const i32x4 (&qd)[NB][3][D / 64],
+                                                                   const u32x4 (&qw)[NB][D / 64][2],
+                                                                   float (&sc)[2][NB][4]) {
   // ---- S^T = K Q^T: int8 codes on the int8 matrix cores with three digit planes of Q; E4M3
   // codes widened to fp16 (exactly) on the f16 matrix cores with Q's own fp16 values ----
   i32x4 sd[2][NB][3];
@@ -395,11 +393,35 @@ __device__ __attribute__((always_inline)) inline void block_softmax(
             sd[tau][nb][pc] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka, qd[nb][pc][jj], sd[tau][nb][pc], 0, 0, 0);
       }
     }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (F8) {
+          sc[tau][nb][e] = sf[tau][nb][e];
+        } else {
+          const int hm = (sd[tau][nb][0][e] << 8) + sd[tau][nb][1][e];  // |.| < 2^30: exact
+          sc[tau][nb][e] = __builtin_fmaf((float)hm, 256.0f, (float)sd[tau][nb][2][e]);
+        }
+      }
+}
+
+// The online softmax of one block from its scores: z = sc * k_scale * cz in log2 units, the
+// masks, and the block's p = 2^(z - base) per row and token in pexp (the acc rescale included).
+// ks_words: the K-scale words of the two tiles (fp16 scales of tokens 4g .. 4g + 3).
+template <int D, int NB, bool WIN>
+__device__ __attribute__((always_inline)) inline void block_softmax_scores(
+    const float (&sc)[2][NB][4], const uint32_t (&ks_words)[2][2], int blk, bool masked, float e5,
+    const float (&cz)[NB], const int (&first_tok)[NB], const int (&last_tok)[NB], int g,
+    floatx4 (&acc)[NB][D / 16], float (&base)[NB], float (&l_run)[NB], float (&pexp)[NB][2][4]) {
+  constexpr int DB = D / 16;
   float ks[2][4];
 #pragma unroll
   for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ks[tau][e] = h_at(raw[tau].ks, e);
+    for (int e = 0; e < 4; ++e) ks[tau][e] = h_at(ks_words[tau], e);
 
   // ---- logits and the online softmax (log2 units) ----
   bool rescale = false;
@@ -411,16 +433,7 @@ __device__ __attribute__((always_inline)) inline void block_softmax(
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float sc;
-        if constexpr (F8) {
-          sc = sf[tau][nb][e];
-        } else {
-          const int hm = (sd[tau][nb][0][e] << 8) + sd[tau][nb][1][e];  // |.| < 2^30: exact
-          sc = __builtin_fmaf((float)hm, 256.0f, (float)sd[tau][nb][2][e]);
-        }
-        z[tau][e] = sc * (ks[tau][e] * cz[nb]);
-      }
+      for (int e = 0; e < 4; ++e) z[tau][e] = sc[tau][nb][e] * (ks[tau][e] * cz[nb]);
     if (masked) {  // wave-uniform: only the blocks at the end of a context
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau)
@@ -468,6 +481,20 @@ __device__ __attribute__((always_inline)) inline void block_softmax(
         for (int e = 0; e < 4; ++e) acc[nb][db][e] *= alpha[nb];
   }
 
+}
+
+// The first half of the block step: Q K^T and the online softmax, leaving the block's
+// p = 2^(z - base) per row and token in pexp (the acc rescale included).
+template <int D, int NB, int VB, bool WIN, bool F8>
+__device__ __attribute__((always_inline)) inline void block_softmax(
+    TileRaw<D, VB> (&raw)[2], int blk, bool masked, float e5, const i32x4 (&qd)[NB][3][D / 64],
+    const u32x4 (&qw)[NB][D / 64][2], const float (&cz)[NB],
+    const int (&first_tok)[NB], const int (&last_tok)[NB], int g, floatx4 (&acc)[NB][D / 16], float (&base)[NB],
+    float (&l_run)[NB], float (&pexp)[NB][2][4]) {
+  float sc[2][NB][4];
+  block_scores<D, NB, VB, F8>(raw, qd, qw, sc);
+  const uint32_t ksw[2][2] = {{raw[0].ks[0], raw[0].ks[1]}, {raw[1].ks[0], raw[1].ks[1]}};
+  block_softmax_scores<D, NB, WIN>(sc, ksw, blk, masked, e5, cz, first_tok, last_tok, g, acc, base, l_run, pexp);
 }
 
 // The second half: O^T += V^T P^T, one 32-dim scale group at a time, with the V scale folded

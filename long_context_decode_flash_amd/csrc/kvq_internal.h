@@ -75,6 +75,6 @@ hipError_t launch_append(int head_dim, const AppendArgs& a, hipStream_t stream);
 hipError_t launch_decode(int head_dim, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(int head_dim, const DecodeArgs& a, hipStream_t stream);
 
-constexpr int kPrefillRowsPerTile = 128;  // query rows of one prefill workgroup (32 per wave)
+constexpr int kPrefillRowsPerTile = 256;  // query rows of one prefill workgroup (32 per wave)
 
 }  // namespace kvq

@@ -8,14 +8,15 @@
 // decode's multi-row attention with C rows; what changes is the shape.  Every cached byte now
 // meets thousands of query rows, so the work is dense matrix-core work, not a byte stream:
 //
-//   * one workgroup of 8 waves per (sequence, KV head, tile of 128 query rows, piece of the
+//   * one workgroup of 8 waves per (sequence, KV head, tile of 256 query rows, piece of the
 //     context); the rows of a KV head are (chunk position, query head of its group) pairs in
-//     position-major order, and wave w owns rows 16w .. 16w + 15 of the tile: the decode's
-//     Q K^T (int8 on three exact digit planes of the query, or fp16 for E4M3 keys) and online
-//     softmax for one 16-row block;
-//   * P V takes its V operands from LDS, built once per block for all eight waves: codes times
-//     V scale as exact fp16 hi + lo pairs (the decode instead folds the scale into each row's P,
-//     which costs per row what this costs once);
+//     position-major order, and wave w owns rows 32w .. 32w + 31 of the tile as two 16-row
+//     blocks, with the decode's online softmax;
+//   * both products take their K and V operands from LDS, built once per block for all eight
+//     waves: K codes widened to fp16 (exact; the K scale multiplies the logit) against the
+//     rows' own fp16 query words, and V codes times V scale as exact fp16 hi + lo pairs (the
+//     decode instead folds the scale into each row's P, which costs per row what this costs
+//     once); every operand read serves both row blocks of a wave;
 //   * waves 0 and 1 stage tiles 0 and 1 of each 32-token block into one of three LDS buffers
 //     shared by all eight waves, so two blocks are in flight while the workgroup computes one;
 //     one barrier per block publishes the staged block, a second its V operands;
@@ -102,54 +103,116 @@ __device__ inline void build_vhat(const uint8_t* src, VHat<D / 32>& vh, int it, 
   vh.w[j][dh][1][lane] = u32x4{lo[0], lo[1], lo[2], lo[3]};
 }
 
-// The K codes and K scales of a staged tile for this lane (the K part of read_tile).
-template <int D, int VB>
-__device__ inline void read_tile_k(TileRaw<D, VB>& r, const uint8_t* src, int lane) {
+// ---- K of a staged block as fp16 operands, built once per workgroup ----
+// For tile tau and 64-dim step jj, lane l holds the A operand of Q K^T for token l%16 of the tile
+// and the 16 dims 16(4jj + l/16) .. + 15, as two half8 words (dims + 0..7, + 8..15): the codes
+// widened to fp16, exact for int8 and E4M3 alike; the K scale multiplies the logit.
+template <int D>
+struct KHat {
+  u32x4 w[2][D / 64][2][kWave];  // [tile][64-dim step][half][lane]
+};
+
+template <int D, int VB, bool F8>
+__device__ inline void build_khat(const uint8_t* src, KHat<D>& kh, int it, int lane) {
   using S = Stage<D, VB>;
+  const int tau = it / (D / 64), jj = it % (D / 64);
+  const u32x4 x = *(const u32x4*)(src + tau * S::kTileBytes + S::kK + 1024 * jj + 16 * lane);
+  const half2v off = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  const uint32_t xw[4] = {x[0], x[1], x[2], x[3]};
+  uint32_t o[8];
 #pragma unroll
-  for (int jj = 0; jj < TileRaw<D, VB>::kLoadsK; ++jj) r.k[jj] = *(const u32x4*)(src + S::kK + 1024 * jj + 16 * lane);
-  const u32x2 ks = *(const u32x2*)(src + S::kKs + 8 * (lane >> 4));
-  r.ks[0] = ks[0];
-  r.ks[1] = ks[1];
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (F8) {
+      o[2 * i] = e4m3x2_to_h2<false>(xw[i]);
+      o[2 * i + 1] = e4m3x2_to_h2<true>(xw[i]);
+    } else {
+      // bytes (0, 1) and (2, 3) into the low bytes of the halves; byte ^ 0x80 is code + 128 and
+      // 0x6400 | m is the fp16 value 1024 + m, so the half minus 1152 is the code, exactly
+      o[2 * i] = as_u32(as_h2(__builtin_amdgcn_perm(xw[i], xw[i], 0x0C010C00u) ^ 0x64806480u) + off);
+      o[2 * i + 1] = as_u32(as_h2(__builtin_amdgcn_perm(xw[i], xw[i], 0x0C030C02u) ^ 0x64806480u) + off);
+    }
+  }
+  kh.w[tau][jj][0][lane] = u32x4{o[0], o[1], o[2], o[3]};
+  kh.w[tau][jj][1][lane] = u32x4{o[4], o[5], o[6], o[7]};
+}
+
+// Q K^T from the shared K operands and the rows' own fp16 query words: sc[tau][nb][e] is the
+// dot product of the lane's query row (block nb) with token 4g + e of tile tau.
+template <int D, int NB>
+__device__ __attribute__((always_inline)) inline void block_scores_khat(const KHat<D>& kh, int lane,
+                                                                        const u32x4 (&qw)[NB][D / 64][2],
+                                                                        float (&sc)[2][NB][4]) {
+  floatx4 sf[2][NB];
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) sf[tau][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int jj = 0; jj < D / 64; ++jj)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        const half8 k8 = __builtin_bit_cast(half8, kh.w[tau][jj][hf][lane]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          sf[tau][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k8, __builtin_bit_cast(half8, qw[nb][jj][hf]),
+                                                               sf[tau][nb], 0, 0, 0);
+      }
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const floatx4 v = sf[tau][nb];
+      sc[tau][nb][0] = v[0];
+      sc[tau][nb][1] = v[1];
+      sc[tau][nb][2] = v[2];
+      sc[tau][nb][3] = v[3];
+    }
 }
 
 // O^T += V^T P^T from the shared operands: P as fp16 hi + lo with 2^(e5 - 15) applied, three
-// products per operand pair (hi*hi, hi*lo, lo*hi; lo*lo is below 2^-22 of the product).
+// products per operand pair (hi*hi, hi*lo, lo*hi; lo*lo is below 2^-22 of the product); each V
+// operand read from LDS serves every row block of the wave.
 template <int D, int NB>
 __device__ __attribute__((always_inline)) inline void block_pv_vhat(const VHat<D / 32>& vh, int lane,
                                                                     const float (&pexp)[NB][2][4], float pf,
                                                                     floatx4 (&acc)[NB][D / 16]) {
   constexpr int NG = D / 32;
   constexpr uint32_t kOne = 0x3C003C00u;  // fp16 1.0 in both halves
+  uint32_t hw[NB][4], lw[NB][4];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    uint32_t hw[4], lw[4];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
-      mix_hi_lo<0>(pexp[nb][tau][0] * pf, kOne, pexp[nb][tau][2] * pf, kOne, hw[2 * tau], lw[2 * tau]);
-      mix_hi_lo<0>(pexp[nb][tau][1] * pf, kOne, pexp[nb][tau][3] * pf, kOne, hw[2 * tau + 1], lw[2 * tau + 1]);
+      mix_hi_lo<0>(pexp[nb][tau][0] * pf, kOne, pexp[nb][tau][2] * pf, kOne, hw[nb][2 * tau], lw[nb][2 * tau]);
+      mix_hi_lo<0>(pexp[nb][tau][1] * pf, kOne, pexp[nb][tau][3] * pf, kOne, hw[nb][2 * tau + 1],
+                   lw[nb][2 * tau + 1]);
     }
     // two wait states between the inline-asm writes of P and the matrix-core reads (the
     // compiler's hazard tracking does not see inline-asm results)
-    asm("s_nop 1" : "+v"(hw[0]), "+v"(hw[1]), "+v"(hw[2]), "+v"(hw[3]), "+v"(lw[0]), "+v"(lw[1]), "+v"(lw[2]),
-        "+v"(lw[3]));
-    const half8 phi = __builtin_bit_cast(half8, u32x4{hw[0], hw[1], hw[2], hw[3]});
-    const half8 plo = __builtin_bit_cast(half8, u32x4{lw[0], lw[1], lw[2], lw[3]});
+    asm("s_nop 1" : "+v"(hw[nb][0]), "+v"(hw[nb][1]), "+v"(hw[nb][2]), "+v"(hw[nb][3]), "+v"(lw[nb][0]),
+        "+v"(lw[nb][1]), "+v"(lw[nb][2]), "+v"(lw[nb][3]));
+  }
 #pragma unroll
-    for (int j = 0; j < NG; ++j)
+  for (int j = 0; j < NG; ++j)
 #pragma unroll
-      for (int dh = 0; dh < 2; ++dh) {
-        const half8 vhi = __builtin_bit_cast(half8, vh.w[j][dh][0][lane]);
-        const half8 vlo = __builtin_bit_cast(half8, vh.w[j][dh][1][lane]);
+    for (int dh = 0; dh < 2; ++dh) {
+      const half8 vhi = __builtin_bit_cast(half8, vh.w[j][dh][0][lane]);
+      const half8 vlo = __builtin_bit_cast(half8, vh.w[j][dh][1][lane]);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const half8 phi = __builtin_bit_cast(half8, u32x4{hw[nb][0], hw[nb][1], hw[nb][2], hw[nb][3]});
+        const half8 plo = __builtin_bit_cast(half8, u32x4{lw[nb][0], lw[nb][1], lw[nb][2], lw[nb][3]});
         floatx4& c = acc[nb][2 * j + dh];
         c = __builtin_amdgcn_mfma_f32_16x16x32_f16(vhi, phi, c, 0, 0, 0);
         c = __builtin_amdgcn_mfma_f32_16x16x32_f16(vhi, plo, c, 0, 0, 0);
         c = __builtin_amdgcn_mfma_f32_16x16x32_f16(vlo, phi, c, 0, 0, 0);
       }
-  }
+    }
 }
 
-// NB: 16-row blocks per wave; the 128 rows of a tile take 128 / (16 NB) waves.
+// NB: 16-row blocks per wave; the rows of a tile take kPrefillRowsPerTile / (16 NB) waves.
 template <int D, int VB, bool F8, int NB>
 __global__ __launch_bounds__(kPrefillRowsPerTile / 16 / NB * kWave) void prefill_kernel(DecodeArgs a) {
   constexpr int kRowsPerWave = 16 * NB;
@@ -162,6 +225,7 @@ __global__ __launch_bounds__(kPrefillRowsPerTile / 16 / NB * kWave) void prefill
   constexpr int NWAVES = kPrefillRowsPerTile / kRowsPerWave;
   __shared__ __attribute__((aligned(16))) uint8_t s_stage[NSTAGE][BS];
   __shared__ VHat<D / 32> s_vh;
+  __shared__ KHat<D> s_kh;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -249,9 +313,9 @@ __global__ __launch_bounds__(kPrefillRowsPerTile / 16 / NB * kWave) void prefill
     if (n_blocks > 1) issue(1);
   }
 
-  i32x4 qd[NB][3][D / 64];
-  float cz[NB];
-  prepare_queries<D, NB, F8>(qw, a.scale_log2, qd, cz);
+  float cz[NB];  // the query's fp16 words are the B operands as they are
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) cz[nb] = a.scale_log2;
 
   floatx4 acc[NB][DB];
   float base[NB], l_run[NB];
@@ -305,18 +369,26 @@ __global__ __launch_bounds__(kPrefillRowsPerTile / 16 / NB * kWave) void prefill
       const half2v vfac = {f, f};
 #pragma unroll
       for (int it = w; it < 2 * (D / 32); it += NWAVES) build_vhat<D, VB, F8>(src, s_vh, it, lane, blk * kBlock, Lc, vfac);
+#pragma unroll
+      for (int it = w; it < 2 * (D / 64); it += NWAVES) build_khat<D, VB, F8>(src, s_kh, it, lane);
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();  // the operands are complete
     asm volatile("" ::: "memory");
     if (blk * kBlock > w_any) continue;  // no row of this wave sees the block (wave-uniform)
     const bool masked = blk * kBlock + kBlock - 1 > w_all;
-    TileRaw<D, VB> raw[2];
-    read_tile_k<D, VB>(raw[0], src, lane);
-    read_tile_k<D, VB>(raw[1], src + TB, lane);
+    float sc[2][NB][4];
+    block_scores_khat<D, NB>(s_kh, lane, qw, sc);
+    uint32_t ksw[2][2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      const u32x2 kw = *(const u32x2*)(src + tau * TB + Stage<D, VB>::kKs + 8 * g);
+      ksw[tau][0] = kw[0];
+      ksw[tau][1] = kw[1];
+    }
     float pexp[NB][2][4];
-    block_softmax<D, NB, VB, false, F8>(raw, blk, masked, e5, qd, qw, cz, first_tok, last_tok, g, acc, base, l_run,
-                                        pexp);
+    block_softmax_scores<D, NB, false>(sc, ksw, blk, masked, e5, cz, first_tok, last_tok, g, acc, base, l_run,
+                                       pexp);
     block_pv_vhat<D, NB>(s_vh, lane, pexp, __builtin_ldexpf(1.0f, (int)e5 - 15), acc);
   }
 
@@ -342,11 +414,12 @@ __global__ __launch_bounds__(kPrefillRowsPerTile / 16 / NB * kWave) void prefill
   }
 }
 
-// One 16-row block per wave, eight waves per tile: 234 VGPRs and no AGPRs, so two waves share
-// each SIMD and one's vector work overlaps the other's matrix-core work.  Two 16-row blocks per
-// wave (four waves) need all 256 VGPRs plus AGPR spills, one wave per SIMD: the 1,024-position
-// chunk of the 184K-token pool measured 14.0 ms that way against 11.6 ms this way.
-constexpr int kPrefillNB = 1;
+// Two 16-row blocks per wave, eight waves per tile (two waves per SIMD).  The query's fp16 words
+// (64 VGPRs at head dim 256, against 96 for three int8 digit planes) leave room for the second
+// row block; at head dim 256 the kernel still spills about 20 dwords per lane.  On the
+// 1,024-position chunk of the 184K-token pool this took 10.3 ms, against 11.6 ms for one 16-row
+// block per wave with int8 digit planes (128-row tiles), and 14.0 ms for four waves of two.
+constexpr int kPrefillNB = 2;
 
 template <int D>
 hipError_t launch_prefill_d(const DecodeArgs& a, hipStream_t stream) {

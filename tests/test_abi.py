@@ -294,11 +294,11 @@ def test_prefill_validation(lib):
 
 def test_prefill_split_plan(lib):
     """The prefill plan fills the 256 CUs in whole rounds where it can: the 1,024-position chunk
-    of two 92,160-token sequences (4 KV heads, 6 query heads each) has 2 x 4 x 48 row tiles, and
-    two pieces per tile make 768 workgroups (3 rounds); the workspace holds each piece's
-    partials."""
+    of two 92,160-token sequences (4 KV heads, 6 query heads each) has 2 x 4 x 24 tiles of 256
+    rows, and four pieces per tile make 768 workgroups (3 rounds); the workspace holds each
+    piece's partials."""
     s = kvq.prefill_num_splits(2, 1024, 24, 4, 92160)
-    assert s == 2 and (2 * 4 * 48 * s) % 256 == 0
+    assert s == 4 and (2 * 4 * 24 * s) % 256 == 0
     nblk = 92160 // 32
     assert kvq.prefill_num_splits(1, 1024, 24, 4, 92160, 3) == 3
     assert kvq.prefill_num_splits(1, 1, 1, 1, 64) == 1  # too few blocks to split
