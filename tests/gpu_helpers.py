@@ -11,6 +11,8 @@ import oracle
 from long_context_decode_flash_amd import workloads as W
 
 TOL_ABS = 2e-3  # attention max-abs bound against the fp64 oracle
+TOL_REL = 1e-3  # the same max-abs error, relative to the largest |ref| of the compared outputs
+LSE_ABS = 1e-4  # log-sum-exp max-abs bound (natural-log units)
 
 
 def say(*a):
@@ -104,6 +106,29 @@ def full_workload(name: str):
     """(inputs, oracle pool) of a full-size workload, cached across tests."""
     inp = W.generate(W.WORKLOADS[name])
     return inp, oracle_fill(inp)
+
+
+def assert_close(tag, got, ref, tol_abs=TOL_ABS, tol_rel=TOL_REL):
+    """Attention outputs against the oracle, element by element: max-abs within tol_abs and
+    within tol_rel of the largest |ref| (at long contexts |out| is only ~sqrt(e/N), so the
+    absolute bound alone would be loose)."""
+    assert np.all(np.isfinite(got)), f"{tag}: non-finite output"
+    mx = report(tag, got, ref)
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    assert mx <= tol_abs, f"{tag}: max-abs {mx:.3e} > {tol_abs:g}"
+    assert mx <= tol_rel * scale, f"{tag}: max-abs {mx:.3e} > {tol_rel:g} * max|ref| = {tol_rel * scale:.3e}"
+    return mx
+
+
+def assert_lse(tag, got, ref, tol=LSE_ABS):
+    """Log-sum-exp: -inf exactly where the oracle has it (a row that sees no token), else
+    within tol."""
+    fin = np.isfinite(ref)
+    assert np.array_equal(fin, np.isfinite(got)), f"{tag}: lse finiteness differs"
+    assert np.all(got[~fin] == ref[~fin]), f"{tag}: lse of rows that see nothing"
+    err = float(np.max(np.abs(got[fin] - ref[fin]), initial=0.0))
+    assert err <= tol, f"{tag}: lse max-abs {err:.3e} > {tol:g}"
+    return err
 
 
 def report(tag, got, ref):

@@ -284,7 +284,69 @@ def check_window_ring(o):
     return True
 
 
-CHECKS = [check_window_ring, check_fp16, check_quantizer_golden, check_quantizer_argmin, check_format_golden,
+def clamped_page_brute(inp, bad_table, vqmax=7):
+    """Pure-Python attention of ``inp`` read through ``bad_table``, whose out-of-range entries
+    name the nearest page in range (the library header's contract: an id below 0 reads page 0,
+    one at or past num_pages reads the last page).  The pool was filled through the valid
+    table, so each slot of a clamped page holds the token the valid table put there, or nothing
+    (zero codes and scales) where no token was appended."""
+    wl = inp.wl
+    P, H, D = wl.page_size, wl.num_kv_heads, wl.head_dim
+    owner = {}  # physical page -> (sequence, logical page) of the valid table
+    for b in range(wl.n_seq):
+        for n in range(-(-int(inp.seq_lens[b]) // P)):
+            owner[int(inp.page_table[b, n])] = (b, n)
+    n, L = wl.n_seq, wl.seq_len
+    kc = np.zeros((n, L, H, D), np.int8)
+    vc = np.zeros((n, L, H, D), np.int8)
+    ks = np.zeros((n, L, H), np.uint16)
+    vs = np.zeros((n, L, H, D // 32), np.uint16)
+    for b in range(n):
+        for t in range(int(inp.seq_lens[b])):
+            phys = min(max(int(bad_table[b, t // P]), 0), wl.pool_pages - 1)
+            if phys not in owner:
+                continue
+            b2, n2 = owner[phys]
+            t2 = n2 * P + t % P
+            if t2 >= int(inp.seq_lens[b2]):
+                continue
+            for h in range(H):
+                kc[b, t, h], ks[b, t, h], vc[b, t, h], vs[b, t, h] = brute.quantize_token_np(
+                    inp.k[b2, t2, h], inp.v[b2, t2, h], vqmax)
+    return brute.attention_brute(inp.q_bits, kc, ks, vc, vs, inp.seq_lens, wl.n_rows,
+                                 wl.n_q_heads, H, 1.0 / math.sqrt(D))
+
+
+def clamp_case():
+    """Two sequences whose valid table leaves page 0 and the last page holding different
+    tokens, and a table with entries -1, -7, num_pages + 5 and 2^31 - 1 in place of valid ones."""
+    inp = W.custom(n_seq=2, seq_lens=(45, 29), num_kv_heads=2, n_q_heads=6, head_dim=64,
+                   page_size=16, n_rows=2, extra_pages=3, seed=4242)
+    wl = inp.wl
+    used = {int(inp.page_table[b, n]) for b in range(wl.n_seq)
+            for n in range(-(-int(inp.seq_lens[b]) // wl.page_size))}
+    assert 0 in used and wl.pool_pages - 1 in used, "case must put tokens in both end pages"
+    bad = inp.page_table.copy()
+    bad[0, 1] = -1
+    bad[0, 2] = wl.pool_pages + 5
+    bad[1, 0] = 2 ** 31 - 1
+    bad[1, 1] = -7
+    return inp, bad
+
+
+def check_page_clamp(o):
+    """Out-of-range page-table entries read the clamped page, against the brute force."""
+    inp, bad = clamp_case()
+    wl = inp.wl
+    pool = _fill(o, inp)
+    out, lse = o.decode_attn(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
+                             inp.q_bits, bad, inp.seq_lens, wl.n_rows, wl.n_q_heads)
+    out_b, lse_b = clamped_page_brute(inp, bad)
+    return (np.allclose(out, out_b, rtol=0, atol=1e-12) and
+            np.allclose(lse, lse_b, rtol=0, atol=1e-11))
+
+
+CHECKS = [check_page_clamp, check_window_ring, check_fp16, check_quantizer_golden, check_quantizer_argmin, check_format_golden,
           check_brute_force, check_closed_forms, check_large_logits, check_format_golden_v8,
           check_brute_force_v8, check_e4m3, check_brute_force_f8]
 

@@ -38,13 +38,8 @@ def _prefill(inp, cache, num_splits=0, max_seq_len=None):
 
 
 def _check(tag, out, lse, ref_out, ref_lse):
-    assert np.all(np.isfinite(out)), tag
-    err = H.report(tag, out, ref_out)
-    assert err <= H.TOL_ABS, tag
-    assert err <= 1e-3 * max(float(np.max(np.abs(ref_out))), 1e-30), tag
-    fin = np.isfinite(ref_lse)
-    assert np.array_equal(fin, np.isfinite(lse)), tag
-    assert np.max(np.abs(lse[fin] - ref_lse[fin]), initial=0.0) <= 1e-4, tag
+    H.assert_close(tag, out, ref_out)
+    H.assert_lse(tag, lse, ref_lse)
 
 
 @FMTS

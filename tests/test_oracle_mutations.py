@@ -52,6 +52,10 @@ MUTATIONS = {
                         "q + (((size_t)b * R + (R - 1)) * Hq + hq) * D"),
     "no_normalize": ("for (int t = first; t <= last; ++t) w[t] /= sum;", ""),
     "no_running_max": ("if (w[t] > m) m = w[t];", "m = 0.0;"),
+    # page-table entries outside the pool (clamped into [0, num_pages))
+    "page_clamp_low_wraps": ("if (page < 0) page = 0;", "if (page < 0) page = num_pages - 1;"),
+    "page_clamp_high_to_zero": ("if (page >= num_pages) page = num_pages - 1;",
+                                "if (page >= num_pages) page = 0;"),
     # K8/V8 (8-bit V codes)
     "v8_qmax": ("const int vqmax = vb == 8 ? 127 : 7;", "const int vqmax = vb == 8 ? 63 : 7;"),
     "v8_dim_pair_bit": ("(size_t)4 * ((d / 16) % 2) + (size_t)(t % 4)",

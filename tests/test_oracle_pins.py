@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import oracle
-from tests import brute
+from tests import brute, pin_battery
 from long_context_decode_flash_amd import workloads as W
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -428,3 +428,22 @@ def test_rows_that_see_no_token_give_zero_and_minus_inf():
     out, lse = _attend(o, inp, _fill(o, inp))
     assert np.all(out[0, :2] == 0) and np.all(np.isneginf(lse[0, :2]))
     assert np.all(np.isfinite(lse[0, 2:]))
+
+
+def test_out_of_range_page_ids_read_the_clamped_page():
+    """Page-table entries below 0 read page 0 and entries at or past num_pages read the last
+    page (the library header's out-of-range contract), against a pure-Python brute force that
+    resolves each clamped page to the tokens the valid table stored there (or to unwritten,
+    all-zero slots)."""
+    o = oracle.default()
+    assert pin_battery.check_page_clamp(o)
+    # and the clamp is all there is to it: the same table with the entries clamped by hand
+    inp, bad = pin_battery.clamp_case()
+    wl = inp.wl
+    pool = _fill(o, inp)
+    fixed = np.clip(bad, 0, wl.pool_pages - 1).astype(np.int32)
+    a = o.decode_attn(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
+                      inp.q_bits, bad, inp.seq_lens, wl.n_rows, wl.n_q_heads)
+    b = o.decode_attn(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
+                      inp.q_bits, fixed, inp.seq_lens, wl.n_rows, wl.n_q_heads)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
