@@ -156,7 +156,7 @@ int kvq_append(void* pool, int32_t num_pages, int32_t page_size, int32_t num_kv_
  * engine's --spec mtp --draft-tokens 3 in the forum post's launch-flag table.)
  *
  *   pool, num_pages, page_size, num_kv_heads, head_dim   as for kvq_append (read only).
- *   q             device fp16 bits [n_seq][n_rows][n_q_heads][head_dim].
+ *   q             device fp16 bits [n_seq][n_rows][n_q_heads][head_dim], 16-byte aligned.
  *   page_table    device int32 [n_seq][max_pages_per_seq], logical -> physical page.  Entries
  *                 up to ceil(max_seq_len / page_size) of a row may be read, but only the first
  *                 ceil(L / page_size) are used; an entry outside [0, num_pages) is clamped into
@@ -170,7 +170,7 @@ int kvq_append(void* pool, int32_t num_pages, int32_t page_size, int32_t num_kv_
  *                 pieces each (sequence, KV head) context is cut into (one workgroup each),
  *                 clamped to the number of 32-token blocks and to 128.  The result does not depend on it
  *                 beyond fp32 rounding.
- *   out           device fp32 [n_seq][n_rows][n_q_heads][head_dim].
+ *   out           device fp32 [n_seq][n_rows][n_q_heads][head_dim], 16-byte aligned.
  *   lse           device fp32 [n_seq][n_rows][n_q_heads], or NULL.
  *   workspace     device scratch of at least kvq_decode_workspace_bytes(...) bytes, 16-byte
  *                 aligned, for the pieces' partial results (numerators, running max and sum).
@@ -179,6 +179,8 @@ int kvq_append(void* pool, int32_t num_pages, int32_t page_size, int32_t num_kv_
  * With more than one piece per context the call is two launches on `stream`: the split-KV
  * attention, then the log-sum-exp merge of the pieces.
  * Returns KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE or KVQ_ERR_HIP.
+ * KVQ_ERR_UNSUPPORTED also covers a call whose attention or merge grid would count 2^32
+ * work-items or more (HIP's grid limit): such a call is refused, never launched truncated.
  */
 int kvq_decode_attn(const void* pool, int32_t num_pages, int32_t page_size,
                     int32_t num_kv_heads, int32_t head_dim, const uint16_t* q,
@@ -305,7 +307,8 @@ size_t kvq_decode_workspace_bytes_win(int32_t n_seq, int32_t n_rows, int32_t n_q
  * Other arguments, the KV formats, the page table and the device-data contract are those of
  * kvq_decode_attn_fmt.  Stream-ordered, allocates nothing, never synchronizes.  Returns KVQ_OK,
  * KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE or KVQ_ERR_HIP; every argument error is
- * found on the host before any launch. */
+ * found on the host before any launch (KVQ_ERR_UNSUPPORTED for a grid of 2^32 work-items or more,
+ * as for kvq_decode_attn). */
 int kvq_prefill_attn(int32_t kv_format, const void* pool, int32_t num_pages, int32_t page_size,
                      int32_t num_kv_heads, int32_t head_dim, const uint16_t* q,
                      const int32_t* page_table, const int32_t* seq_lens, int32_t n_seq,

@@ -64,6 +64,17 @@ size_t workspace_for(long long units, int splits, int rows, int head_dim) {
   return acc + ml;
 }
 
+// Every launch of a call counts fewer than 2^32 work-items (HIP's grid limit): the attention
+// grid (units x row tiles x splits workgroups of `threads`) and, with more than one split, the
+// merge grid (units x merge_groups(rows, D) workgroups of one wave).
+bool grids_fit(long long units, int row_tiles, int splits, int threads, int rows, int head_dim) {
+  const unsigned long long lim = 1ULL << 32;
+  const unsigned long long attn = (unsigned long long)units * row_tiles * splits * threads;
+  const unsigned long long merge =
+      splits > 1 ? (unsigned long long)units * kvq::merge_groups(rows, head_dim) * kvq::kWave : 0;
+  return attn < lim && merge < lim;
+}
+
 int pool_args_ok(const void* pool, int32_t num_pages, int32_t page_size, int32_t num_kv_heads,
                  int32_t head_dim, int vb) {
   if (!pool || num_pages <= 0 || num_kv_heads <= 0 || page_size <= 0) return KVQ_ERR_ARG;
@@ -187,13 +198,15 @@ int decode_impl(int32_t kv_format, const void* pool, int32_t num_pages, int32_t 
   // a fused step appends only tokens some row sees (the pieces that attend them write them)
   if (window > 0 && (long long)n_new > (long long)window + n_rows - 1) return KVQ_ERR_ARG;
   if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return KVQ_ERR_ARG;
-  if (((uintptr_t)q & 15) != 0) return KVQ_ERR_ARG;
+  if (((uintptr_t)q & 15) != 0 || ((uintptr_t)out & 15) != 0) return KVQ_ERR_ARG;
   Plan plan;
   rc = plan_splits(n_seq, num_kv_heads, (int)span_tokens(max_seq_len, n_rows, window), num_splits,
                    &plan);
   if (rc != KVQ_OK) return rc;
   const int rows = group * n_rows;
   const long long units = (long long)n_seq * num_kv_heads;
+  if (!grids_fit(units, 1, plan.splits, kvq::kWave * kvq::kWavesPerGroup, rows, head_dim))
+    return KVQ_ERR_UNSUPPORTED;
   const size_t need = workspace_for(units, plan.splits, rows, head_dim);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15) != 0)
     return KVQ_ERR_WORKSPACE;
@@ -434,6 +447,8 @@ int kvq_prefill_attn(int32_t kv_format, const void* pool, int32_t num_pages, int
   rc = plan_prefill(n_seq, num_kv_heads, rows, max_seq_len, num_splits, &plan, &tiles);
   if (rc != KVQ_OK) return rc;
   const long long units = (long long)n_seq * num_kv_heads;
+  if (!grids_fit(units, tiles, plan.splits, kvq::kPrefillThreads, rows, head_dim))
+    return KVQ_ERR_UNSUPPORTED;
   const size_t need = workspace_for(units, plan.splits, rows, head_dim);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15) != 0)
     return KVQ_ERR_WORKSPACE;

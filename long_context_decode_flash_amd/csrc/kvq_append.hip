@@ -51,6 +51,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     uint8_t* st = s_tile[wv];
 #pragma unroll
     for (int i = 0; i < kTokensPerWave; ++i) store_row<D, VB, F8>(st, kTile, i, rv[i], lane);
+    wave_lds_order();  // the copies below read bytes other lanes wrote
     const int page = (int)(s0 / P), tile = (int)(s0 % P) / kTile;
     uint8_t* blk = a.pool + ((size_t)page * a.num_kv_heads + h) * block_bytes(P, D, VB);
     copy16<D>(blk + (size_t)kTile * D * tile, st, kTile * D, lane);                                 // K codes

@@ -638,12 +638,6 @@ __device__ __attribute__((always_inline)) inline void prepare_queries(
 // row of 16 lanes, so the merge needs no LDS and no barrier.  The partials come from the
 // previous launch on the stream.  On the 184K-token step (32 splits) one lane per item took
 // about 1 us longer per step than 4 lanes, and 8 and 16 lanes measured 0.3-0.6 us below 4.
-constexpr int kMergeLanes = 8;                       // lanes per output item (4, 8 or 16)
-constexpr int kMergeItems = kWave / kMergeLanes;     // items per wave
-
-__host__ __device__ constexpr unsigned merge_groups(int rows, int head_dim) {
-  return (unsigned)(((long long)rows * (head_dim / 4) + kMergeItems - 1) / kMergeItems);
-}
 
 template <int D>
 __global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a) {

@@ -236,6 +236,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
           else *(uint32_t*)vs = 0u;
         }
       }
+      if (masked) wave_lds_order();  // every lane reads the scales lanes < 32 cleared
       TileRaw<D, VB> raw[2];
       read_tile<D, VB>(raw[0], src, lane);
       read_tile<D, VB>(raw[1], src + Stage<D, VB>::kTileBytes, lane);
@@ -343,7 +344,7 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
     launch_attn<D, false>(a, dim3(grid), block, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
-  const unsigned per_unit = merge_groups(a.rows, D);
+  const unsigned per_unit = (unsigned)merge_groups(a.rows, D);  // grid size checked on the host
   hipLaunchKernelGGL((merge_kernel<D>), dim3(units * per_unit), dim3(kWave), 0, stream, a);
   return hipGetLastError();
 }

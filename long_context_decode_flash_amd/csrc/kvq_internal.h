@@ -76,5 +76,14 @@ hipError_t launch_decode(int head_dim, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(int head_dim, const DecodeArgs& a, hipStream_t stream);
 
 constexpr int kPrefillRowsPerTile = 256;  // query rows of one prefill workgroup (32 per wave)
+constexpr int kPrefillThreads = 512;      // 8 waves per prefill workgroup
+
+// The split merge launch: kMergeLanes lanes per (unit, query row, 4 dims) item, kMergeItems
+// items per 64-lane workgroup, merge_groups(rows, D) workgroups per unit.
+constexpr int kMergeLanes = 8;                       // lanes per output item (4, 8 or 16)
+constexpr int kMergeItems = kWave / kMergeLanes;     // items per wave
+__host__ __device__ constexpr unsigned long long merge_groups(int rows, int head_dim) {
+  return ((unsigned long long)rows * (head_dim / 4) + kMergeItems - 1) / kMergeItems;
+}
 
 }  // namespace kvq

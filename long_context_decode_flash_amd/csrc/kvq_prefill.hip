@@ -424,8 +424,8 @@ constexpr int kPrefillNB = 2;
 template <int D>
 hipError_t launch_prefill_d(const DecodeArgs& a, hipStream_t stream) {
   const unsigned units = (unsigned)((long long)a.n_seq * a.num_kv_heads);
-  const dim3 grid(units * (unsigned)a.row_tiles * (unsigned)a.splits),
-      block(kPrefillRowsPerTile / 16 / kPrefillNB * kWave);
+  static_assert(kPrefillRowsPerTile / 16 / kPrefillNB * kWave == kPrefillThreads, "prefill block");
+  const dim3 grid(units * (unsigned)a.row_tiles * (unsigned)a.splits), block(kPrefillThreads);
   if (a.fp8)
     hipLaunchKernelGGL((prefill_kernel<D, 8, true, kPrefillNB>), grid, block, 0, stream, a);
   else if (a.vbits == 8)
@@ -434,7 +434,7 @@ hipError_t launch_prefill_d(const DecodeArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((prefill_kernel<D, 4, false, kPrefillNB>), grid, block, 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
-  const unsigned per_unit = merge_groups(a.rows, D);
+  const unsigned per_unit = (unsigned)merge_groups(a.rows, D);  // grid size checked on the host
   hipLaunchKernelGGL((merge_kernel<D>), dim3(units * per_unit), dim3(kWave), 0, stream, a);
   return hipGetLastError();
 }

@@ -13,6 +13,15 @@
 
 namespace kvq {
 
+// Lanes of one wave hand data to each other through LDS (one lane writes bytes another lane
+// reads): this ordering point keeps the compiler from moving the reads above the writes.  It
+// emits no instruction; a wave's LDS operations complete in program order.
+__device__ inline void wave_lds_order() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ inline float wave_max(float x, int width) {
   // butterfly over groups of `width` lanes (width a power of two <= 64)
   for (int off = width / 2; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));

@@ -173,6 +173,12 @@ def test_decode_validation(lib):
     assert decode_rc(lib, q=ctypes.c_void_p(0x100002)) == E.KVQ_ERR_ARG
 
 
+def test_decode_rejects_misaligned_out(lib):
+    """out is written with 16-byte stores: a misaligned pointer is refused on the host."""
+    assert decode_rc(lib, out=ctypes.c_void_p(0x100004)) == kvq.KVQ_ERR_ARG
+    assert step_rc(lib, out=ctypes.c_void_p(0x100008)) == kvq.KVQ_ERR_ARG
+
+
 def test_strerror(lib):
     for code in (0, -1, -2, -3, -4, 7):
         assert isinstance(kvq.strerror(code), str) and kvq.strerror(code)
@@ -307,3 +313,26 @@ def test_prefill_split_plan(lib):
     assert ws >= 8 * s * rows * 256 * 4 + 8 * s * rows * 8
     assert kvq.prefill_workspace_bytes(1, 0, 4, 2, 64, 100) == 0
     assert nblk > 0
+
+
+def test_grids_beyond_32_bit_work_items_are_refused(lib):
+    """A call whose attention or merge grid would count 2^32 work-items or more is refused on
+    the host (HIP's grid limit), instead of launching a truncated grid."""
+    E = kvq
+    # decode: 2^24 units (sequences x KV heads) of one split: 2^24 x 256 threads
+    assert decode_rc(lib, n_seq=1 << 16, hkv=256, hq=256, num_pages=1 << 10, splits=1) == \
+        E.KVQ_ERR_UNSUPPORTED
+    # one sequence fewer passes the grid check and stops at the (missing) workspace
+    assert decode_rc(lib, n_seq=(1 << 16) - 1, hkv=256, hq=256, num_pages=1 << 10, splits=1,
+                     ws=None) == E.KVQ_ERR_WORKSPACE
+    # decode merge: 2^18 units x 2 splits: 256 merge workgroups of 64 lanes per unit
+    assert decode_rc(lib, n_seq=1 << 16, hkv=4, hq=128, d=256, page_size=64, num_pages=64,
+                     max_pages=8, max_seq_len=400, splits=2) == E.KVQ_ERR_UNSUPPORTED
+    # prefill merge: 128 units x 65,536 rows x 64 dims-of-4 / 8 items x 64 lanes = 2^32
+    assert prefill_rc(lib, n_seq=32, hkv=4, hq=32, d=256, chunk=8192, page_size=64,
+                      num_pages=1 << 14, max_pages=256, max_seq_len=16384, splits=2) == \
+        E.KVQ_ERR_UNSUPPORTED
+    # the same with one piece has no merge launch and passes the grid check
+    assert prefill_rc(lib, n_seq=32, hkv=4, hq=32, d=256, chunk=8192, page_size=64,
+                      num_pages=1 << 14, max_pages=256, max_seq_len=16384, splits=1,
+                      ws=None) == E.KVQ_ERR_WORKSPACE
