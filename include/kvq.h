@@ -18,6 +18,8 @@
  *   - All array arguments are device pointers to memory the caller owns (e.g. torch tensors).
  *     The library allocates nothing, keeps no state between calls, never synchronizes, and
  *     enqueues its kernels on `stream` (a hipStream_t passed as void*; NULL = default stream).
+ *     The one exception is kvq_decode_step_noalloc, whose scratch is a static device array of
+ *     the library (stated with that call).
  *   - Calls are asynchronous and stream-ordered: kvq_append followed by kvq_decode_attn on
  *     the same stream makes the appended tokens visible to the attention.
  *   - Every scalar argument is validated on the host before any HIP call; a bad argument
@@ -41,6 +43,7 @@ extern "C" {
 #define KVQ_ERR_UNSUPPORTED (-2)  /* head_dim, page_size, rows-per-KV-head or KV format not built     */
 #define KVQ_ERR_WORKSPACE   (-3)  /* workspace NULL or smaller than kvq_decode_workspace_bytes()      */
 #define KVQ_ERR_HIP         (-4)  /* a HIP launch reported an error (hipGetLastError)                 */
+#define KVQ_ERR_SCRATCH     (-5)  /* kvq_decode_step_noalloc: needs more than its static scratch      */
 
 /* ---- supported shapes ------------------------------------------------------------------ */
 /* head_dim D in {64, 128, 256}; page_size P a power of two in [16, 256];
@@ -282,6 +285,32 @@ int kvq_decode_step_win(int32_t kv_format, void* pool, int32_t num_pages, int32_
                         int32_t max_seq_len, int32_t window, int32_t ring_pages,
                         float softmax_scale, int32_t num_splits, float* out, float* lse,
                         void* workspace, size_t workspace_bytes, void* stream);
+/* ---- kvq_decode_step_noalloc: the decode step without a workspace ------------------------
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): kvq_decode_step_fmt with the same arguments minus
+ * (workspace, workspace_bytes).  The split partials (the workspace of kvq_decode_step_fmt) go to
+ * a static device array of KVQ_NOALLOC_SCRATCH_BYTES inside the library instead: one copy per
+ * GPU, on the device current on the calling thread (`stream` must belong to it), held until
+ * the process ends.  The call allocates nothing and clears nothing (no entry of the array is
+ * read before the same launch writes it), and gives bit-identical results to
+ * kvq_decode_step_fmt with the same split plan.
+ *   - A call whose partials would exceed the array (kvq_decode_workspace_bytes() >
+ *     KVQ_NOALLOC_SCRATCH_BYTES) returns KVQ_ERR_SCRATCH and enqueues nothing.  Every automatic
+ *     plan of the supported shapes fits (at most about 8.5 MB at 32 rows per KV head, D = 256).
+ *   - All calls on one GPU share its array: calls that may overlap in time on one GPU (different
+ *     streams without ordering between them) race on it and give undefined results.  Order them
+ *     on one stream, or use kvq_decode_step_fmt with a workspace per stream.
+ *   - The first call on a device looks the array's address up (hipGetSymbolAddress) and keeps
+ *     it; KVQ_ERR_HIP if that fails. */
+#define KVQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+int kvq_decode_step_noalloc(int32_t kv_format, void* pool, int32_t num_pages, int32_t page_size,
+                            int32_t num_kv_heads, int32_t head_dim, const float* k_new,
+                            const float* v_new, int32_t n_new, const uint16_t* q,
+                            const int32_t* page_table, const int32_t* seq_lens, int32_t n_seq,
+                            int32_t n_rows, int32_t n_q_heads, int32_t max_pages_per_seq,
+                            int32_t max_seq_len, float softmax_scale, int32_t num_splits,
+                            float* out, float* lse, void* stream);
+
 int32_t kvq_decode_num_splits_win(int32_t n_seq, int32_t num_kv_heads, int32_t max_seq_len,
                                   int32_t n_rows, int32_t window, int32_t num_splits_request);
 size_t kvq_decode_workspace_bytes_win(int32_t n_seq, int32_t n_rows, int32_t n_q_heads,

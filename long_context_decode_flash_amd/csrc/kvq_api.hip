@@ -5,6 +5,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "kvq_internal.h"
 
@@ -107,6 +108,8 @@ const char* kvq_strerror(int code) {
     case KVQ_ERR_UNSUPPORTED: return "unsupported shape (head_dim, page_size or rows per KV head)";
     case KVQ_ERR_WORKSPACE: return "workspace missing or smaller than kvq_decode_workspace_bytes()";
     case KVQ_ERR_HIP: return "HIP launch error";
+    case KVQ_ERR_SCRATCH:
+      return "the call needs more split scratch than the library's static array holds (KVQ_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown kvq error code";
 }
@@ -171,12 +174,38 @@ long long ring_pages_needed(int32_t page_size, int32_t n_rows, int32_t window) {
   return ((long long)window + n_rows - 1 + page_size - 2) / page_size + 1;
 }
 
+// The split partials of kvq_decode_step_noalloc (nothing in them needs clearing: every entry
+// a launch reads, the same launch wrote first).  Each GPU the library runs on holds its own
+// copy until the process ends; host code reaches it only through the address that
+// hipGetSymbolAddress returns for the current device, never through the array's name.
+static __device__ __align__(256) uint8_t scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_at[kMaxDevices];  // per device: the device address of `scratch`, once looked up
+
+// Device address of the current device's copy of `scratch`, looked up on the first call on
+// that device (with it current) and kept.
+int scratch_address(void** at) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KVQ_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_at[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return KVQ_ERR_HIP;
+    g_scratch_at[dev] = p;
+  }
+  *at = g_scratch_at[dev];
+  return KVQ_OK;
+}
+
 int decode_impl(int32_t kv_format, const void* pool, int32_t num_pages, int32_t page_size,
                 int32_t num_kv_heads, int32_t head_dim, const float* k_new, const float* v_new, int32_t n_new,
                 const uint16_t* q, const int32_t* page_table, const int32_t* seq_lens, int32_t n_seq,
                 int32_t n_rows, int32_t n_q_heads, int32_t max_pages_per_seq, int32_t max_seq_len,
                 int32_t window, int32_t ring_pages, float softmax_scale, int32_t num_splits,
-                float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+                float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream,
+                bool noalloc = false) {
   const int vb = vbits_of(kv_format);
   int rc = pool_args_ok(pool, num_pages, page_size, num_kv_heads, head_dim, vb);
   if (rc != KVQ_OK) return rc;
@@ -208,6 +237,13 @@ int decode_impl(int32_t kv_format, const void* pool, int32_t num_pages, int32_t 
   if (!grids_fit(units, 1, plan.splits, kvq::kWave * kvq::kWavesPerGroup, rows, head_dim))
     return KVQ_ERR_UNSUPPORTED;
   const size_t need = workspace_for(units, plan.splits, rows, head_dim);
+  if (noalloc) {
+    // the partials go to this device's copy of the library's static array instead
+    if (need > (size_t)KVQ_NOALLOC_SCRATCH_BYTES) return KVQ_ERR_SCRATCH;
+    rc = scratch_address(&workspace);
+    if (rc != KVQ_OK) return rc;
+    workspace_bytes = KVQ_NOALLOC_SCRATCH_BYTES;
+  }
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15) != 0)
     return KVQ_ERR_WORKSPACE;
   const double scale = softmax_scale > 0.0f ? (double)softmax_scale : 1.0 / sqrt((double)head_dim);
@@ -300,6 +336,21 @@ int kvq_decode_step(void* pool, int32_t num_pages, int32_t page_size, int32_t nu
                              v_new, n_new, q, page_table, seq_lens, n_seq, n_rows, n_q_heads,
                              max_pages_per_seq, max_seq_len, softmax_scale, num_splits, out, lse,
                              workspace, workspace_bytes, stream);
+}
+
+int kvq_decode_step_noalloc(int32_t kv_format, void* pool, int32_t num_pages, int32_t page_size,
+                            int32_t num_kv_heads, int32_t head_dim, const float* k_new,
+                            const float* v_new, int32_t n_new, const uint16_t* q,
+                            const int32_t* page_table, const int32_t* seq_lens, int32_t n_seq,
+                            int32_t n_rows, int32_t n_q_heads, int32_t max_pages_per_seq,
+                            int32_t max_seq_len, float softmax_scale, int32_t num_splits,
+                            float* out, float* lse, void* stream) {
+  if (n_new < 0 || n_new > KVQ_MAX_STEP_TOKENS) return KVQ_ERR_ARG;
+  if (n_new > 0 && (!k_new || !v_new)) return KVQ_ERR_ARG;
+  return decode_impl(kv_format, pool, num_pages, page_size, num_kv_heads, head_dim, k_new, v_new, n_new,
+                     q, page_table, seq_lens, n_seq, n_rows, n_q_heads, max_pages_per_seq,
+                     max_seq_len, 0, 0, softmax_scale, num_splits, out, lse, nullptr, 0, stream,
+                     /*noalloc=*/true);
 }
 
 int32_t kvq_decode_num_splits_win(int32_t n_seq, int32_t num_kv_heads, int32_t max_seq_len,

@@ -20,6 +20,8 @@ KVQ_ERR_ARG = -1
 KVQ_ERR_UNSUPPORTED = -2
 KVQ_ERR_WORKSPACE = -3
 KVQ_ERR_HIP = -4
+KVQ_ERR_SCRATCH = -5
+KVQ_NOALLOC_SCRATCH_BYTES = 16 << 20  # the static split scratch of kvq_decode_step_noalloc
 KVQ_MAX_STEP_TOKENS = 64
 KVQ_FORMAT_K8V4 = 0  # 4-bit V codes
 KVQ_FORMAT_K8V8 = 1  # 8-bit V codes
@@ -81,6 +83,9 @@ def lib():
         st = L.kvq_decode_step_fmt.argtypes
         L.kvq_decode_step_win.argtypes = st[:17] + [I, I] + st[17:]
         L.kvq_decode_step_win.restype = ctypes.c_int
+        # the step without a workspace: the step_fmt arguments minus (workspace, bytes)
+        L.kvq_decode_step_noalloc.argtypes = st[:-3] + [P]
+        L.kvq_decode_step_noalloc.restype = ctypes.c_int
         L.kvq_decode_num_splits_win.argtypes = [I, I, I, I, I, I]
         L.kvq_decode_num_splits_win.restype = I
         L.kvq_decode_workspace_bytes_win.argtypes = [I, I, I, I, I, I, I, I]
@@ -337,7 +342,30 @@ def _step_args(cache, k_new, v_new, q, page_table, seq_lens, max_seq_len, out, l
             n_seq, n_rows, n_q_heads, int(page_table.shape[1]), int(max_seq_len),
             float(softmax_scale), int(num_splits), _dev(out, "out", torch.float32),
             _dev(lse, "lse", torch.float32) if lse is not None else None,
-            _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream_ptr(stream))
+            _dev(workspace, "workspace", torch.uint8) if workspace is not None else None,
+            workspace.numel() if workspace is not None else 0, _stream_ptr(stream))
+
+
+def decode_step_noalloc(cache: PagedCache, k_new: torch.Tensor | None, v_new: torch.Tensor | None,
+                        q: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                        max_seq_len: int, *, softmax_scale: float = 0.0, num_splits: int = 0,
+                        out: torch.Tensor | None = None, want_lse: bool = True,
+                        lse: torch.Tensor | None = None, stream=None):
+    """kvq_decode_step_noalloc: kvq_decode_step (format of the cache) with the split partials in
+    the library's static device array instead of a workspace.  The C call allocates nothing;
+    this wrapper allocates ``out`` / ``lse`` only when they are not given."""
+    n_seq, n_rows, n_q_heads, D = (int(x) for x in q.shape)
+    dev = q.device
+    if out is None:
+        out = torch.empty((n_seq, n_rows, n_q_heads, D), dtype=torch.float32, device=dev)
+    if want_lse and lse is None:
+        lse = torch.empty((n_seq, n_rows, n_q_heads), dtype=torch.float32, device=dev)
+    args = _step_args(cache, k_new, v_new, q, page_table, seq_lens, max_seq_len, out, lse, None,
+                      softmax_scale, num_splits, stream)
+    rc = lib().kvq_decode_step_noalloc(*(args[:-3] + args[-1:]))
+    if rc != KVQ_OK:
+        raise KVQError(rc, "kvq_decode_step_noalloc")
+    return out, lse
 
 
 def decode_step(cache: PagedCache, k_new: torch.Tensor | None, v_new: torch.Tensor | None,

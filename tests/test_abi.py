@@ -179,6 +179,43 @@ def test_decode_rejects_misaligned_out(lib):
     assert step_rc(lib, out=ctypes.c_void_p(0x100008)) == kvq.KVQ_ERR_ARG
 
 
+def noalloc_rc(lib, **kw):
+    a = dict(fmt=0, pool=FAKE, num_pages=8, page_size=16, hkv=2, d=64, k=None, v=None, n_new=0,
+             q=FAKE, pt=FAKE, sl=FAKE, n_seq=1, n_rows=1, hq=4, max_pages=8, max_seq_len=100,
+             scale=0.0, splits=0, out=FAKE, lse=None)
+    a.update(kw)
+    return lib.kvq_decode_step_noalloc(a["fmt"], a["pool"], a["num_pages"], a["page_size"],
+                                       a["hkv"], a["d"], a["k"], a["v"], a["n_new"], a["q"],
+                                       a["pt"], a["sl"], a["n_seq"], a["n_rows"], a["hq"],
+                                       a["max_pages"], a["max_seq_len"], a["scale"], a["splits"],
+                                       a["out"], a["lse"], None)
+
+
+def test_noalloc_validation(lib):
+    """kvq_decode_step_noalloc checks its arguments as kvq_decode_step does, and refuses a call
+    whose partials exceed the static scratch with KVQ_ERR_SCRATCH; all before any HIP call."""
+    E = kvq
+    assert noalloc_rc(lib, pool=None) == E.KVQ_ERR_ARG
+    assert noalloc_rc(lib, q=None) == E.KVQ_ERR_ARG
+    assert noalloc_rc(lib, out=ctypes.c_void_p(0x100004)) == E.KVQ_ERR_ARG
+    assert noalloc_rc(lib, d=96) == E.KVQ_ERR_UNSUPPORTED
+    assert noalloc_rc(lib, fmt=5) == E.KVQ_ERR_UNSUPPORTED
+    assert noalloc_rc(lib, n_new=-1) == E.KVQ_ERR_ARG
+    assert noalloc_rc(lib, n_new=2) == E.KVQ_ERR_ARG  # k_new / v_new missing
+    assert noalloc_rc(lib, n_new=E.KVQ_MAX_STEP_TOKENS + 1, k=FAKE, v=FAKE) == E.KVQ_ERR_ARG
+    # 32 sequences x 8 KV heads x 128 splits x 32 rows x D 256: far past 16 MiB
+    big = dict(n_seq=32, hkv=8, hq=64, n_rows=4, d=256, page_size=64, num_pages=1 << 16,
+               max_pages=4096, max_seq_len=1 << 18, splits=128)
+    need = kvq.decode_workspace_bytes(32, 4, 64, 8, 256, 1 << 18, 128)
+    assert need > E.KVQ_NOALLOC_SCRATCH_BYTES
+    assert noalloc_rc(lib, **big) == E.KVQ_ERR_SCRATCH
+    assert "static" in kvq.strerror(E.KVQ_ERR_SCRATCH)
+    # every automatic plan of the benchmark's workloads fits
+    for n_seq, hkv, hq, R, L in ((1, 1, 4, 1, 512), (1, 4, 24, 1, 8192), (1, 4, 24, 1, 65536),
+                                 (2, 4, 24, 1, 92160), (1, 4, 24, 4, 262144), (1, 8, 256, 1, 1 << 20)):
+        assert kvq.decode_workspace_bytes(n_seq, R, hq, hkv, 256, L) <= E.KVQ_NOALLOC_SCRATCH_BYTES
+
+
 def test_strerror(lib):
     for code in (0, -1, -2, -3, -4, 7):
         assert isinstance(kvq.strerror(code), str) and kvq.strerror(code)
