@@ -111,6 +111,105 @@ def cpu_baseline(wl, inp, min_seconds=10.0, window=0, kv_format=0):
             return dt / steps, steps, oracle.num_threads()
 
 
+def cpu_baseline_one_thread(wl, inp, rows=6, window=0, kv_format=0):
+    """The oracle on one host thread, over a bounded sample: `rows` of the step's output rows
+    (the first query row of the first heads of sequence 0), scaled to a whole step by the row
+    count; the step's append (a few tokens) is negligible beside the attention.  Returns
+    (seconds per step, sample description)."""
+    import oracle
+    pool = oracle.new_pool(wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
+                           4 if kv_format == 0 else 8)
+    oracle.append(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
+                  *inp.all_tokens(), kv_format=kv_format)
+    total = wl.n_seq * wl.n_rows * wl.n_q_heads
+    rows = min(rows, total)
+    sel = [(0, 0, hq) for hq in range(rows)]
+    before = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        t0 = time.perf_counter()
+        oracle.decode_attn(pool, wl.pool_pages, wl.page_size, wl.num_kv_heads, wl.head_dim,
+                           inp.q_bits, inp.page_table, inp.seq_lens, wl.n_rows, wl.n_q_heads,
+                           select=sel, window=window, kv_format=kv_format)
+        dt = time.perf_counter() - t0
+    finally:
+        oracle.set_num_threads(before)
+    return dt * total / rows, (f"{rows} of the step's {total} output rows on 1 thread "
+                               f"({dt:.1f} s), scaled by {total}/{rows}")
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def read_telemetry() -> dict:
+    """GPU clocks, power and power cap as the driver reports them.  The firmware's metrics table
+    refreshes about every 100 ms, so a reading describes the state around the timed region,
+    not inside it."""
+    t = {}
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[0]
+        m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+        for k in ("current_gfxclk", "current_gfxclks", "current_uclk", "current_socclk",
+                  "current_socket_power", "temperature_hotspot", "temperature_mem",
+                  "average_gfx_activity", "average_umc_activity"):
+            if k in m:
+                t[k] = m[k]
+        t["power_cap_w"] = amdsmi.amdsmi_get_power_cap_info(h)["power_cap"] / 1e6
+    except Exception as e:  # telemetry is informative only
+        t["amdsmi_error"] = str(e)[:120]
+    import glob
+    for name in ("pp_dpm_sclk", "pp_dpm_mclk"):
+        paths = sorted(glob.glob(f"/sys/class/drm/card*/device/{name}"))
+        try:
+            with open(paths[0]) as f:
+                cur = [l.strip() for l in f if "*" in l]
+            t[name] = cur[0] if cur else None
+        except (OSError, IndexError):
+            t[name] = None
+    return t
+
+
+def attainable_probe(kvq, torch, dev, stream, gib=2, reps=5):
+    """The plain streaming read (kvq_probe_stream_read) over a `gib` GiB buffer in each load form
+    and a few grid sizes, event-timed over `reps` calls each; returns the best and every
+    result.  The sweep streams for a few tens of milliseconds, and runs right before the
+    decode's warm-up, so both are measured in the same sustained state of the GPU."""
+    n = gib << 30
+    buf = torch.empty(n, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    rows = []
+    for mode, form in ((0, "16-byte register loads, nt"), (1, "16-byte register loads"),
+                       (2, "direct-to-LDS 16-byte loads, nt")):
+        for wgs in (256, 512, 1024, 2048):
+            call = kvq.prepare_stream_probe(buf, mode, wgs, sink, stream=stream)
+            call()
+            e0.record(stream)
+            for _ in range(reps):
+                call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            rows.append({"mode": mode, "form": form, "workgroups": wgs, "us": round(us, 1),
+                         "GB_s": round(n / us / 1e3, 1)})
+    del buf
+    best = max(rows, key=lambda r: r["GB_s"])
+    log(f"[bench] attainable read: {best['GB_s']:.0f} GB/s ({best['form']}, "
+        f"{best['workgroups']} workgroups, {gib} GiB)")
+    return best, rows, n
+
+
 def _counter_rows(path):
     import csv
     with open(path) as f:
@@ -174,13 +273,21 @@ def ingest_trace(stats_csv, command, bench_log=None):
         k = int(js[-1]["steps"])
         tr = _counter_rows(trace_csv)
         avg = {}
+        lines += ["", f"Over the last {k} calls of each kernel (the timed steps):", "",
+                  "| kernel | mean us | median us | p90 us | min us | max us |",
+                  "|---|---:|---:|---:|---:|---:|"]
         for name in ("decode_kernel", "merge_kernel"):
             d = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in tr
                        if name in r["Kernel_Name"])[-k:]
-            avg[name] = sum(e - s for s, e in d) / len(d) / 1e3
-        lines.append(f"Over the last {k} calls (the timed steps): decode_kernel {avg['decode_kernel']:.2f} us, "
-                     f"merge_kernel {avg['merge_kernel']:.2f} us, sum "
-                     f"{avg['decode_kernel'] + avg['merge_kernel']:.2f} us.")
+            if not d:
+                avg[name] = 0.0
+                continue
+            us = sorted((e - s) / 1e3 for s, e in d)
+            avg[name] = sum(us) / len(us)
+            med = us[len(us) // 2] if len(us) % 2 else 0.5 * (us[len(us) // 2 - 1] + us[len(us) // 2])
+            p90 = us[min(len(us) - 1, int(0.9 * len(us)))]
+            lines.append(f"| {name} | {avg[name]:.2f} | {med:.2f} | {p90:.2f} | {us[0]:.2f} | {us[-1]:.2f} |")
+        lines += ["", f"Sum of the two means: {avg['decode_kernel'] + avg['merge_kernel']:.2f} us."]
     if js:
         lines.append(f"bench.py's own line in the same profiled run: {js[-1]['ms_per_step'] * 1e3:.2f} us "
                      "per step (kernel boundaries overlap slightly in the trace's timestamps).")
@@ -274,6 +381,8 @@ def main(argv=None):
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window: each row sees only its last W tokens (0 = all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-attainable", action="store_true",
+                    help="skip the streaming-read probe (it also runs right before the warm-up)")
     ap.add_argument("--prefill-chunk", type=int, default=1024,
                     help="positions of the chunked-prefill measurement (0: skip it)")
     ap.add_argument("--unfused", action="store_true",
@@ -367,7 +476,27 @@ def main(argv=None):
     prefill_bytes = n_pre * wl.num_kv_heads * (2 * D * 4 + token_bytes(D, vbits)) + n_pre * 4
     log(f"[bench] prefill append of {n_pre} tokens: {prefill_us:.1f} us, "
         f"{prefill_bytes / prefill_us / 1e3:.0f} GB/s")
-    del k_pre, v_pre, apps
+    # one prefill chunk of one sequence (the engine's --prefill-chunk 1024 in the forum post,
+    # 一、部署): the last `chunk` cached tokens of sequence 0, rewritten in place (idempotent)
+    chunk_n = min(args.prefill_chunk or 1024, wl.seq_len - wl.n_new)
+    c0 = wl.seq_len - wl.n_new - chunk_n
+    ck = dev_t(inp.k[0, c0:c0 + chunk_n])
+    cv = dev_t(inp.v[0, c0:c0 + chunk_n])
+    cs = dev_t(W.slots_for(inp.page_table, wl.page_size, 0, c0, c0 + chunk_n))
+    capp = kvq.prepare_append(caches[0], ck, cv, cs)
+    capp()
+    torch.cuda.synchronize()
+    creps = 50
+    e0.record()
+    for _ in range(creps):
+        capp()
+    e1.record()
+    torch.cuda.synchronize()
+    chunk_us = e0.elapsed_time(e1) * 1e3 / creps
+    chunk_bytes = chunk_n * wl.num_kv_heads * (2 * D * 4 + token_bytes(D, vbits)) + chunk_n * 4
+    log(f"[bench] append of one {chunk_n}-token chunk: {chunk_us:.1f} us, "
+        f"{chunk_bytes / chunk_us / 1e3:.0f} GB/s")
+    del k_pre, v_pre, apps, ck, cv, cs, capp
     for _ in range(args.copies - 1):
         c = kvq.PagedCache.allocate(wl.pool_pages, wl.page_size, wl.num_kv_heads, D, dev,
                                     kv_format=fmt)
@@ -411,6 +540,11 @@ def main(argv=None):
     def step(i):
         calls[i % len(calls)]()
 
+    telemetry = {"idle": read_telemetry()}
+    attainable = None
+    if not args.no_attainable:
+        attainable = attainable_probe(kvq, torch, dev, stream)
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -428,6 +562,7 @@ def main(argv=None):
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
+    telemetry["after_timed_steps"] = read_telemetry()
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
     log(f"[bench] {args.steps} steps in {total_ms:.2f} ms (wall {wall * 1e3:.1f} ms): "
@@ -497,6 +632,13 @@ def main(argv=None):
             "launch_us_mean": round(ms_per_step * 1e3, 2),
         },
     }
+    if attainable is not None:
+        best, rows, nbytes = attainable
+        res["roofline"]["attainable"] = best["GB_s"]
+        res["roofline"]["frac_of_attainable"] = round(achieved / best["GB_s"], 4)
+        res["attainable_read"] = {"best": best, "bytes": nbytes, "sweep": rows,
+                                  "kernel": "kvq_probe_stream_read (plain streaming read)"}
+    res["telemetry"] = telemetry
 
     if args.prefill_chunk > 0 and not win:
         res["prefill_attn"] = bench_prefill(kvq, torch, wl, inp, caches, stream, args.prefill_chunk)
@@ -508,6 +650,9 @@ def main(argv=None):
         "GB_s": round(prefill_bytes / prefill_us / 1e3, 1),
         "frac_of_hbm_peak": round(prefill_bytes / prefill_us / 1e3 / HBM_PEAK_GBS, 4),
         "kernel": "kvq_append: append_kernel, one call per sequence over its cached tokens",
+        "chunk": {"tokens": chunk_n, "us": round(chunk_us, 2), "algorithmic_bytes": chunk_bytes,
+                  "GB_s": round(chunk_bytes / chunk_us / 1e3, 1),
+                  "note": "one kvq_append of one sequence's chunk, back-to-back calls, event-timed"},
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline: oracle on full steps, about 10 s")
@@ -522,7 +667,13 @@ def main(argv=None):
                       f"over {min(wl.seq_len, win) if win else wl.seq_len} tokens each), fp64, "
                       f"{dt * n_cpu:.1f} s in all",
             "s_per_step": round(dt, 3),
+            "cpu_model": cpu_model(),
         }
+        log("[bench] cpu baseline: one-thread sample")
+        dt1, sample1 = cpu_baseline_one_thread(wl, inp, window=win, kv_format=fmt)
+        res["cpu_baseline"]["one_thread"] = {"s_per_step": round(dt1, 2),
+                                             "value": round(step_bytes / dt1 / 1e9, 5),
+                                             "sample": sample1}
     print(json.dumps(res), flush=True)
     return 0
 

@@ -356,6 +356,19 @@ size_t kvq_prefill_workspace_bytes(int32_t n_seq, int32_t chunk, int32_t n_q_hea
 /* Static description of a return code. */
 const char* kvq_strerror(int code);
 
+/* ---- measurement helper (not part of the method) -------------------------------------------
+ * kvq_probe_stream_read: read `bytes` of device memory at `buf` once, as a plain stream, so that
+ * a benchmark can set the decode's achieved bandwidth against what this GPU attains for a pure
+ * read (the forum post, 二、测评, weighs decode speed as bytes per token against the card's
+ * bandwidth).  mode 0: 16-byte non-temporal loads into registers; 1: the same with normal
+ * caching; 2: gfx950 direct-to-LDS 16-byte non-temporal loads, the decode kernel's own form.
+ * `workgroups` of 256 threads share the buffer (grid-stride).  `sink` (one device uint32) is
+ * written only for data that xors to a fixed improbable value; it exists so the loads cannot be
+ * dropped.  buf 4096-byte aligned, bytes a non-zero multiple of 4096, workgroups 1 .. 2^20.
+ * Returns KVQ_OK, KVQ_ERR_ARG or KVQ_ERR_HIP. */
+int kvq_probe_stream_read(const void* buf, size_t bytes, int32_t mode, int32_t workgroups,
+                          uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

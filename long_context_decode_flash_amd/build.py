@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
-SOURCES = ["kvq_api.hip", "kvq_append.hip", "kvq_decode.hip", "kvq_prefill.hip"]
+SOURCES = ["kvq_api.hip", "kvq_append.hip", "kvq_decode.hip", "kvq_prefill.hip", "kvq_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -538,3 +538,15 @@ int kvq_prefill_attn(int32_t kv_format, const void* pool, int32_t num_pages, int
 }
 
 }  // extern "C"
+
+// ---- measurement helper ----------------------------------------------------------------------
+
+extern "C" int kvq_probe_stream_read(const void* buf, size_t bytes, int32_t mode, int32_t workgroups,
+                                     uint32_t* sink, void* stream) {
+  if (!buf || !sink || bytes == 0 || (bytes & 4095) != 0 || ((uintptr_t)buf & 4095) != 0) return KVQ_ERR_ARG;
+  if (mode < 0 || mode > 2 || workgroups < 1 || workgroups > (1 << 20)) return KVQ_ERR_ARG;
+  (void)hipGetLastError();
+  return kvq::launch_stream_probe(buf, bytes, mode, workgroups, sink, (hipStream_t)stream) == hipSuccess
+             ? KVQ_OK
+             : KVQ_ERR_HIP;
+}

@@ -74,6 +74,8 @@ struct DecodeArgs {
 hipError_t launch_append(int head_dim, const AppendArgs& a, hipStream_t stream);
 hipError_t launch_decode(int head_dim, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(int head_dim, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_stream_probe(const void* buf, size_t bytes, int mode, int workgroups, uint32_t* sink,
+                               hipStream_t stream);
 
 constexpr int kPrefillRowsPerTile = 256;  // query rows of one prefill workgroup (32 per wave)
 constexpr int kPrefillThreads = 512;      // 8 waves per prefill workgroup

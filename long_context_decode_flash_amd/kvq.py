@@ -97,6 +97,8 @@ def lib():
         L.kvq_prefill_num_splits.restype = I
         L.kvq_prefill_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
         L.kvq_prefill_workspace_bytes.restype = ctypes.c_size_t
+        L.kvq_probe_stream_read.argtypes = [P, ctypes.c_size_t, I, I, P, P]
+        L.kvq_probe_stream_read.restype = ctypes.c_int
         _lib = L
         return L
 
@@ -455,4 +457,19 @@ def prepare_decode_attn(cache: PagedCache, q: torch.Tensor, page_table: torch.Te
         rc = fn(*args)
         if rc != KVQ_OK:
             raise KVQError(rc, "kvq_decode_attn")
+    return call
+
+
+def prepare_stream_probe(buf: torch.Tensor, mode: int, workgroups: int, sink: torch.Tensor,
+                         stream=None):
+    """kvq_probe_stream_read over all of ``buf`` (uint8, 4 KB-aligned, a multiple of 4 KB):
+    the plain streaming read the decode's bandwidth is set against.  Returns a callable that
+    re-issues it."""
+    args = (_dev(buf, "buf", torch.uint8), buf.numel(), int(mode), int(workgroups),
+            _dev(sink, "sink", torch.int32), _stream_ptr(stream))
+
+    def call():
+        rc = lib().kvq_probe_stream_read(*args)
+        if rc != KVQ_OK:
+            raise KVQError(rc, "kvq_probe_stream_read")
     return call

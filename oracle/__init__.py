@@ -67,6 +67,8 @@ def _declare(lib):
     lib.kvq_oracle_quantize_group_f8.restype = None
     lib.kvq_oracle_num_threads.argtypes = []
     lib.kvq_oracle_num_threads.restype = I
+    lib.kvq_oracle_set_num_threads.argtypes = [I]
+    lib.kvq_oracle_set_num_threads.restype = None
     return lib
 
 
@@ -97,6 +99,9 @@ class Oracle:
 
     def num_threads(self) -> int:
         return self.lib.kvq_oracle_num_threads()
+
+    def set_num_threads(self, n: int) -> None:
+        self.lib.kvq_oracle_set_num_threads(int(n))
 
     def fp16_to_double(self, bits: int) -> float:
         return self.lib.kvq_oracle_fp16_to_double(int(bits))

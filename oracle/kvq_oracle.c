@@ -495,3 +495,12 @@ int kvq_oracle_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Threads the attention loops use from now on (the benchmark's 1-thread baseline). */
+void kvq_oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
