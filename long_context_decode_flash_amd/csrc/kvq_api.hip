@@ -25,6 +25,9 @@ int vbits_of(int32_t kv_format) {
 constexpr long long kTargetGroups = 256;
 // A split covers at least one 32-token block per wave of its workgroup.
 constexpr long long kMinBlocksPerSplit = kvq::kWavesPerGroup;
+// Workgroups that keep HBM saturated: with at least this many streaming (90% of the CUs), the
+// decode is bandwidth-bound and fewer workgroups each stream proportionally faster.
+constexpr long long kSaturatingGroups = 230;
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
@@ -41,9 +44,25 @@ int plan_splits(int n_seq, int num_kv_heads, int max_seq_len, int request, Plan*
   if (request > 0) {
     s = request;
   } else {
-    s = ceil_div(kTargetGroups, units);
+    // At most one workgroup per CU.  A split's blocks go to its 4 waves in turn, so a count
+    // that leaves some waves one block more than others idles part of each CU's bandwidth at
+    // the end; the time of a plan is modelled as (blocks of the busiest wave) x (workgroups,
+    // or the saturating count if fewer), and the fastest plan is taken, the most splits on ties.
+    long long s_max = ceil_div(kTargetGroups, units);
     const long long cap = ceil_div(nblk, kMinBlocksPerSplit);
-    s = s < cap ? s : cap;
+    s_max = s_max < cap ? s_max : cap;
+    s = 1;
+    long long best = -1;
+    for (long long c = s_max; c >= 1; --c) {
+      const long long bps = ceil_div(nblk, c);
+      const long long used = ceil_div(nblk, bps);  // splits that start inside the context
+      const long long groups = units * used;
+      const long long t = ceil_div(bps, kvq::kWavesPerGroup) * (groups > kSaturatingGroups ? groups : kSaturatingGroups);
+      if (best < 0 || t < best) {
+        best = t;
+        s = c;
+      }
+    }
   }
   if (s < 1) s = 1;
   if (s > nblk) s = nblk;

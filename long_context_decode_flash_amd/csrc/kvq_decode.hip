@@ -163,17 +163,52 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // The first chunk's first blocks are in flight while the queries are prepared (an empty split
   // gets n_my = 0).  The query words are used here on every path, so the compiler's own wait for
   // them (loaded with the page ids, one round trip for both) sits here and not after the DMAs.
+  //
   // Fused append: the wave that will stage the block of a new token quantizes the token's K/V
-  // rows (this KV head) into its slot first; chunk_start's wait covers the stores, so the
-  // block's loads see them.
-  for (int j = 0; j < a.n_new; ++j) {
-    const int t = L - a.n_new + j;
-    const int blk = t >> 5;
-    if (t < 0 || blk < g_blk0 || blk >= g_blk1 || ((blk - g_blk0) & (kWavesPerGroup - 1)) != w) continue;
-    const int page = min(max(pt[entry(t >> lgP)], 0), a.num_pages - 1);
-    const size_t row = (((size_t)b * a.n_new + j) * a.num_kv_heads + h) * D;
-    append_row<D, VB, F8>(a.pool_rw + ((size_t)page * a.num_kv_heads + h) * bb, P, t & (P - 1), a.k_new + row,
-                  a.v_new + row, lane);
+  // rows (this KV head) into its slot, and the block's loads must see those bytes.  The new
+  // tokens L - n_new .. L - 1 fall in at most three consecutive blocks, so a wave owns at most
+  // one run [ta, tb) of them, in one block at place kb of its list (blocks w, w + 4, ... of the
+  // split).
+  //   * Usual case (the block at place kb >= 2 NSTAGE - 2, at most kFastTokens tokens): the rows
+  //     and page ids load with the queries and page ids (one round trip for all), and the
+  //     quantized bytes are stored once the first stage loads are out, so the work overlaps the
+  //     first block's flight.  Vector memory operations complete in issue order; the stores go
+  //     out between the loads of places NSTAGE - 2 and NSTAGE - 1, the loop's wait at iteration
+  //     NSTAGE - 2 retires everything issued before the loads of place NSTAGE - 1, and the
+  //     block at place kb >= 2 NSTAGE - 2 is issued after that wait (a block of a later chunk:
+  //     that chunk's chunk_start waits for everything).  On the 184K-token step the token is its
+  //     wave's last block; written before the first loads, it held its workgroup ~2 us behind
+  //     the others.
+  //   * Otherwise (a block whose loads may leave before that wait, or a longer run) the tokens
+  //     are written before the first loads, and chunk_start's wait covers their stores.
+  constexpr int kEarlyPlaces = 2 * NSTAGE - 2;
+  constexpr int kFastTokens = 4;
+  int ta = 0, tb = 0, kb_app = -1;
+  if (a.n_new > 0) {
+    const int t_first = max(L - a.n_new, 0);
+    for (int blk = t_first >> 5; blk <= (L - 1) >> 5; ++blk)
+      if (blk >= g_blk0 && blk < g_blk1 && ((blk - g_blk0) & (kWavesPerGroup - 1)) == w) {
+        ta = max(t_first, blk * kBlock);
+        tb = min(L, blk * kBlock + kBlock);
+        kb_app = (blk - g_blk0) / kWavesPerGroup;
+      }
+  }
+  const bool app_fast = kb_app >= kEarlyPlaces && tb - ta <= kFastTokens;
+  auto new_row = [&](int t) { return (((size_t)b * a.n_new + (t - (L - a.n_new))) * a.num_kv_heads + h) * D; };
+  auto slot_block = [&](int pid) { return a.pool_rw + ((size_t)min(max(pid, 0), a.num_pages - 1) * a.num_kv_heads + h) * bb; };
+  if (kb_app >= 0 && !app_fast)
+    for (int t = ta; t < tb; ++t)
+      append_row<D, VB, F8>(slot_block(pt[entry(t >> lgP)]), P, t & (P - 1), a.k_new + new_row(t), a.v_new + new_row(t),
+                            lane);
+  RowVals<D> app_rows[kFastTokens];
+  int app_pid[kFastTokens];
+#pragma unroll
+  for (int i = 0; i < kFastTokens; ++i) {
+    const bool on = app_fast && ta + i < tb;
+    const int t = on ? ta + i : 0;
+    app_pid[i] = on ? pt[entry(t >> lgP)] : 0;
+    app_rows[i] = RowVals<D>{};
+    if (on) app_rows[i] = load_row<D>(a.k_new + new_row(t), a.v_new + new_row(t), lane);
   }
   chunk_count();
   asm volatile("" ::"v"(my_pid));
@@ -181,7 +216,18 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int jj = 0; jj < D / 64; ++jj) asm volatile("" ::"v"(qw[nb][jj][0]), "v"(qw[nb][jj][1]));
+#pragma unroll
+  for (int i = 0; i < kFastTokens; ++i) {
+    asm volatile("" ::"v"(app_pid[i]));
+#pragma unroll
+    for (int e = 0; e < RowVals<D>::E; ++e) asm volatile("" ::"v"(app_rows[i].k[e]), "v"(app_rows[i].v[e]));
+  }
   chunk_start();
+#pragma unroll
+  for (int i = 0; i < kFastTokens; ++i) {
+    const int t = ta + i;
+    if (app_fast && t < tb) store_row<D, VB, F8>(slot_block(app_pid[i]), P, t & (P - 1), app_rows[i], lane);
+  }
 
   i32x4 qd[NB][3][D / 64];
   float cz[NB];
