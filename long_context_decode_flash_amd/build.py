@@ -24,8 +24,30 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra: list[str] | None = None, out: str = LIB) -> str:
+# The host half of the library built with AddressSanitizer and UndefinedBehaviorSanitizer (the
+# device code is unchanged): the CPU tests of argument validation and planning run against it.
+SANITIZED_LIB = os.path.join(HERE, "libkvq_san.so")
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+                 "-Xarch_host", "-g"]
+
+
+def asan_runtime() -> str:
+    """The clang AddressSanitizer runtime matching hipcc's host compiler (to LD_PRELOAD into a
+    Python process that loads the sanitized library)."""
+    import glob
+    found = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not found:
+        raise RuntimeError("clang AddressSanitizer runtime not found under /opt/rocm/llvm")
+    return found[-1]
+
+
+def build(verbose: bool = False, extra: list[str] | None = None, out: str = LIB,
+          sanitize: bool = False) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    if sanitize:
+        extra = [*(extra or []), *HOST_SANITIZE]
+        out = SANITIZED_LIB if out == LIB else out
     cmd = [HIPCC, *FLAGS, *(extra or []), "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            "-o", out + ".tmp", *srcs]
     if verbose:

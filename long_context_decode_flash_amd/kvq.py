@@ -13,7 +13,8 @@ from dataclasses import dataclass
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkvq.so")
+# KVQ_LIB names another build of the same library (the sanitizer build of the CPU tests)
+LIB_PATH = os.environ.get("KVQ_LIB") or os.path.join(_HERE, "libkvq.so")
 
 KVQ_OK = 0
 KVQ_ERR_ARG = -1

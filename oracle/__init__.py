@@ -25,11 +25,21 @@ CFLAGS = ["-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
           "-fPIC", "-shared", "-Wall"]
 
 
-def build(force: bool = False, source: str = SOURCE, out: str = _SO) -> str:
-    """Compile the oracle C source into a shared library (gcc). Returns the library path."""
+SANITIZED_SO = os.path.join(_HERE, "liboracle_san.so")
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                  "-fno-omit-frame-pointer", "-g"]
+
+
+def build(force: bool = False, source: str = SOURCE, out: str = _SO, sanitize: bool = False) -> str:
+    """Compile the oracle C source into a shared library (gcc). Returns the library path.
+    sanitize: AddressSanitizer + UndefinedBehaviorSanitizer build (liboracle_san.so), for a
+    process that preloads gcc's libasan."""
+    if sanitize and out == _SO:
+        out = SANITIZED_SO
     if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(source):
         tmp = out + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", *CFLAGS, "-o", tmp, source, "-lm"])
+        flags = CFLAGS + (SANITIZE_FLAGS if sanitize else [])
+        subprocess.check_call(["gcc", *flags, "-o", tmp, source, "-lm"])
         os.replace(tmp, out)
     return out
 
@@ -243,7 +253,8 @@ def default() -> Oracle:
     global _default
     with _lock:
         if _default is None:
-            _default = Oracle(build())
+            # KVQ_ORACLE_LIB names another build of the same source (the sanitizer build)
+            _default = Oracle(os.environ.get("KVQ_ORACLE_LIB") or build())
         return _default
 
 
