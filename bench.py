@@ -180,6 +180,66 @@ def read_telemetry() -> dict:
     return t
 
 
+class ShaderClock:
+    """Reads the shader clock on the GPU itself (kvq_probe_clock: shader-clock cycles against the
+    constant-rate counter over a 20 us spin in 256 one-wave workgroups).  The driver's metrics
+    table refreshes about every 100 ms and cannot resolve a millisecond-long timed region; this
+    probe is enqueued on the stream right beside it.  enqueue() queues a reading into the next
+    slot; read() returns every queued reading (mean MHz and the slowest and fastest XCD)."""
+
+    WG = 256
+
+    def __init__(self, kvq, torch, dev, stream, slots=64):
+        self.torch = torch
+        self.buf = torch.zeros((slots, 3 * self.WG), dtype=torch.int64, device=dev)
+        self.calls = [kvq.prepare_clock_probe(self.buf[i], 2000, stream=stream) for i in range(slots)]
+        self.khz = kvq.clock_counter_khz()
+        self.n = 0
+
+    def enqueue(self):
+        self.calls[self.n]()
+        self.n += 1
+        return self.n - 1
+
+    def read(self, i):
+        v = self.buf[i].view(self.WG, 3).cpu().numpy()
+        mhz = v[:, 0] / v[:, 1] * self.khz / 1000.0
+        per = [float(mhz[v[:, 2] == x].mean()) for x in sorted(set(v[:, 2].tolist()))]
+        return {"mhz": round(float(mhz.mean())), "xcd_min_mhz": round(min(per)),
+                "xcd_max_mhz": round(max(per))}
+
+
+def sustained_run(torch, stream, step, clk, n, group=50):
+    """n more back-to-back steps (after the timed region, which they do not touch), timed in
+    groups of `group` with a shader-clock reading after each group: how the step time follows
+    the clock as the GPU's power management settles under a continuous decode load."""
+    groups = []
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * (n // group))]
+    idx = []
+    for g in range(n // group):
+        ev[2 * g].record(stream)
+        for i in range(group):
+            step(g * group + i)
+        ev[2 * g + 1].record(stream)
+        idx.append(clk.enqueue() if clk.n < len(clk.calls) else None)
+    torch.cuda.synchronize()
+    t0 = ev[0]
+    for g in range(n // group):
+        r = {"t_ms": round(t0.elapsed_time(ev[2 * g]), 2),
+             "us_per_step": round(ev[2 * g].elapsed_time(ev[2 * g + 1]) * 1e3 / group, 2)}
+        if idx[g] is not None:
+            r.update(clk.read(idx[g]))
+        groups.append(r)
+    last = groups[len(groups) // 2:]
+    med = sorted(x["us_per_step"] for x in last)[len(last) // 2]
+    log(f"[bench] sustained: {n} more steps, first group {groups[0]['us_per_step']} us/step at "
+        f"{groups[0].get('mhz')} MHz, median of the second half {med} us/step")
+    return {"steps": n, "group": group, "groups": groups,
+            "second_half_median_us_per_step": med,
+            "note": "not the timed value: back-to-back steps after every timed measurement, "
+                    "with the shader clock read after each group"}
+
+
 def attainable_probe(kvq, torch, dev, stream, gib=2, reps=5):
     """The plain streaming read (kvq_probe_stream_read) over a `gib` GiB buffer in each load form
     and a few grid sizes, event-timed over `reps` calls each; returns the best and every
@@ -294,6 +354,43 @@ def ingest_trace(stats_csv, command, bench_log=None):
     return "\n".join(lines) + "\n"
 
 
+def ingest_counters(dirs, command_lines, kernel_names, per_wave_units=None):
+    """Markdown table of rocprofv3 --pmc counters per kernel: the mean per dispatch over all
+    dispatches of each kernel in the runs (one run per counter set; the SQ counters are summed
+    over the chip).  per_wave_units: {kernel substring: (units of work per wave, label)} adds
+    per-unit figures (instructions of each kind per wave and unit)."""
+    import collections
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for d in dirs:
+        for root, _, files in os.walk(d):
+            for fn in files:
+                if fn.endswith("counter_collection.csv"):
+                    for r in _counter_rows(os.path.join(root, fn)):
+                        k = r["Kernel_Name"].replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+                        agg[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    lines = ["# Hardware counters per kernel", "", "Commands (one rocprofv3 --pmc run per counter set):", "", "```"]
+    lines += command_lines + ["```", ""]
+    for k, cs in sorted(agg.items()):
+        if not any(n in k for n in kernel_names):
+            continue
+        lines += [f"## {k}", "", "| counter | mean per dispatch | dispatches |", "|---|---:|---:|"]
+        mean = {c: sum(v) / len(v) for c, v in cs.items()}
+        for c in sorted(mean):
+            lines.append(f"| {c} | {mean[c]:,.1f} | {len(cs[c])} |")
+        waves = mean.get("SQ_WAVES")
+        for sub, (units, label) in (per_wave_units or {}).items():
+            if sub in k and waves:
+                lines += ["", f"Per wave and {label} ({units:g} per wave):", ""]
+                for c in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_VMEM"):
+                    if c in mean:
+                        lines.append(f"- {c}: {mean[c] / waves / units:,.1f}")
+                for c in ("SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_ANY", "SQ_VALU_MFMA_BUSY_CYCLES"):
+                    if c in mean and "SQ_WAVE_CYCLES" in mean:
+                        lines.append(f"- {c} / SQ_WAVE_CYCLES: {mean[c] / mean['SQ_WAVE_CYCLES']:.3f}")
+        lines.append("")
+    return "\n".join(lines) + "\n"
+
+
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix-core peak
 
 
@@ -381,6 +478,10 @@ def main(argv=None):
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window: each row sees only its last W tokens (0 = all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sustained", type=int, default=600,
+                    help="after everything timed, this many more back-to-back steps in groups of "
+                         "50, each followed by a shader-clock reading (0: skip); reported apart "
+                         "from the timed value")
     ap.add_argument("--no-attainable", action="store_true",
                     help="skip the streaming-read probe (it also runs right before the warm-up)")
     ap.add_argument("--prefill-chunk", type=int, default=1024,
@@ -398,9 +499,28 @@ def main(argv=None):
                     help="summarize a long --kernel-trace run: decode duration per group of calls")
     ap.add_argument("--ingest-out", default=None,
                     help="file name under profiles/ for --ingest-trace (default: the decode trace)")
+    ap.add_argument("--ingest-counters", nargs="+", metavar="DIR",
+                    help="summarize rocprofv3 --pmc runs (counter_collection.csv under each DIR) into "
+                         "profiles/ (--ingest-out names the file)")
     ap.add_argument("--bench-log", default=None,
                     help="stdout of bench.py in the profiled run (its JSON line), for --ingest-trace")
     args = ap.parse_args(argv)
+
+    if args.ingest_counters:
+        from long_context_decode_flash_amd import workloads as W
+        wl = W.WORKLOADS[args.workload or W.HEADLINE]
+        splits = int(args.splits) or None
+        units = {}
+        if splits:
+            blocks = -(-wl.seq_len // 32) * wl.n_seq * wl.num_kv_heads / (splits * wl.n_seq * wl.num_kv_heads * 4)
+            units["decode_kernel"] = (blocks, "32-token block")
+        path = os.path.join(ROOT, "profiles", args.ingest_out or f"counters_{args.workload or W.HEADLINE}.md")
+        with open(path, "w") as f:
+            f.write(ingest_counters(args.ingest_counters, args.command.split(" ;; ") if args.command else [],
+                                    ["decode_kernel", "merge_kernel", "prefill_kernel", "append_kernel",
+                                     "stream_read"], units))
+        print(path)
+        return 0
 
     if args.ingest_settling:
         from long_context_decode_flash_amd import workloads as W
@@ -541,9 +661,13 @@ def main(argv=None):
         calls[i % len(calls)]()
 
     telemetry = {"idle": read_telemetry()}
+    clk = ShaderClock(kvq, torch, dev, stream)
+    torch.cuda.synchronize()
+    clk_at = {"before_attainable": clk.enqueue()}
     attainable = None
     if not args.no_attainable:
         attainable = attainable_probe(kvq, torch, dev, stream)
+        clk_at["after_attainable"] = clk.enqueue()
 
     for i in range(args.warmup):
         step(i)
@@ -552,17 +676,22 @@ def main(argv=None):
 
     # The timed region: K steps bracketed by two events.  No event sits between the calls: each
     # event record costs the stream a few microseconds of its own.
+    # The shader clock is read right before the start event and right after the end event, on
+    # the same stream, outside the timed region.
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    clk_at["before_timed_steps"] = clk.enqueue()
     t_wall = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
         step(i)
     end.record(stream)
+    clk_at["after_timed_steps"] = clk.enqueue()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     telemetry["after_timed_steps"] = read_telemetry()
+    telemetry["shader_clock"] = {k: clk.read(i) for k, i in clk_at.items()}
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
     log(f"[bench] {args.steps} steps in {total_ms:.2f} ms (wall {wall * 1e3:.1f} ms): "
@@ -639,6 +768,8 @@ def main(argv=None):
         res["attainable_read"] = {"best": best, "bytes": nbytes, "sweep": rows,
                                   "kernel": "kvq_probe_stream_read (plain streaming read)"}
     res["telemetry"] = telemetry
+    if args.sustained > 0:
+        res["sustained"] = sustained_run(torch, stream, step, clk, args.sustained)
 
     if args.prefill_chunk > 0 and not win:
         res["prefill_attn"] = bench_prefill(kvq, torch, wl, inp, caches, stream, args.prefill_chunk)

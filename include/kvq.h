@@ -369,6 +369,20 @@ const char* kvq_strerror(int code);
 int kvq_probe_stream_read(const void* buf, size_t bytes, int32_t mode, int32_t workgroups,
                           uint32_t* sink, void* stream);
 
+/* kvq_probe_clock: the shader clock the GPU runs at right now, read from its own counters (the
+ * forum post, 二、测评, reports core clock and power cap beside its decode speeds, since both move
+ * them).  Each of `workgroups` one-wave workgroups spins until the GPU's constant-rate counter
+ * has advanced `spin_ticks` ticks and writes three uint64 to out[3 i .. 3 i + 2]: the
+ * shader-clock cycles counted over the spin, the constant-rate ticks, and the XCD (accelerator
+ * complex die) the wave ran on.  cycles / ticks * *const_rate_khz is the clock in kHz.
+ * out: device memory, 8-byte aligned, 3 * workgroups entries, written by the kernel;
+ * const_rate_khz: host, may be NULL, receives the constant counter's rate when not NULL.
+ * workgroups 1 .. 4096, spin_ticks 1 .. 10,000,000.  With out NULL and workgroups 0 nothing is
+ * launched and only *const_rate_khz is written (it must then be given).  Returns KVQ_OK,
+ * KVQ_ERR_ARG or KVQ_ERR_HIP. */
+int kvq_probe_clock(uint64_t* out, int32_t workgroups, uint32_t spin_ticks, int32_t* const_rate_khz,
+                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -569,3 +569,24 @@ extern "C" int kvq_probe_stream_read(const void* buf, size_t bytes, int32_t mode
              ? KVQ_OK
              : KVQ_ERR_HIP;
 }
+
+extern "C" int kvq_probe_clock(uint64_t* out, int32_t workgroups, uint32_t spin_ticks, int32_t* const_rate_khz,
+                               void* stream) {
+  const bool query_only = !out && workgroups == 0;  // only the constant counter's rate
+  if (query_only ? !const_rate_khz : (!out || ((uintptr_t)out & 7) != 0 || workgroups < 1 || workgroups > 4096))
+    return KVQ_ERR_ARG;
+  if (!query_only && (spin_ticks < 1 || spin_ticks > 10000000u)) return KVQ_ERR_ARG;
+  (void)hipGetLastError();
+  if (const_rate_khz) {
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+      return KVQ_ERR_HIP;
+    *const_rate_khz = khz;
+  }
+  if (query_only) return KVQ_OK;
+  return kvq::launch_clock_probe((unsigned long long*)out, workgroups, spin_ticks, (hipStream_t)stream) ==
+                 hipSuccess
+             ? KVQ_OK
+             : KVQ_ERR_HIP;
+}

@@ -76,6 +76,7 @@ hipError_t launch_decode(int head_dim, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(int head_dim, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_stream_probe(const void* buf, size_t bytes, int mode, int workgroups, uint32_t* sink,
                                hipStream_t stream);
+hipError_t launch_clock_probe(unsigned long long* out, int workgroups, unsigned ticks, hipStream_t stream);
 
 constexpr int kPrefillRowsPerTile = 256;  // query rows of one prefill workgroup (32 per wave)
 constexpr int kPrefillThreads = 512;      // 8 waves per prefill workgroup

@@ -4,6 +4,8 @@
 // per token against the card's bandwidth; this kernel measures that bandwidth on the device
 // itself, with nothing else to do but read.
 //
+// A second probe reads the shader clock the kernels run at, from the GPU's own counters.
+//
 // Three load forms: 16-byte loads into registers, non-temporal (mode 0) or normal (mode 1), and
 // the decode's own form, gfx950 direct-to-LDS 16-byte loads, non-temporal (mode 2).  Every byte
 // is read once.  A per-lane xor of the loaded words goes to `sink` only if it equals a value
@@ -60,7 +62,32 @@ __global__ __launch_bounds__(kProbeThreads) void stream_read_lds_kernel(const ui
   if (threadIdx.x == 0 && s_ring[0][0][0] == 0xA5 && s_ring[0][0][1] == 0x5A && n4k == 0) sink[0] = kSinkMagic;
 }
 
+// Shader clock: each one-wave workgroup counts shader-clock cycles (s_memtime) across a spin
+// of `ticks` ticks of the constant-rate counter (s_memrealtime); the spin ends when the
+// constant-rate counter has moved that far, which it always does.  Lane 0 writes the cycles,
+// the ticks and the XCD the wave ran on (hardware register XCC_ID).
+__global__ __launch_bounds__(kWave) void clock_probe_kernel(unsigned long long* out, unsigned ticks) {
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  const unsigned long long c0 = __builtin_amdgcn_s_memtime();
+  unsigned long long r1;
+  do {
+    r1 = __builtin_amdgcn_s_memrealtime();
+  } while (r1 - r0 < ticks);
+  const unsigned long long c1 = __builtin_amdgcn_s_memtime();
+  const unsigned xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xFu;  // XCC_ID bits 3:0
+  if (threadIdx.x == 0) {
+    out[3 * blockIdx.x] = c1 - c0;
+    out[3 * blockIdx.x + 1] = r1 - r0;
+    out[3 * blockIdx.x + 2] = xcc;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_clock_probe(unsigned long long* out, int workgroups, unsigned ticks, hipStream_t stream) {
+  hipLaunchKernelGGL(clock_probe_kernel, dim3((unsigned)workgroups), dim3(kWave), 0, stream, out, ticks);
+  return hipGetLastError();
+}
 
 hipError_t launch_stream_probe(const void* buf, size_t bytes, int mode, int workgroups, uint32_t* sink,
                                hipStream_t stream) {

@@ -100,6 +100,8 @@ def lib():
         L.kvq_prefill_workspace_bytes.restype = ctypes.c_size_t
         L.kvq_probe_stream_read.argtypes = [P, ctypes.c_size_t, I, I, P, P]
         L.kvq_probe_stream_read.restype = ctypes.c_int
+        L.kvq_probe_clock.argtypes = [P, I, ctypes.c_uint32, ctypes.POINTER(ctypes.c_int32), P]
+        L.kvq_probe_clock.restype = ctypes.c_int
         _lib = L
         return L
 
@@ -473,4 +475,30 @@ def prepare_stream_probe(buf: torch.Tensor, mode: int, workgroups: int, sink: to
         rc = lib().kvq_probe_stream_read(*args)
         if rc != KVQ_OK:
             raise KVQError(rc, "kvq_probe_stream_read")
+    return call
+
+
+def clock_counter_khz() -> int:
+    """Rate of the GPU's constant-rate counter that kvq_probe_clock sets the shader clock
+    against, in kHz (no launch)."""
+    khz = ctypes.c_int32(0)
+    rc = lib().kvq_probe_clock(None, 0, 0, ctypes.byref(khz), None)
+    if rc != KVQ_OK:
+        raise KVQError(rc, "kvq_probe_clock")
+    return khz.value
+
+
+def prepare_clock_probe(out: torch.Tensor, spin_ticks: int = 2000, stream=None):
+    """kvq_probe_clock with one workgroup per three int64 entries of ``out``: each call of the
+    returned callable enqueues a spin of ``spin_ticks`` constant-rate ticks and leaves
+    (shader cycles, ticks, XCD) per workgroup in ``out``; shader MHz = cycles / ticks *
+    clock_counter_khz() / 1000."""
+    if out.dtype != torch.int64 or out.numel() % 3 != 0:
+        raise ValueError("out: int64 with 3 entries per workgroup")
+    args = (_dev(out, "out", torch.int64), out.numel() // 3, int(spin_ticks), None, _stream_ptr(stream))
+
+    def call():
+        rc = lib().kvq_probe_clock(*args)
+        if rc != KVQ_OK:
+            raise KVQError(rc, "kvq_probe_clock")
     return call

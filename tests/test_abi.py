@@ -373,3 +373,28 @@ def test_grids_beyond_32_bit_work_items_are_refused(lib):
     assert prefill_rc(lib, n_seq=32, hkv=4, hq=32, d=256, chunk=8192, page_size=64,
                       num_pages=1 << 14, max_pages=256, max_seq_len=16384, splits=1,
                       ws=None) == E.KVQ_ERR_WORKSPACE
+
+
+def test_probe_validation(lib):
+    """The measurement probes refuse bad arguments on the host, before any HIP call."""
+    E = kvq
+    P = ctypes.c_void_p
+    buf = P(1 << 20)
+    sink = P(4096)
+    f = lib.kvq_probe_stream_read
+    assert f(None, 4096, 0, 1, sink, None) == E.KVQ_ERR_ARG
+    assert f(buf, 4095, 0, 1, sink, None) == E.KVQ_ERR_ARG          # not a multiple of 4 KB
+    assert f(P((1 << 20) + 16), 4096, 0, 1, sink, None) == E.KVQ_ERR_ARG  # not 4 KB aligned
+    assert f(buf, 4096, 3, 1, sink, None) == E.KVQ_ERR_ARG          # no such load form
+    assert f(buf, 4096, 0, 0, sink, None) == E.KVQ_ERR_ARG
+    assert f(buf, 4096, 0, (1 << 20) + 1, sink, None) == E.KVQ_ERR_ARG
+    assert f(buf, 4096, 0, 1, None, None) == E.KVQ_ERR_ARG
+    g = lib.kvq_probe_clock
+    out = P(1 << 20)
+    assert g(None, 1, 100, None, None) == E.KVQ_ERR_ARG
+    assert g(P((1 << 20) + 4), 1, 100, None, None) == E.KVQ_ERR_ARG  # not 8-byte aligned
+    assert g(out, 0, 100, None, None) == E.KVQ_ERR_ARG
+    assert g(out, 4097, 100, None, None) == E.KVQ_ERR_ARG
+    assert g(out, 1, 0, None, None) == E.KVQ_ERR_ARG
+    assert g(out, 1, 10000001, None, None) == E.KVQ_ERR_ARG
+    assert g(None, 0, 0, None, None) == E.KVQ_ERR_ARG  # the rate query needs somewhere to write
