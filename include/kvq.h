@@ -140,7 +140,9 @@ size_t kvq_block_bytes_fmt(int32_t kv_format, int32_t page_size, int32_t head_di
  * Tokens are taken in groups of 16 (token indices 16i .. 16i+15).  A group whose slots are the
  * 16 slots of one tile in order (a prefill or a chunk of one, starting at a tile boundary) is
  * written as whole tiles, which is the fast case; any other group token by token.  The bytes
- * are the same either way.
+ * are the same either way.  Each group and KV head is one workgroup of 256 threads, so a call
+ * with ceil(n_tok / 16) * num_kv_heads * 256 >= 2^32 (HIP's grid limit) is refused with
+ * KVQ_ERR_UNSUPPORTED.
  * Returns KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED or KVQ_ERR_HIP.
  */
 int kvq_append(void* pool, int32_t num_pages, int32_t page_size, int32_t num_kv_heads,

@@ -161,7 +161,8 @@ int kvq_append_fmt(int32_t kv_format, void* pool, int32_t num_pages, int32_t pag
   if (n_tok < 0) return KVQ_ERR_ARG;
   if (n_tok == 0) return KVQ_OK;
   if (!k || !v || !slot_mapping) return KVQ_ERR_ARG;
-  if ((long long)n_tok * num_kv_heads > (1LL << 33)) return KVQ_ERR_ARG;
+  // one 256-thread workgroup per 16 tokens and KV head: fewer than 2^32 work-items
+  if ((unsigned long long)((n_tok + 15) / 16) * num_kv_heads * 256 >= (1ULL << 32)) return KVQ_ERR_UNSUPPORTED;
   kvq::AppendArgs a{(uint8_t*)pool, num_pages,    page_size, num_kv_heads, vb,
                     kv_format == KVQ_FORMAT_FP8, k, v,         slot_mapping, n_tok};
   (void)hipGetLastError();  // start from a clean error state

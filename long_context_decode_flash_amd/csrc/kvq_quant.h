@@ -22,16 +22,57 @@ __device__ inline void wave_lds_order() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ inline float wave_max(float x, int width) {
-  // butterfly over groups of `width` lanes (width a power of two <= 64)
-  for (int off = width / 2; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));
-  return x;
+// max over each aligned group of W lanes (W a power of two <= 64) of a non-negative float
+// given by its bits (for those, unsigned order of the bits is value order), with DPP moves
+// inside rows of 16 lanes and the gfx950 row / half swaps across them: VALU only, no LDS round
+// trips.  After the quad steps a lane holds its quad's max; the half-row mirror pairs the two
+// quads of an 8-lane group, the row mirror the two halves of a row.
+template <int W>
+__device__ inline uint32_t group_max_bits(uint32_t u) {
+  static_assert(W >= 1 && W <= 64 && (W & (W - 1)) == 0, "group width");
+  auto mx = [](uint32_t a, int b) { return a > (uint32_t)b ? a : (uint32_t)b; };
+  if constexpr (W >= 2) u = mx(u, __builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
+  if constexpr (W >= 4) u = mx(u, __builtin_amdgcn_mov_dpp((int)u, 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
+  if constexpr (W >= 8) u = mx(u, __builtin_amdgcn_mov_dpp((int)u, 0x141, 0xF, 0xF, true));  // row_half_mirror
+  if constexpr (W >= 16) u = mx(u, __builtin_amdgcn_mov_dpp((int)u, 0x140, 0xF, 0xF, true)); // row_mirror
+  if constexpr (W >= 32) {  // rows (0, 1) and (2, 3) meet
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    u = mx(a[0], (int)a[1]);
+  }
+  if constexpr (W >= 64) {  // the two halves meet
+    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    u = mx(a[0], (int)a[1]);
+  }
+  return u;
+}
+
+// absolute-value bits of a float (non-finite inputs are undefined)
+__device__ inline uint32_t abs_bits(float x) { return __builtin_bit_cast(uint32_t, x) & 0x7FFFFFFFu; }
+
+// The IEEE fp32 quotient x / d (round to nearest even) from r = recip_for(d), so that every
+// element of a group shares one reciprocal.  These are the steps of the correctly rounded
+// divide this library is built with (reciprocal, one refinement, then two fused remainder
+// corrections of the quotient) without its range scaling, which only acts when x or x / d is
+// near the subnormal range or their exponents lie about 96 or more apart.  Every quotient the
+// quantizer takes is outside those cases for finite inputs except two whose result does not
+// depend on the last bit: a subnormal x (code 0) and a saturated scale (|x / d| far above the
+// largest code, clamped).  Unlike the full divide it returns +0 for x = -0 (the corrections add
+// +0); a caller that needs the sign of a zero quotient restores it.  Non-finite inputs are
+// undefined.
+__device__ inline float recip_for(float d) {
+  const float r = __builtin_amdgcn_rcpf(d);
+  return __builtin_fmaf(__builtin_fmaf(-d, r, 1.0f), r, r);
+}
+__device__ inline float div_rn(float x, float d, float r) {
+  float y = x * r;
+  y = __builtin_fmaf(__builtin_fmaf(-d, y, x), r, y);
+  return __builtin_fmaf(__builtin_fmaf(-d, y, x), r, y);
 }
 
 // fp16 scale of one group: round-to-nearest-even of the fp32 quotient, saturated to the largest
 // finite fp16.  Returns the fp16 bits; *s receives its value in fp32.
 __device__ inline uint16_t group_scale(float absmax, float qmax, float* s) {
-  float s32 = absmax / qmax;  // IEEE fp32 division (built with correctly rounded divide)
+  float s32 = div_rn(absmax, qmax, recip_for(qmax));  // the IEEE fp32 quotient
   _Float16 h = (_Float16)s32;  // v_cvt_f16_f32: round to nearest even
   uint16_t bits = __builtin_bit_cast(uint16_t, h);
   if ((bits & 0x7FFF) == 0x7C00) bits = 0x7BFF;
@@ -39,11 +80,12 @@ __device__ inline uint16_t group_scale(float absmax, float qmax, float* s) {
   return bits;
 }
 
-__device__ inline int quantize_one(float x, float s, float qmax) {
-  if (s == 0.0f) return 0;
-  float c = __builtin_rintf(x / s);  // IEEE divide, round half to even
-  c = fminf(fmaxf(c, -qmax), qmax);
-  return (int)c;
+// code of x at scale s (r = recip_for(s)); a zero scale gives code 0 (the quotient is then
+// computed and dropped: a select, not a branch per element)
+__device__ inline int quantize_one(float x, float s, float r, float qmax) {
+  const float c = __builtin_rintf(div_rn(x, s, r));  // IEEE quotient, round half to even
+  const int code = (int)__builtin_amdgcn_fmed3f(c, -qmax, qmax);
+  return s == 0.0f ? 0 : code;
 }
 
 // OCP FP8 E4M3 code of y, |y| <= 448, rounded to the nearest E4M3 value with ties to the even
@@ -63,10 +105,12 @@ __device__ inline uint32_t e4m3_rne(float y) {
   return sign | mag;
 }
 
-__device__ inline uint32_t quantize_one_f8(float x, float s) {
-  if (s == 0.0f) return 0u;
-  const float y = x / s;  // IEEE divide
-  return e4m3_rne(fminf(fmaxf(y, -448.0f), 448.0f));
+__device__ inline uint32_t quantize_one_f8(float x, float s, float r) {
+  // IEEE quotient; the corrections turn -0 / s into +0, so the sign (s > 0) is x's: -0 keeps
+  // its own code (0x80), as in the IEEE divide
+  const float y = __builtin_copysignf(div_rn(x, s, r), x);
+  const uint32_t code = e4m3_rne(__builtin_amdgcn_fmed3f(y, -448.0f, 448.0f));
+  return s == 0.0f ? 0u : code;
 }
 
 // A wave's share of one token's K and V rows: lane l holds dims E*l .. E*l + E-1.
@@ -76,14 +120,16 @@ struct RowVals {
   float k[E], v[E];
 };
 
+// The lane's E values of a token's K and V rows, loaded non-temporally (each input row is read
+// once).
 template <int D>
 __device__ __attribute__((always_inline)) inline RowVals<D> load_row(const float* krow_base, const float* vrow_base, int lane) {
   RowVals<D> r;
   const int d0 = lane * RowVals<D>::E;
 #pragma unroll
   for (int e = 0; e < RowVals<D>::E; ++e) {
-    r.k[e] = krow_base[d0 + e];
-    r.v[e] = vrow_base[d0 + e];
+    r.k[e] = __builtin_nontemporal_load(krow_base + d0 + e);
+    r.v[e] = __builtin_nontemporal_load(vrow_base + d0 + e);
   }
   return r;
 }
@@ -101,16 +147,17 @@ __device__ __attribute__((always_inline)) inline void store_row(uint8_t* blk, in
   const float* vx = r.v;
 
   // ---- K: one scale per token and head (qmax 127) ----
-  float ka = 0.0f;
+  uint32_t kab = 0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) ka = fmaxf(ka, fabsf(kx[e]));
-  ka = wave_max(ka, kWave);
+  for (int e = 0; e < E; ++e) kab = max(kab, abs_bits(kx[e]));
+  const float ka = __builtin_bit_cast(float, group_max_bits<kWave>(kab));
   float ks;
   const uint16_t ks_bits = group_scale(ka, F8 ? 448.0f : 127.0f, &ks);
+  const float kr = recip_for(ks);
   uint32_t kpacked = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e)
-    kpacked |= (F8 ? quantize_one_f8(kx[e], ks) : (uint32_t)(quantize_one(kx[e], ks, 127.0f) & 0xFF)) << (8 * e);
+    kpacked |= (F8 ? quantize_one_f8(kx[e], ks, kr) : (uint32_t)(quantize_one(kx[e], ks, kr, 127.0f) & 0xFF)) << (8 * e);
   // K code (t, d) at 16*D*tile + 256*(d/16) + 16*t + d%16; E consecutive dims stay in one chunk
   uint8_t* kdst = blk + (size_t)16 * D * tile + 256 * (d0 / 16) + 16 * t + d0 % 16;
   if constexpr (E == 4) {
@@ -124,12 +171,13 @@ __device__ __attribute__((always_inline)) inline void store_row(uint8_t* blk, in
 
   // ---- V: one scale per 32 dims (qmax 7, or 127 for 8-bit codes), 32/E lanes per group ----
   constexpr float vqmax = F8 ? 448.0f : VB == 8 ? 127.0f : 7.0f;
-  float va = 0.0f;
+  uint32_t vab = 0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) va = fmaxf(va, fabsf(vx[e]));
-  va = wave_max(va, 32 / E);
+  for (int e = 0; e < E; ++e) vab = max(vab, abs_bits(vx[e]));
+  const float va = __builtin_bit_cast(float, group_max_bits<32 / E>(vab));
   float vsc;
   const uint16_t vs_bits = group_scale(va, vqmax, &vsc);
+  const float vr = recip_for(vsc);
   const int j = d0 / 32;
   if (d0 % 32 == 0) *(uint16_t*)(blk + v_scales_at(P, D, VB) + 2 * ((size_t)s * (D / 32) + j)) = vs_bits;
   if constexpr (VB == 8) {
@@ -141,17 +189,25 @@ __device__ __attribute__((always_inline)) inline void store_row(uint8_t* blk, in
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int vlane = 16 * (t / 4) + (d0 + e) % 16;
-      vbase[8 * w * vlane] = F8 ? (uint8_t)quantize_one_f8(vx[e], vsc) : (uint8_t)(quantize_one(vx[e], vsc, vqmax) & 0xFF);
+      vbase[8 * w * vlane] = F8 ? (uint8_t)quantize_one_f8(vx[e], vsc, vr) : (uint8_t)(quantize_one(vx[e], vsc, vr, vqmax) & 0xFF);
     }
     return;
   }
   uint32_t vnib = 0;  // E nibbles, dim d0+e at bits 4e
 #pragma unroll
-  for (int e = 0; e < E; ++e) vnib |= (uint32_t)(quantize_one(vx[e], vsc, 7.0f) & 0xF) << (4 * e);
+  for (int e = 0; e < E; ++e) vnib |= (uint32_t)(quantize_one(vx[e], vsc, vr, 7.0f) & 0xF) << (4 * e);
 
   // Dims d (d/16 even) and d+16 share a byte (low / high nibble).  The lane holding d gets the
-  // partner's nibbles from 16/E lanes up and writes the E bytes.
-  const uint32_t partner = __shfl_down(vnib, 16 / E, kWave);
+  // partner's nibbles from 16/E lanes up and writes the E bytes.  With E = 4 or 2 the partner is
+  // in the same row of 16 lanes (DPP row shift left: lane i reads lane i + 16/E); with E = 1 it
+  // is in the next row.
+  uint32_t partner;
+  if constexpr (E == 4)
+    partner = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)vnib, 0x104, 0xF, 0xF, false);  // row_shl:4
+  else if constexpr (E == 2)
+    partner = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)vnib, 0x108, 0xF, 0xF, false);  // row_shl:8
+  else
+    partner = __shfl_down(vnib, 16, kWave);
   if (((d0 / 16) & 1) == 0) {
     constexpr int w = (D / 32) < 4 ? (D / 32) : 4;
     const int r = t % 4;

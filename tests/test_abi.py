@@ -362,6 +362,9 @@ def test_grids_beyond_32_bit_work_items_are_refused(lib):
     # one sequence fewer passes the grid check and stops at the (missing) workspace
     assert decode_rc(lib, n_seq=(1 << 16) - 1, hkv=256, hq=256, num_pages=1 << 10, splits=1,
                      ws=None) == E.KVQ_ERR_WORKSPACE
+    # append: one 256-thread workgroup per 16 tokens and KV head: 2^20 groups x 16 heads x 256
+    assert append_rc(lib, hkv=16, n_tok=1 << 24, num_pages=1 << 10) == E.KVQ_ERR_UNSUPPORTED
+    assert append_rc(lib, hkv=16, n_tok=(1 << 24) - 15, num_pages=1 << 10) == E.KVQ_ERR_UNSUPPORTED
     # decode merge: 2^18 units x 2 splits: 256 merge workgroups of 64 lanes per unit
     assert decode_rc(lib, n_seq=1 << 16, hkv=4, hq=128, d=256, page_size=64, num_pages=64,
                      max_pages=8, max_seq_len=400, splits=2) == E.KVQ_ERR_UNSUPPORTED

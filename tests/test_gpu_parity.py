@@ -63,7 +63,8 @@ def test_append_fp8_rounding_edges_bit_exact():
     absmax 448 the scale is exactly 1, so each value is its own quotient: exact midpoints
     between normal neighbours (ties go to the even mantissa), midpoints between subnormals and
     at the subnormal/normal edge, negative values that round to zero (code 0x80), the largest
-    value; plus zero, tiny and huge rows and V groups of mixed magnitudes."""
+    value, and -0.0 itself (code 0x80, the sign of the IEEE quotient); plus zero, tiny and huge
+    rows and V groups of mixed magnitudes."""
     H.say("[append fp8 edges]")
     rng = np.random.default_rng(79)
     ties = np.array([1.0625, 1.1875, 1.3125, 3.75 + 0.125, 0.5 * 2.0 ** -9, 1.5 * 2.0 ** -9,
@@ -82,8 +83,11 @@ def test_append_fp8_rounding_edges_bit_exact():
         v[2] *= np.float32(1e6)
         row = np.resize(np.concatenate([ties, -ties]), D).astype(np.float32)
         row[0] = 448.0
+        row[1] = -0.0
         k[3] = row
         v[3] = row
+        k[7, :, 3::17] = np.float32(-0.0)
+        v[7, :, 5::11] = np.float32(-0.0)
         v[4, :, :] = np.float32(3.5)
         v[4, :, ::32] = np.float32(448.0)
         slots = rng.choice(pages * P, n, replace=False).astype(np.int32)
