@@ -209,6 +209,58 @@ class ShaderClock:
                 "xcd_max_mhz": round(max(per))}
 
 
+def time_appends(kvq, torch, wl, inp, caches, apps, n_pre, D, vbits, dev_t, chunk_arg):
+    """The prefill append (`reps` more passes of every sequence's kvq_append over its cached
+    tokens, rewriting the same bytes) and one prefill chunk of one sequence (the engine's
+    --prefill-chunk 1024 in the forum post, 一、部署: the last `chunk` cached tokens of
+    sequence 0, rewritten in place), each event-timed over back-to-back calls."""
+    from long_context_decode_flash_amd import workloads as W
+    reps = 5
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for app in apps:
+        app()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        for app in apps:
+            app()
+    e1.record()
+    torch.cuda.synchronize()
+    prefill_us = e0.elapsed_time(e1) * 1e3 / reps
+    prefill_bytes = n_pre * wl.num_kv_heads * (2 * D * 4 + token_bytes(D, vbits)) + n_pre * 4
+    log(f"[bench] prefill append of {n_pre} tokens: {prefill_us:.1f} us, "
+        f"{prefill_bytes / prefill_us / 1e3:.0f} GB/s")
+    chunk_n = min(chunk_arg or 1024, wl.seq_len - wl.n_new)
+    c0 = wl.seq_len - wl.n_new - chunk_n
+    ck = dev_t(inp.k[0, c0:c0 + chunk_n])
+    cv = dev_t(inp.v[0, c0:c0 + chunk_n])
+    cs = dev_t(W.slots_for(inp.page_table, wl.page_size, 0, c0, c0 + chunk_n))
+    capp = kvq.prepare_append(caches[0], ck, cv, cs)
+    capp()
+    torch.cuda.synchronize()
+    creps = 50
+    e0.record()
+    for _ in range(creps):
+        capp()
+    e1.record()
+    torch.cuda.synchronize()
+    chunk_us = e0.elapsed_time(e1) * 1e3 / creps
+    chunk_bytes = chunk_n * wl.num_kv_heads * (2 * D * 4 + token_bytes(D, vbits)) + chunk_n * 4
+    log(f"[bench] append of one {chunk_n}-token chunk: {chunk_us:.1f} us, "
+        f"{chunk_bytes / chunk_us / 1e3:.0f} GB/s")
+    return {
+        "tokens": n_pre,
+        "us": round(prefill_us, 1),
+        "algorithmic_bytes": prefill_bytes,
+        "GB_s": round(prefill_bytes / prefill_us / 1e3, 1),
+        "frac_of_hbm_peak": round(prefill_bytes / prefill_us / 1e3 / HBM_PEAK_GBS, 4),
+        "kernel": "kvq_append: append_kernel, one call per sequence over its cached tokens",
+        "chunk": {"tokens": chunk_n, "us": round(chunk_us, 2), "algorithmic_bytes": chunk_bytes,
+                  "GB_s": round(chunk_bytes / chunk_us / 1e3, 1),
+                  "note": "one kvq_append of one sequence's chunk, back-to-back calls, event-timed"},
+    }
+
+
 def sustained_run(torch, stream, step, clk, n, group=50):
     """n more back-to-back steps (after the timed region, which they do not touch), timed in
     groups of `group` with a shader-clock reading after each group: how the step time follows
@@ -243,8 +295,10 @@ def sustained_run(torch, stream, step, clk, n, group=50):
 def attainable_probe(kvq, torch, dev, stream, gib=2, reps=5):
     """The plain streaming read (kvq_probe_stream_read) over a `gib` GiB buffer in each load form
     and a few grid sizes, event-timed over `reps` calls each; returns the best and every
-    result.  The sweep streams for a few tens of milliseconds, and runs right before the
-    decode's warm-up, so both are measured in the same sustained state of the GPU."""
+    result.  The sweep streams for a few tens of milliseconds; it runs after the timed decode
+    steps, whose shader clock it would otherwise lower (the power management's answer to a
+    sustained streaming load lasts some milliseconds after it)."""
+
     n = gib << 30
     buf = torch.empty(n, dtype=torch.uint8, device=dev)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -575,8 +629,7 @@ def main(argv=None):
                                       kv_format=fmt)]
     k_pre, v_pre, s_pre = (dev_t(x) for x in inp.prefill())
     # The prefill append (one kvq_append call per sequence, over all its cached tokens, as an
-    # engine's prefill writes them) is timed too: once to fill the pool, then `reps` more times
-    # over the same slots (idempotent), event-timed.
+    # engine's prefill writes them) fills the pool here; it is timed after the decode.
     n_pre = int(s_pre.numel())
     per = n_pre // wl.n_seq  # tokens are sequence-major, the same count per sequence
     apps = [kvq.prepare_append(caches[0], k_pre[i * per:(i + 1) * per], v_pre[i * per:(i + 1) * per],
@@ -584,39 +637,6 @@ def main(argv=None):
     for app in apps:
         app()
     torch.cuda.synchronize()
-    reps = 5
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        for app in apps:
-            app()
-    e1.record()
-    torch.cuda.synchronize()
-    prefill_us = e0.elapsed_time(e1) * 1e3 / reps
-    prefill_bytes = n_pre * wl.num_kv_heads * (2 * D * 4 + token_bytes(D, vbits)) + n_pre * 4
-    log(f"[bench] prefill append of {n_pre} tokens: {prefill_us:.1f} us, "
-        f"{prefill_bytes / prefill_us / 1e3:.0f} GB/s")
-    # one prefill chunk of one sequence (the engine's --prefill-chunk 1024 in the forum post,
-    # 一、部署): the last `chunk` cached tokens of sequence 0, rewritten in place (idempotent)
-    chunk_n = min(args.prefill_chunk or 1024, wl.seq_len - wl.n_new)
-    c0 = wl.seq_len - wl.n_new - chunk_n
-    ck = dev_t(inp.k[0, c0:c0 + chunk_n])
-    cv = dev_t(inp.v[0, c0:c0 + chunk_n])
-    cs = dev_t(W.slots_for(inp.page_table, wl.page_size, 0, c0, c0 + chunk_n))
-    capp = kvq.prepare_append(caches[0], ck, cv, cs)
-    capp()
-    torch.cuda.synchronize()
-    creps = 50
-    e0.record()
-    for _ in range(creps):
-        capp()
-    e1.record()
-    torch.cuda.synchronize()
-    chunk_us = e0.elapsed_time(e1) * 1e3 / creps
-    chunk_bytes = chunk_n * wl.num_kv_heads * (2 * D * 4 + token_bytes(D, vbits)) + chunk_n * 4
-    log(f"[bench] append of one {chunk_n}-token chunk: {chunk_us:.1f} us, "
-        f"{chunk_bytes / chunk_us / 1e3:.0f} GB/s")
-    del k_pre, v_pre, apps, ck, cv, cs, capp
     for _ in range(args.copies - 1):
         c = kvq.PagedCache.allocate(wl.pool_pages, wl.page_size, wl.num_kv_heads, D, dev,
                                     kv_format=fmt)
@@ -660,14 +680,15 @@ def main(argv=None):
     def step(i):
         calls[i % len(calls)]()
 
+    # The timed decode comes first after the set-up: the other measurements (the attainable
+    # streaming read, the append timings, the prefill attention) stream for tens of
+    # milliseconds, and the GPU's power management answers such a load by lowering the shader
+    # clock for some milliseconds after it (measured with kvq_probe_clock), which the timed
+    # steps would otherwise inherit.
     telemetry = {"idle": read_telemetry()}
     clk = ShaderClock(kvq, torch, dev, stream)
     torch.cuda.synchronize()
-    clk_at = {"before_attainable": clk.enqueue()}
-    attainable = None
-    if not args.no_attainable:
-        attainable = attainable_probe(kvq, torch, dev, stream)
-        clk_at["after_attainable"] = clk.enqueue()
+    clk_at = {}
 
     for i in range(args.warmup):
         step(i)
@@ -692,6 +713,11 @@ def main(argv=None):
     wall = time.perf_counter() - t_wall
     telemetry["after_timed_steps"] = read_telemetry()
     telemetry["shader_clock"] = {k: clk.read(i) for k, i in clk_at.items()}
+    attainable = None
+    if not args.no_attainable:
+        attainable = attainable_probe(kvq, torch, dev, stream)
+    append_res = time_appends(kvq, torch, wl, inp, caches, apps, n_pre, D, vbits, dev_t, args.prefill_chunk)
+    del k_pre, v_pre, apps
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
     log(f"[bench] {args.steps} steps in {total_ms:.2f} ms (wall {wall * 1e3:.1f} ms): "
@@ -774,17 +800,7 @@ def main(argv=None):
     if args.prefill_chunk > 0 and not win:
         res["prefill_attn"] = bench_prefill(kvq, torch, wl, inp, caches, stream, args.prefill_chunk)
 
-    res["prefill_append"] = {
-        "tokens": n_pre,
-        "us": round(prefill_us, 1),
-        "algorithmic_bytes": prefill_bytes,
-        "GB_s": round(prefill_bytes / prefill_us / 1e3, 1),
-        "frac_of_hbm_peak": round(prefill_bytes / prefill_us / 1e3 / HBM_PEAK_GBS, 4),
-        "kernel": "kvq_append: append_kernel, one call per sequence over its cached tokens",
-        "chunk": {"tokens": chunk_n, "us": round(chunk_us, 2), "algorithmic_bytes": chunk_bytes,
-                  "GB_s": round(chunk_bytes / chunk_us / 1e3, 1),
-                  "note": "one kvq_append of one sequence's chunk, back-to-back calls, event-timed"},
-    }
+    res["prefill_append"] = append_res
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline: oracle on full steps, about 10 s")
         dt, n_cpu, cores = cpu_baseline(wl, inp, window=win, kv_format=fmt)
