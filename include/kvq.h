@@ -358,6 +358,22 @@ size_t kvq_prefill_workspace_bytes(int32_t n_seq, int32_t chunk, int32_t n_q_hea
 /* Static description of a return code. */
 const char* kvq_strerror(int code);
 
+/* ---- KVQ_DEBUG builds: device-side range reports -------------------------------------------
+ * The library built with -DKVQ_DEBUG (libkvq_debug.so) computes exactly what the normal build
+ * does, and its kernels also record, in one word per GPU, any input they had to correct: bit
+ * KVQ_DBG_PAGE_ID when a page-table entry the call reads lies outside [0, num_pages) (decode,
+ * fused append, prefill; the id is still clamped, never followed), bit KVQ_DBG_SLOT when an
+ * append slot lies at or past num_pages * page_size (still skipped; negative slots mark padding
+ * and are not reported).  This is the device-side counterpart of the host's argument checks:
+ * ids and slots live in device memory, so only the kernels see them.
+ * kvq_debug_errors: waits for `stream`, writes the word to *errors (host), and clears it when
+ * `clear` is non-zero.  Host-synchronous; not for use under graph capture.  Every call on a GPU
+ * reports into the same word.  Returns KVQ_OK, KVQ_ERR_ARG (errors NULL) or KVQ_ERR_HIP in a
+ * KVQ_DEBUG build, and KVQ_ERR_UNSUPPORTED in any other build. */
+#define KVQ_DBG_PAGE_ID 1u
+#define KVQ_DBG_SLOT 2u
+int kvq_debug_errors(uint32_t* errors, int32_t clear, void* stream);
+
 /* ---- measurement helper (not part of the method) -------------------------------------------
  * kvq_probe_stream_read: read `bytes` of device memory at `buf` once, as a plain stream, so that
  * a benchmark can set the decode's achieved bandwidth against what this GPU attains for a pure

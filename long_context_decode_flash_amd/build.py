@@ -32,6 +32,11 @@ HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize
                  "-Xarch_host", "-g"]
 
 
+# The device-side range-check build (kernels also report corrected page ids and slots; see
+# kvq_debug_errors in include/kvq.h).
+DEBUG_LIB = os.path.join(HERE, "libkvq_debug.so")
+
+
 def asan_runtime() -> str:
     """The clang AddressSanitizer runtime matching hipcc's host compiler (to LD_PRELOAD into a
     Python process that loads the sanitized library)."""
@@ -43,11 +48,14 @@ def asan_runtime() -> str:
 
 
 def build(verbose: bool = False, extra: list[str] | None = None, out: str = LIB,
-          sanitize: bool = False) -> str:
+          sanitize: bool = False, debug: bool = False) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     if sanitize:
         extra = [*(extra or []), *HOST_SANITIZE]
         out = SANITIZED_LIB if out == LIB else out
+    if debug:
+        extra = [*(extra or []), "-DKVQ_DEBUG"]
+        out = DEBUG_LIB if out == LIB else out
     cmd = [HIPCC, *FLAGS, *(extra or []), "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            "-o", out + ".tmp", *srcs]
     if verbose:
@@ -58,7 +66,7 @@ def build(verbose: bool = False, extra: list[str] | None = None, out: str = LIB,
             if l.strip() and "packed-fp32-ops" not in l and "not a recognized feature" not in l]
     if res.returncode != 0:
         sys.stderr.write("\n".join(msgs) + "\n")
-        raise RuntimeError("hipcc failed building libkvq.so")
+        raise RuntimeError(f"hipcc failed building {os.path.basename(out)}")
     if verbose and msgs:
         print("\n".join(msgs))
     os.replace(out + ".tmp", out)
@@ -67,3 +75,4 @@ def build(verbose: bool = False, extra: list[str] | None = None, out: str = LIB,
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build(verbose=True, debug=True))

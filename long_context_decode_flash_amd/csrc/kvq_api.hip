@@ -106,6 +106,32 @@ int pool_args_ok(const void* pool, int32_t num_pages, int32_t page_size, int32_t
   return KVQ_OK;
 }
 
+#ifdef KVQ_DEBUG
+// The range-report word of KVQ_DEBUG builds: one per GPU; host code reaches it only through the
+// address hipGetSymbolAddress returns for the current device, looked up once per device.
+static __device__ __align__(256) unsigned debug_word;
+std::mutex g_dbg_mu;
+unsigned* g_dbg_at[64];  // per device (up to 64): the device address of `debug_word`
+#endif
+
+// Device address of the current device's report word (KVQ_DEBUG builds), or nullptr in other
+// builds; KVQ_ERR_HIP if the lookup fails.
+int debug_address(unsigned** at) {
+  *at = nullptr;
+#ifdef KVQ_DEBUG
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return KVQ_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_dbg_mu);
+  if (g_dbg_at[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(debug_word)) != hipSuccess || p == nullptr) return KVQ_ERR_HIP;
+    g_dbg_at[dev] = (unsigned*)p;
+  }
+  *at = g_dbg_at[dev];
+#endif
+  return KVQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -164,7 +190,9 @@ int kvq_append_fmt(int32_t kv_format, void* pool, int32_t num_pages, int32_t pag
   // one 256-thread workgroup per 16 tokens and KV head: fewer than 2^32 work-items
   if ((unsigned long long)((n_tok + 15) / 16) * num_kv_heads * 256 >= (1ULL << 32)) return KVQ_ERR_UNSUPPORTED;
   kvq::AppendArgs a{(uint8_t*)pool, num_pages,    page_size, num_kv_heads, vb,
-                    kv_format == KVQ_FORMAT_FP8, k, v,         slot_mapping, n_tok};
+                    kv_format == KVQ_FORMAT_FP8, k, v,         slot_mapping, n_tok, nullptr};
+  rc = debug_address(&a.dbg);
+  if (rc != KVQ_OK) return rc;
   (void)hipGetLastError();  // start from a clean error state
   return kvq::launch_append(head_dim, a, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
@@ -299,6 +327,8 @@ int decode_impl(int32_t kv_format, const void* pool, int32_t num_pages, int32_t 
   a.k_new = k_new;
   a.v_new = v_new;
   a.n_new = n_new;
+  rc = debug_address(&a.dbg);
+  if (rc != KVQ_OK) return rc;
   (void)hipGetLastError();
   return kvq::launch_decode(head_dim, a, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
@@ -553,6 +583,8 @@ int kvq_prefill_attn(int32_t kv_format, const void* pool, int32_t num_pages, int
                 : nullptr;
   a.out = out;
   a.lse = lse;
+  const int drc = debug_address(&a.dbg);
+  if (drc != KVQ_OK) return drc;
   (void)hipGetLastError();
   return kvq::launch_prefill(head_dim, a, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
@@ -590,4 +622,30 @@ extern "C" int kvq_probe_clock(uint64_t* out, int32_t workgroups, uint32_t spin_
                  hipSuccess
              ? KVQ_OK
              : KVQ_ERR_HIP;
+}
+
+// ---- KVQ_DEBUG builds: the range-report word ----
+
+extern "C" int kvq_debug_errors(uint32_t* errors, int32_t clear, void* stream) {
+#ifdef KVQ_DEBUG
+  if (!errors) return KVQ_ERR_ARG;
+  unsigned* at = nullptr;
+  int rc = debug_address(&at);
+  if (rc != KVQ_OK) return rc;
+  (void)hipGetLastError();
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return KVQ_ERR_HIP;
+  unsigned v = 0;
+  if (hipMemcpy(&v, at, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return KVQ_ERR_HIP;
+  *errors = v;
+  if (clear) {
+    const unsigned zero = 0;
+    if (hipMemcpy(at, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return KVQ_ERR_HIP;
+  }
+  return KVQ_OK;
+#else
+  (void)errors;
+  (void)clear;
+  (void)stream;
+  return KVQ_ERR_UNSUPPORTED;
+#endif
 }

@@ -43,6 +43,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   // slots of the group: lane i < cnt holds token n0 + i's (every wave loads all 16, so each
   // takes the same tile-or-rows decision on its own)
   const long long my_slot = lane < cnt ? (long long)a.slots[n0 + lane] : -1;
+  debug_report(a.dbg, my_slot >= pool_slots, kDbgSlot);  // (negative slots mark padding)
   RowVals<D> rv[kRowsPerWave];
 #pragma unroll
   for (int i = 0; i < kRowsPerWave; ++i) {

@@ -82,6 +82,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // page-table entry of logical page n (a ring reuses its entries cyclically)
   auto entry = [&](int n) { return WIN && ring > 0 ? n % ring : n; };
   int c0 = g_blk0, first = 0, n_my = 0, my_pid = 0;
+  bool my_id_real = false;  // this lane's id is a real entry of the chunk (not the entry-0 filler)
+  int my_tok0 = 0;          // first token of the tile this lane's id is for
   // Lane kk < 32 holds the physical page of tile 0 of this wave's kk-th block of the chunk, lane
   // 32 + kk that of tile 1.  The ids are loaded for the blocks below max_seq_len, so the load
   // does not wait for the sequence length; blocks and tiles past the context are not staged.
@@ -93,7 +95,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int blk = first + kWavesPerGroup * kk;
     int tok0 = blk * kBlock + kTile * (lane >> 5);
     if (tok0 >= a.max_seq_len) tok0 = blk * kBlock;
-    my_pid = pt[kk < n_ids ? entry(tok0 >> lgP) : 0];  // every lane loads (entry 0 always exists)
+    my_id_real = kk < n_ids;
+    my_tok0 = tok0;
+    my_pid = pt[my_id_real ? entry(tok0 >> lgP) : 0];  // every lane loads (entry 0 always exists)
   };
   chunk_pages();  // the first chunk's ids load alongside the sequence length and the queries
 
@@ -149,6 +153,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   auto chunk_count = [&]() {
     const int c1 = min(c0 + CHUNK, g_blk1);
     n_my = first < c1 ? (c1 - first + kWavesPerGroup - 1) / kWavesPerGroup : 0;
+    // (only ids of tiles inside the context are followed; past it an entry may be padding)
+    debug_report(a.dbg, my_id_real && my_tok0 < Lc && (my_pid < 0 || my_pid >= a.num_pages), kDbgPageId);
     my_pid = min(max(my_pid, 0), a.num_pages - 1);  // out-of-range ids are clamped, never followed
   };
   auto chunk_start = [&]() {
@@ -195,7 +201,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
   const bool app_fast = kb_app >= kEarlyPlaces && tb - ta <= kFastTokens;
   auto new_row = [&](int t) { return (((size_t)b * a.n_new + (t - (L - a.n_new))) * a.num_kv_heads + h) * D; };
-  auto slot_block = [&](int pid) { return a.pool_rw + ((size_t)min(max(pid, 0), a.num_pages - 1) * a.num_kv_heads + h) * bb; };
+  auto slot_block = [&](int pid) {
+    debug_report(a.dbg, pid < 0 || pid >= a.num_pages, kDbgPageId);
+    return a.pool_rw + ((size_t)min(max(pid, 0), a.num_pages - 1) * a.num_kv_heads + h) * bb;
+  };
   if (kb_app >= 0 && !app_fast)
     for (int t = ta; t < tb; ++t)
       append_row<D, VB, F8>(slot_block(pt[entry(t >> lgP)]), P, t & (P - 1), a.k_new + new_row(t), a.v_new + new_row(t),

@@ -8,6 +8,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "kvq.h"
+
 namespace kvq {
 
 constexpr int kTile = 16;        // tokens per tile
@@ -39,6 +41,7 @@ struct AppendArgs {
   const float* v;
   const int32_t* slots;
   int n_tok;
+  unsigned* dbg;  // KVQ_DEBUG builds: the word range reports are ORed into (null otherwise)
 };
 
 struct DecodeArgs {
@@ -69,7 +72,24 @@ struct DecodeArgs {
   const float* k_new;
   const float* v_new;
   int n_new;
+  unsigned* dbg;  // KVQ_DEBUG builds: the word range reports are ORed into (null otherwise)
 };
+
+// ---- KVQ_DEBUG builds: device-side range reports ----
+// Bits of the report word (KVQ_DBG_PAGE_ID and KVQ_DBG_SLOT of kvq_debug_errors).  The kernels still clamp an
+// out-of-range page id and skip an out-of-pool slot; a debug build also records that it saw one.
+constexpr unsigned kDbgPageId = KVQ_DBG_PAGE_ID;  // a page-table entry outside [0, num_pages)
+constexpr unsigned kDbgSlot = KVQ_DBG_SLOT;       // an append slot at or past num_pages * page_size
+
+__device__ inline void debug_report(unsigned* dbg, bool bad, unsigned bit) {
+#ifdef KVQ_DEBUG
+  if (bad) atomicOr(dbg, bit);
+#else
+  (void)dbg;
+  (void)bad;
+  (void)bit;
+#endif
+}
 
 hipError_t launch_append(int head_dim, const AppendArgs& a, hipStream_t stream);
 hipError_t launch_decode(int head_dim, const DecodeArgs& a, hipStream_t stream);

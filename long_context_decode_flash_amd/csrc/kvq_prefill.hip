@@ -289,6 +289,7 @@ __global__ __launch_bounds__(kPrefillRowsPerTile / 16 / NB * kWave) void prefill
     int tok0 = blk * kBlock + kTile * w;
     if (tok0 >= Lc) tok0 = blk * kBlock;  // a tile past the end stages tile 0 again, all masked
     const int id = pt[k0 + lane < n_blocks ? (tok0 >> lgP) : 0];  // entry 0 always exists
+    debug_report(a.dbg, k0 + lane < n_blocks && (id < 0 || id >= a.num_pages), kDbgPageId);
     my_pid = min(max(id, 0), a.num_pages - 1);  // out-of-range ids are clamped, never followed
   };
   auto issue = [&](int k) {

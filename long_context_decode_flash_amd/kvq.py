@@ -102,6 +102,8 @@ def lib():
         L.kvq_probe_stream_read.restype = ctypes.c_int
         L.kvq_probe_clock.argtypes = [P, I, ctypes.c_uint32, ctypes.POINTER(ctypes.c_int32), P]
         L.kvq_probe_clock.restype = ctypes.c_int
+        L.kvq_debug_errors.argtypes = [ctypes.POINTER(ctypes.c_uint32), I, P]
+        L.kvq_debug_errors.restype = ctypes.c_int
         _lib = L
         return L
 
@@ -476,6 +478,21 @@ def prepare_stream_probe(buf: torch.Tensor, mode: int, workgroups: int, sink: to
         if rc != KVQ_OK:
             raise KVQError(rc, "kvq_probe_stream_read")
     return call
+
+
+KVQ_DBG_PAGE_ID = 1
+KVQ_DBG_SLOT = 2
+
+
+def debug_errors(clear: bool = True, stream=None) -> int:
+    """The range-report word of the KVQ_DEBUG build (KVQ_DBG_PAGE_ID | KVQ_DBG_SLOT bits), after
+    waiting for ``stream``; cleared when ``clear``.  Raises KVQError(KVQ_ERR_UNSUPPORTED) when
+    the loaded library is not a KVQ_DEBUG build."""
+    v = ctypes.c_uint32(0)
+    rc = lib().kvq_debug_errors(ctypes.byref(v), 1 if clear else 0, _stream_ptr(stream))
+    if rc != KVQ_OK:
+        raise KVQError(rc, "kvq_debug_errors")
+    return v.value
 
 
 def clock_counter_khz() -> int:

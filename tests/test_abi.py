@@ -401,3 +401,20 @@ def test_probe_validation(lib):
     assert g(out, 1, 0, None, None) == E.KVQ_ERR_ARG
     assert g(out, 1, 10000001, None, None) == E.KVQ_ERR_ARG
     assert g(None, 0, 0, None, None) == E.KVQ_ERR_ARG  # the rate query needs somewhere to write
+
+
+def test_debug_errors_entry(lib):
+    """kvq_debug_errors is a KVQ_DEBUG-build feature: the normal build refuses it; the debug
+    build exports every declared symbol and refuses a NULL output before any HIP call."""
+    E = kvq
+    v = ctypes.c_uint32(0)
+    assert lib.kvq_debug_errors(ctypes.byref(v), 1, None) == E.KVQ_ERR_UNSUPPORTED
+    if not os.path.exists(B.DEBUG_LIB):
+        B.build(debug=True)
+    out = subprocess.run(["nm", "-D", "--defined-only", B.DEBUG_LIB], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (kvq_\w+)", out))
+    assert not [n for n in declared_functions() if n not in exported]
+    dbg = ctypes.CDLL(B.DEBUG_LIB)
+    dbg.kvq_debug_errors.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    assert dbg.kvq_debug_errors(None, 1, None) == E.KVQ_ERR_ARG
