@@ -597,3 +597,43 @@ def test_decode_step_full_size_headline():
     torch.cuda.synchronize()
     assert torch.equal(a.pool, b.pool)
     assert torch.equal(out_a, out_b) and torch.equal(lse_a, lse_b)
+
+
+def test_run_to_run_bit_identical():
+    """The same call twice gives the same bytes: the decode step (append + attention, several
+    splits), the chunked prefill and the append, with the workspace dirtied in between.  No
+    result depends on which workgroup finishes first: splits merge in a fixed order and no
+    kernel accumulates through atomics."""
+    import torch
+    H.say("[run to run]")
+    kvq = H.kvq()
+    inp = W.custom(n_seq=2, seq_lens=(3000, 1300), num_kv_heads=2, n_q_heads=12, head_dim=256,
+                   page_size=64, n_rows=4, seed=515)
+    wl = inp.wl
+    q = H.to_dev(inp.q_bits).view(torch.float16)
+    pt, sl = H.to_dev(inp.page_table), H.to_dev(inp.seq_lens)
+    n_new = 4
+    k_new = H.to_dev(np.ascontiguousarray(np.stack([inp.k[b, int(L) - n_new:int(L)] for b, L in
+                                                    enumerate(inp.seq_lens)])))
+    v_new = H.to_dev(np.ascontiguousarray(np.stack([inp.v[b, int(L) - n_new:int(L)] for b, L in
+                                                    enumerate(inp.seq_lens)])))
+    results = []
+    for rep in range(2):
+        cache = H.gpu_cache(inp)
+        k, v, s = inp.all_tokens()
+        keep = np.ones(len(s), bool)  # the step's tokens are appended by the step itself
+        off = 0
+        for b, L in enumerate(inp.seq_lens):
+            keep[off + int(L) - n_new: off + int(L)] = False
+            off += int(L)
+        H.gpu_append(cache, k[keep], v[keep], s[keep])
+        ws = torch.full((kvq.decode_workspace_bytes(wl.n_seq, wl.n_rows, wl.n_q_heads,
+                                                    wl.num_kv_heads, wl.head_dim, 3000, 5),),
+                        37 + rep, dtype=torch.uint8, device="cuda")
+        out, lse = kvq.decode_step(cache, k_new, v_new, q, pt, sl, 3000, workspace=ws, num_splits=5)
+        pout, plse = kvq.prefill_attn(cache, q, pt, sl, 3000)
+        torch.cuda.synchronize()
+        results.append([cache.pool.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy(),
+                        pout.cpu().numpy(), plse.cpu().numpy()])
+    for a, b in zip(*results):
+        assert np.array_equal(a, b)
