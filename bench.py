@@ -649,7 +649,7 @@ def main(argv=None):
     msl = int(wl.seq_len)
     win = args.window
     splits = kvq.decode_num_splits(wl.n_seq, wl.num_kv_heads, msl, args.splits, n_rows=wl.n_rows,
-                                   window=win)
+                                   window=win, kv_format=fmt)
     ws = torch.zeros(kvq.decode_workspace_bytes(wl.n_seq, wl.n_rows, wl.n_q_heads,
                                                 wl.num_kv_heads, D, msl, args.splits, window=win),
                      dtype=torch.uint8, device=dev)

@@ -120,7 +120,8 @@ size_t kvq_block_bytes(int32_t page_size, int32_t head_dim);
  *                    mantissa; the sign bit is the quotient's (a negative value that rounds to
  *                    zero is 0x80).  s == 0 gives code 0 for every element.  Dequantized:
  *                    value(code) * s.  The byte layout and block_bytes are those of K8/V8.
- * kvq_decode_num_splits and kvq_decode_workspace_bytes do not depend on the format. */
+ * kvq_decode_workspace_bytes does not depend on the format (it covers the plan of every format);
+ * the automatic split count does (kvq_decode_num_splits_fmt). */
 #define KVQ_FORMAT_K8V4 0
 #define KVQ_FORMAT_K8V8 1
 #define KVQ_FORMAT_FP8 2
@@ -219,12 +220,14 @@ int kvq_decode_step(void* pool, int32_t num_pages, int32_t page_size, int32_t nu
                     int32_t max_seq_len, float softmax_scale, int32_t num_splits, float* out,
                     float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Number of context pieces kvq_decode_attn uses per (sequence, KV head) for these shapes
- * (num_splits_request as in kvq_decode_attn), or a negative KVQ_ERR_* code.  Host only. */
+/* Number of context pieces kvq_decode_attn uses per (sequence, KV head) for these shapes in the
+ * K8/V4 format (num_splits_request as in kvq_decode_attn), or a negative KVQ_ERR_* code.
+ * Host only.  kvq_decode_num_splits_fmt gives the count for any format. */
 int32_t kvq_decode_num_splits(int32_t n_seq, int32_t num_kv_heads, int32_t max_seq_len,
                               int32_t num_splits_request);
 
-/* Workspace bytes kvq_decode_attn needs for these shapes (0 on invalid shapes).  Host only. */
+/* Workspace bytes kvq_decode_attn needs for these shapes, in any format (0 on invalid shapes).
+ * Host only. */
 size_t kvq_decode_workspace_bytes(int32_t n_seq, int32_t n_rows, int32_t n_q_heads,
                                   int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
                                   int32_t num_splits_request);
@@ -318,6 +321,16 @@ int32_t kvq_decode_num_splits_win(int32_t n_seq, int32_t num_kv_heads, int32_t m
 size_t kvq_decode_workspace_bytes_win(int32_t n_seq, int32_t n_rows, int32_t n_q_heads,
                                       int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
                                       int32_t window, int32_t num_splits_request);
+
+/* The number of context pieces per (sequence, KV head) every decode call of this format uses
+ * for these shapes (window 0 = none; num_splits_request as in kvq_decode_attn), or a negative
+ * KVQ_ERR_* code (KVQ_ERR_UNSUPPORTED for an unknown format).  With a request of 0 the plan
+ * depends on the format: the 4-bit-V format's block step is bound by the issue of its own wave
+ * and gets the plan whose busiest wave has the fewest blocks; the 8-bit-V formats, 32% more
+ * bytes per token, are bandwidth-bound and may use fewer splits.  Host only. */
+int32_t kvq_decode_num_splits_fmt(int32_t kv_format, int32_t n_seq, int32_t num_kv_heads,
+                                  int32_t max_seq_len, int32_t n_rows, int32_t window,
+                                  int32_t num_splits_request);
 
 /* ---- kvq_prefill_attn: chunked-prefill attention -------------------------------------------
  * The forum post's engine prefills prompts in chunks of 1,024 tokens (一、部署, launch-flag table,

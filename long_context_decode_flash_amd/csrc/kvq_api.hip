@@ -25,8 +25,8 @@ int vbits_of(int32_t kv_format) {
 constexpr long long kTargetGroups = 256;
 // A split covers at least one 32-token block per wave of its workgroup.
 constexpr long long kMinBlocksPerSplit = kvq::kWavesPerGroup;
-// Workgroups that keep HBM saturated: with at least this many streaming (90% of the CUs), the
-// decode is bandwidth-bound and fewer workgroups each stream proportionally faster.
+// Workgroups that keep HBM saturated (90% of the CUs): with at least this many streaming, a
+// bandwidth-bound decode gains nothing from more.
 constexpr long long kSaturatingGroups = 230;
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
@@ -36,7 +36,11 @@ struct Plan {
   int blocks_per_split;
 };
 
-int plan_splits(int n_seq, int num_kv_heads, int max_seq_len, int request, Plan* plan) {
+// wave_bound: the format's block step is bound by the issue of its own wave (4-bit V: the V
+// widening and the split of P * s_v); otherwise by HBM bandwidth (8-bit V: 32% more bytes per
+// token for about the same instructions).
+int plan_splits(int n_seq, int num_kv_heads, int max_seq_len, int request, Plan* plan,
+                bool wave_bound) {
   if (n_seq <= 0 || num_kv_heads <= 0 || max_seq_len <= 0 || request < 0) return KVQ_ERR_ARG;
   const long long nblk = ceil_div(max_seq_len, kvq::kBlock);
   const long long units = (long long)n_seq * num_kv_heads;
@@ -44,21 +48,27 @@ int plan_splits(int n_seq, int num_kv_heads, int max_seq_len, int request, Plan*
   if (request > 0) {
     s = request;
   } else {
-    // At most one workgroup per CU.  A split's blocks go to its 4 waves in turn, so a count
-    // that leaves some waves one block more than others idles part of each CU's bandwidth at
-    // the end; the time of a plan is modelled as (blocks of the busiest wave) x (workgroups,
-    // or the saturating count if fewer), and the fastest plan is taken, the most splits on ties.
+    // At most one workgroup per CU, about (a grid past the CU count runs in rounds).  A split's
+    // blocks go to its 4 waves in turn.  Wave-bound: one wave per SIMD cannot hide its own block
+    // step, so the time follows the blocks of the busiest wave: (blocks of the busiest wave) x
+    // (rounds of workgroups), the fewest splits on ties (less partial traffic and merge work).
+    // Bandwidth-bound: a wave with one block more than the others idles part of its CU's
+    // bandwidth at the end, and fewer workgroups than the saturating count each stream
+    // proportionally faster: (blocks of the busiest wave) x max(workgroups, saturating count),
+    // the most splits on ties.
     long long s_max = ceil_div(kTargetGroups, units);
     const long long cap = ceil_div(nblk, kMinBlocksPerSplit);
     s_max = s_max < cap ? s_max : cap;
     s = 1;
     long long best = -1;
-    for (long long c = s_max; c >= 1; --c) {
+    for (long long c = 1; c <= s_max; ++c) {
       const long long bps = ceil_div(nblk, c);
       const long long used = ceil_div(nblk, bps);  // splits that start inside the context
       const long long groups = units * used;
-      const long long t = ceil_div(bps, kvq::kWavesPerGroup) * (groups > kSaturatingGroups ? groups : kSaturatingGroups);
-      if (best < 0 || t < best) {
+      const long long per_wave = ceil_div(bps, kvq::kWavesPerGroup);
+      const long long t = wave_bound ? per_wave * ceil_div(groups, kTargetGroups)
+                                     : per_wave * (groups > kSaturatingGroups ? groups : kSaturatingGroups);
+      if (best < 0 || (wave_bound ? t < best : t <= best)) {
         best = t;
         s = c;
       }
@@ -162,7 +172,7 @@ const char* kvq_strerror(int code) {
 int32_t kvq_decode_num_splits(int32_t n_seq, int32_t num_kv_heads, int32_t max_seq_len,
                               int32_t num_splits_request) {
   Plan p;
-  const int rc = plan_splits(n_seq, num_kv_heads, max_seq_len, num_splits_request, &p);
+  const int rc = plan_splits(n_seq, num_kv_heads, max_seq_len, num_splits_request, &p, true);
   return rc == KVQ_OK ? p.splits : rc;
 }
 
@@ -172,10 +182,14 @@ size_t kvq_decode_workspace_bytes(int32_t n_seq, int32_t n_rows, int32_t n_q_hea
   if (n_rows <= 0 || n_q_heads <= 0 || num_kv_heads <= 0 || n_q_heads % num_kv_heads != 0 ||
       !head_dim_ok(head_dim))
     return 0;
-  Plan p;
-  if (plan_splits(n_seq, num_kv_heads, max_seq_len, num_splits_request, &p) != KVQ_OK) return 0;
+  // the larger of the two formats' plans (the workspace grows with the splits)
+  Plan p, p8;
+  if (plan_splits(n_seq, num_kv_heads, max_seq_len, num_splits_request, &p, true) != KVQ_OK ||
+      plan_splits(n_seq, num_kv_heads, max_seq_len, num_splits_request, &p8, false) != KVQ_OK)
+    return 0;
   const int rows = (n_q_heads / num_kv_heads) * n_rows;
-  return workspace_for((long long)n_seq * num_kv_heads, p.splits, rows, head_dim);
+  const int splits = p.splits > p8.splits ? p.splits : p8.splits;
+  return workspace_for((long long)n_seq * num_kv_heads, splits, rows, head_dim);
 }
 
 int kvq_append_fmt(int32_t kv_format, void* pool, int32_t num_pages, int32_t page_size,
@@ -278,7 +292,7 @@ int decode_impl(int32_t kv_format, const void* pool, int32_t num_pages, int32_t 
   if (((uintptr_t)q & 15) != 0 || ((uintptr_t)out & 15) != 0) return KVQ_ERR_ARG;
   Plan plan;
   rc = plan_splits(n_seq, num_kv_heads, (int)span_tokens(max_seq_len, n_rows, window), num_splits,
-                   &plan);
+                   &plan, vb == 4);
   if (rc != KVQ_OK) return rc;
   const int rows = group * n_rows;
   const long long units = (long long)n_seq * num_kv_heads;
@@ -405,10 +419,19 @@ int kvq_decode_step_noalloc(int32_t kv_format, void* pool, int32_t num_pages, in
 
 int32_t kvq_decode_num_splits_win(int32_t n_seq, int32_t num_kv_heads, int32_t max_seq_len,
                                   int32_t n_rows, int32_t window, int32_t num_splits_request) {
+  return kvq_decode_num_splits_fmt(KVQ_FORMAT_K8V4, n_seq, num_kv_heads, max_seq_len, n_rows, window,
+                                   num_splits_request);
+}
+
+int32_t kvq_decode_num_splits_fmt(int32_t kv_format, int32_t n_seq, int32_t num_kv_heads,
+                                  int32_t max_seq_len, int32_t n_rows, int32_t window,
+                                  int32_t num_splits_request) {
+  const int vb = vbits_of(kv_format);
+  if (vb == 0) return KVQ_ERR_UNSUPPORTED;
   if (n_rows < 1 || window < 0) return KVQ_ERR_ARG;
   Plan p;
   const int rc = plan_splits(n_seq, num_kv_heads, (int)span_tokens(max_seq_len, n_rows, window),
-                             num_splits_request, &p);
+                             num_splits_request, &p, vb == 4);
   return rc == KVQ_OK ? p.splits : rc;
 }
 

@@ -89,6 +89,8 @@ def lib():
         L.kvq_decode_step_noalloc.restype = ctypes.c_int
         L.kvq_decode_num_splits_win.argtypes = [I, I, I, I, I, I]
         L.kvq_decode_num_splits_win.restype = I
+        L.kvq_decode_num_splits_fmt.argtypes = [I, I, I, I, I, I, I]
+        L.kvq_decode_num_splits_fmt.restype = I
         L.kvq_decode_workspace_bytes_win.argtypes = [I, I, I, I, I, I, I, I]
         L.kvq_decode_workspace_bytes_win.restype = ctypes.c_size_t
         # chunked prefill: the decode_attn_fmt arguments with chunk in place of n_rows
@@ -122,14 +124,12 @@ def pool_bytes(num_pages: int, page_size: int, num_kv_heads: int, head_dim: int,
 
 
 def decode_num_splits(n_seq: int, num_kv_heads: int, max_seq_len: int,
-                      num_splits: int = 0, *, n_rows: int = 1, window: int = 0) -> int:
-    if window:
-        r = int(lib().kvq_decode_num_splits_win(n_seq, num_kv_heads, max_seq_len, n_rows, window,
-                                                 num_splits))
-    else:
-        r = int(lib().kvq_decode_num_splits(n_seq, num_kv_heads, max_seq_len, num_splits))
+                      num_splits: int = 0, *, n_rows: int = 1, window: int = 0,
+                      kv_format: int = KVQ_FORMAT_K8V4) -> int:
+    r = int(lib().kvq_decode_num_splits_fmt(kv_format, n_seq, num_kv_heads, max_seq_len, n_rows,
+                                             window, num_splits))
     if r < 0:
-        raise KVQError(r, "kvq_decode_num_splits")
+        raise KVQError(r, "kvq_decode_num_splits_fmt")
     return r
 
 

@@ -75,6 +75,33 @@ def test_split_plan(lib):
         kvq.decode_num_splits(1, 4, 100, -1)
 
 
+def test_split_plan_by_format(lib):
+    # the 4-bit-V format takes the plan whose busiest wave has the fewest 32-token blocks (32
+    # splits: 90 blocks, 23 for the busiest of 4 waves); the 8-bit-V formats, bandwidth-bound,
+    # keep 240 workgroups with 24 blocks per wave
+    assert kvq.decode_num_splits(2, 4, 92160, kv_format=0) == 32
+    assert kvq.decode_num_splits(2, 4, 92160) == 32
+    for fmt in (1, 2):
+        assert kvq.decode_num_splits(2, 4, 92160, kv_format=fmt) == 30
+    # the workspace query covers every format's plan
+    for fmt in (0, 1, 2):
+        s = kvq.decode_num_splits(2, 4, 92160, kv_format=fmt)
+        assert kvq.decode_workspace_bytes(2, 1, 24, 4, 256, 92160) >= 2 * 4 * s * 6 * (256 + 2) * 4
+    # shapes where both models agree
+    for fmt in (0, 1, 2):
+        assert kvq.decode_num_splits(1, 4, 262144, n_rows=4, kv_format=fmt) == 64
+        assert kvq.decode_num_splits(1, 4, 65536, kv_format=fmt) == 64
+    # a windowed plan is that of the window's span (a window may start inside a block: 31 more
+    # tokens), in each format
+    for fmt in (0, 1, 2):
+        assert kvq.decode_num_splits(2, 4, 92160, n_rows=1, window=65536, kv_format=fmt) == \
+            kvq.decode_num_splits(2, 4, 65536 + 31, kv_format=fmt)
+    # a request is the same in every format; an unknown format is refused
+    assert kvq.decode_num_splits(2, 4, 92160, 17, kv_format=1) == 17
+    with pytest.raises(kvq.KVQError):
+        kvq.decode_num_splits(2, 4, 92160, kv_format=7)
+
+
 def test_workspace_size(lib):
     s = kvq.decode_num_splits(2, 4, 92160)
     assert kvq.decode_workspace_bytes(2, 1, 24, 4, 256, 92160) == 2 * 4 * s * 6 * (256 + 2) * 4
