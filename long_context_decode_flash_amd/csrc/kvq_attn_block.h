@@ -424,16 +424,14 @@ __device__ __attribute__((always_inline)) inline void block_softmax_scores(
     for (int e = 0; e < 4; ++e) ks[tau][e] = h_at(ks_words[tau], e);
 
   // ---- logits and the online softmax (log2 units) ----
-  bool rescale = false;
-  float alpha[NB];
+  float z[NB][2][4], lm[NB];
+  bool over = false;  // some row needs a larger exponent offset than it has
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    float z[2][4];
-    float bm = kNegInf;
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) z[tau][e] = sc[tau][nb][e] * (ks[tau][e] * cz[nb]);
+      for (int e = 0; e < 4; ++e) z[nb][tau][e] = sc[tau][nb][e] * (ks[tau][e] * cz[nb]);
     if (masked) {  // wave-uniform: only the blocks at the end of a context
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau)
@@ -441,46 +439,59 @@ __device__ __attribute__((always_inline)) inline void block_softmax_scores(
         for (int e = 0; e < 4; ++e) {
           const int t = blk * kBlock + kTile * tau + 4 * g + e;
           const bool seen = WIN ? (t <= last_tok[nb] && t >= first_tok[nb]) : t <= last_tok[nb];
-          z[tau][e] = seen ? z[tau][e] : kNegInf;
+          z[nb][tau][e] = seen ? z[nb][tau][e] : kNegInf;
         }
     }
+    lm[nb] = kNegInf;
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) bm = fmaxf(bm, z[tau][e]);
-    bm = max_over_rows(bm);
-    // p * v_scale < 2^(bm - base + e5 - 14) must stay below 2^15
-    const float need = bm + (e5 - 29.0f);
-    float b_new = base[nb];
-    alpha[nb] = 1.0f;
-    if (need > b_new) {
-      b_new = __builtin_ceilf(need) + 2.0f;  // two powers of two of headroom for later blocks
-      if (base[nb] != kNegInf) {
-        alpha[nb] = __builtin_ldexpf(1.0f, (int)(base[nb] - b_new));
-        rescale = true;
+      for (int e = 0; e < 4; ++e) lm[nb] = fmaxf(lm[nb], z[nb][tau][e]);
+    // p * v_scale < 2^(bm - base + e5 - 14) must stay below 2^15, bm the row's largest logit.
+    // Rounding is monotone, so a row's fl(bm + (e5 - 29)) exceeds its base exactly when one of
+    // its four lanes' fl(lm + (e5 - 29)) does: the lanes test their own maxima, and the row
+    // maximum (a cross-lane reduction) is formed only on the rare blocks that move a base.
+    over |= lm[nb] + (e5 - 29.0f) > base[nb];
+  }
+  float alpha[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) alpha[nb] = 1.0f;
+  if (__builtin_expect(__any(over), 0)) {  // a wave's first block, or a larger logit or V scale
+    bool rescale = false;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const float need = max_over_rows(lm[nb]) + (e5 - 29.0f);
+      if (need > base[nb]) {
+        const float b_new = __builtin_ceilf(need) + 2.0f;  // two powers of two of headroom for later blocks
+        if (base[nb] != kNegInf) {
+          alpha[nb] = __builtin_ldexpf(1.0f, (int)(base[nb] - b_new));
+          rescale = true;
+        }
+        base[nb] = b_new;
       }
-      base[nb] = b_new;
     }
-    const float b_use = (b_new == kNegInf) ? 0.0f : b_new;
+    if (__any(rescale)) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[nb][db][e] *= alpha[nb];
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const float b_use = (base[nb] == kNegInf) ? 0.0f : base[nb];
     float lsum = 0.0f;
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        pexp[nb][tau][e] = __builtin_amdgcn_exp2f(z[tau][e] - b_use);
+        pexp[nb][tau][e] = __builtin_amdgcn_exp2f(z[nb][tau][e] - b_use);
         lsum += pexp[nb][tau][e];
       }
     l_run[nb] = l_run[nb] * alpha[nb] + lsum;
   }
-  if (__builtin_expect(__any(rescale), 0)) {  // rare: a larger logit or V scale than this wave has seen
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[nb][db][e] *= alpha[nb];
-  }
-
 }
 
 // The first half of the block step: Q K^T and the online softmax, leaving the block's
