@@ -20,6 +20,9 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # matrix-core accumulators in VGPRs: the decode loop's rare rescale then needs no AGPR copies
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # the first 16 kernel-argument dwords arrive in SGPRs with the wave (the decode and merge
+    # kernels lead with the scalars of their first memory accesses)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-result",
 ]
 

@@ -650,8 +650,23 @@ __device__ __attribute__((always_inline)) inline void prepare_queries(
 // previous launch on the stream.  On the 184K-token step (32 splits) one lane per item took
 // about 1 us longer per step than 4 lanes, and 8 and 16 lanes measured 0.3-0.6 us below 4.
 
+// The partials' addresses and shape come as separate leading kernel arguments (preloaded into
+// SGPRs, like the decode's), so the partial loads issue without a kernel-argument load first.
 template <int D>
-__global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) void merge_kernel(const float* ws_acc, const float2* ws_ml, float* out,
+                                                   float* lse, int splits, int rows, int num_kv_heads,
+                                                   int group, int n_rows, int n_q_heads, DecodeArgs args) {
+  DecodeArgs a = args;
+  a.ws_acc = (float*)ws_acc;
+  a.ws_ml = (float2*)ws_ml;
+  a.out = out;
+  a.lse = lse;
+  a.splits = splits;
+  a.rows = rows;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.n_rows = n_rows;
+  a.n_q_heads = n_q_heads;
   constexpr int NQ = D / 4;
   constexpr int U = 32 / kMergeLanes;  // splits per lane per batch
   const int S = a.splits, R = a.rows;
@@ -728,6 +743,12 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a) {
   const size_t o = ((size_t)b * a.n_rows + i) * a.n_q_heads + hq;
   *(floatx4*)(a.out + o * D + 4 * q) = num * (den > 0.0f ? 1.0f / den : 0.0f);
   if (q == 0 && a.lse) a.lse[o] = den > 0.0f ? (M + log2f(den)) * 0.69314718055994530942f : kNegInf;
+}
+
+template <int D>
+void launch_merge(const DecodeArgs& a, unsigned groups, hipStream_t stream) {
+  hipLaunchKernelGGL((merge_kernel<D>), dim3(groups), dim3(kWave), 0, stream, a.ws_acc, a.ws_ml, a.out, a.lse,
+                     a.splits, a.rows, a.num_kv_heads, a.group, a.n_rows, a.n_q_heads, a);
 }
 
 }  // namespace

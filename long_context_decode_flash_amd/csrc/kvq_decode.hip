@@ -34,8 +34,31 @@ namespace {
 // NSTAGE - 1 blocks are in flight while it computes one.  The waves merge through LDS into one
 // partial (the output itself when the context is a single piece).  WIN: a sliding window (the
 // pieces start at the first row's window start; pages may be a ring).
+//
+// The scalars of the first memory accesses (the sequence length, the page ids, the queries)
+// come as separate leading kernel arguments: with kernel-argument preloading the first 14
+// argument dwords (all that gfx950's user SGPRs hold besides the argument pointer) are in SGPRs
+// when the wave starts, so those loads need no kernel-argument load before them.  n_q_heads and
+// rows follow from them; the rest comes from the argument struct.
 template <int D, int NB, int VB, bool WIN, bool F8>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void decode_kernel(const int32_t* page_table, const int32_t* seq_lens,
+                                                      const uint16_t* q, int splits, int num_kv_heads,
+                                                      int max_pages, int blocks_per_split, int log2_page,
+                                                      int max_seq_len, int n_rows, int group, DecodeArgs args) {
+  DecodeArgs a = args;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.q = q;
+  a.splits = splits;
+  a.num_kv_heads = num_kv_heads;
+  a.max_pages = max_pages;
+  a.blocks_per_split = blocks_per_split;
+  a.log2_page = log2_page;
+  a.max_seq_len = max_seq_len;
+  a.n_rows = n_rows;
+  a.group = group;
+  a.n_q_heads = group * num_kv_heads;
+  a.rows = group * n_rows;
   constexpr int DB = D / 16;
   constexpr int ROWS = 16 * NB;
   constexpr int LDS_STRIDE = D + 4;  // floats; padding spreads the 16 rows over banks
@@ -372,10 +395,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
 template <int D, bool WIN, int VB, bool F8>
 void launch_attn_f(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t stream) {
+#define KVQ_DECODE_ARGS                                                                                    \
+  a.page_table, a.seq_lens, a.q, a.splits, a.num_kv_heads, a.max_pages, a.blocks_per_split, a.log2_page, \
+      a.max_seq_len, a.n_rows, a.group, a
   if (a.rows <= 16)
-    hipLaunchKernelGGL((decode_kernel<D, 1, VB, WIN, F8>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<D, 1, VB, WIN, F8>), grid, block, 0, stream, KVQ_DECODE_ARGS);
   else
-    hipLaunchKernelGGL((decode_kernel<D, 2, VB, WIN, F8>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<D, 2, VB, WIN, F8>), grid, block, 0, stream, KVQ_DECODE_ARGS);
+#undef KVQ_DECODE_ARGS
 }
 
 template <int D, bool WIN>
@@ -400,7 +427,7 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   const unsigned per_unit = (unsigned)merge_groups(a.rows, D);  // grid size checked on the host
-  hipLaunchKernelGGL((merge_kernel<D>), dim3(units * per_unit), dim3(kWave), 0, stream, a);
+  launch_merge<D>(a, units * per_unit, stream);
   return hipGetLastError();
 }
 

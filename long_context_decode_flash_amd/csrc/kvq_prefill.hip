@@ -436,7 +436,7 @@ hipError_t launch_prefill_d(const DecodeArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   const unsigned per_unit = (unsigned)merge_groups(a.rows, D);  // grid size checked on the host
-  hipLaunchKernelGGL((merge_kernel<D>), dim3(units * per_unit), dim3(kWave), 0, stream, a);
+  launch_merge<D>(a, units * per_unit, stream);
   return hipGetLastError();
 }
 
