@@ -299,9 +299,10 @@ int kvq_decode_step_win(int32_t kv_format, void* pool, int32_t num_pages, int32_
  * the process ends.  The call allocates nothing and clears nothing (no entry of the array is
  * read before the same launch writes it), and gives bit-identical results to
  * kvq_decode_step_fmt with the same split plan.
- *   - A call whose partials would exceed the array (kvq_decode_workspace_bytes() >
- *     KVQ_NOALLOC_SCRATCH_BYTES) returns KVQ_ERR_SCRATCH and enqueues nothing.  Every automatic
- *     plan of the supported shapes fits (at most about 8.5 MB at 32 rows per KV head, D = 256).
+ *   - A call whose partials would exceed the array (its format's split plan needs more than
+ *     KVQ_NOALLOC_SCRATCH_BYTES; kvq_decode_workspace_bytes() bounds that need for every format)
+ *     returns KVQ_ERR_SCRATCH and enqueues nothing.  Every automatic plan of the supported
+ *     shapes fits (at most about 8.5 MB at 32 rows per KV head, D = 256).
  *   - All calls on one GPU share its array: calls that may overlap in time on one GPU (different
  *     streams without ordering between them) race on it and give undefined results.  Order them
  *     on one stream, or use kvq_decode_step_fmt with a workspace per stream.
