@@ -567,6 +567,84 @@ __device__ __attribute__((always_inline)) inline void block_pv_folded(TileRaw<D,
   }
 }
 
+// The P V step for two row blocks: the V scale goes on the V side, once for both row blocks.
+// A code times its fp16 scale has at most 18 significant bits (an 8-bit integer code; 14 for
+// 4-bit codes, 15 for E4M3), so v = code * s_v splits exactly into fp16 hi = rne(v) (one packed
+// multiply) and lo = v - hi (one packed fma, exact).  P splits once per row into fp16 hi + lo,
+// and each operand pair takes three products (hi*hi, hi*lo, lo*hi; lo*lo is below 2^-22 of the
+// product).  Against folding the scale into P per 32-dim group, this trades 128 of the block's
+// VALU instructions per row block for a third matrix-core product; with two row blocks that is
+// the cheaper side.  p stays below 2^13 under the offsets (the caller passes e5 = 14).
+template <int D, int NB, int VB, bool F8>
+__device__ __attribute__((always_inline)) inline void block_pv_vhat_regs(TileRaw<D, VB> (&raw)[2],
+                                                                         const float (&pexp)[NB][2][4],
+                                                                         floatx4 (&acc)[NB][D / 16]) {
+  constexpr int NG = D / 32;
+  constexpr uint32_t kOne = 0x3C003C00u;  // fp16 1.0 in both halves
+  uint32_t hw[NB][4], lw[NB][4];  // token order of the operand: (tau0: 0,2,1,3), (tau1: 0,2,1,3)
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      mix_hi_lo<0>(pexp[nb][tau][0], kOne, pexp[nb][tau][2], kOne, hw[nb][2 * tau], lw[nb][2 * tau]);
+      mix_hi_lo<0>(pexp[nb][tau][1], kOne, pexp[nb][tau][3], kOne, hw[nb][2 * tau + 1], lw[nb][2 * tau + 1]);
+    }
+  static_assert(NB == 2, "the nop below ties the P words of two row blocks");
+  // two wait states between the inline-asm writes of P and the matrix-core reads (the
+  // compiler's hazard tracking does not see inline-asm results)
+  asm("s_nop 1" : "+v"(hw[0][0]), "+v"(hw[0][1]), "+v"(hw[0][2]), "+v"(hw[0][3]), "+v"(lw[0][0]),
+      "+v"(lw[0][1]), "+v"(lw[0][2]), "+v"(lw[0][3]), "+v"(hw[1][0]), "+v"(hw[1][1]), "+v"(hw[1][2]),
+      "+v"(hw[1][3]), "+v"(lw[1][0]), "+v"(lw[1][1]), "+v"(lw[1][2]), "+v"(lw[1][3]));
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    uint32_t l02[2], l13[2], h02[2], h13[2], s02[2], s13[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      if constexpr (F8)
+        f8x8_to_h2x4(raw[tau].v[2 * j], raw[tau].v[2 * j + 1], l02[tau], l13[tau], h02[tau], h13[tau]);
+      else if constexpr (VB == 8)
+        i8x8_to_h2x4(raw[tau].v[2 * j], raw[tau].v[2 * j + 1], l02[tau], l13[tau], h02[tau], h13[tau]);
+      else
+        i4x8_to_h2x4(raw[tau].v[j], l02[tau], l13[tau], h02[tau], h13[tau]);
+      // the scales of tokens (0, 2) and (1, 3) for group j: fp16 half (j & 1) of word (e NG + j) / 2
+      const uint32_t* vs = raw[tau].vs;
+      constexpr uint32_t kSel[2] = {0x05040100u, 0x07060302u};
+      s02[tau] = __builtin_amdgcn_perm(vs[(2 * NG + j) / 2], vs[(0 * NG + j) / 2], kSel[j & 1]);
+      s13[tau] = __builtin_amdgcn_perm(vs[(3 * NG + j) / 2], vs[(1 * NG + j) / 2], kSel[j & 1]);
+    }
+    uint32_t vh[2][2][4];  // [dim half][hi, lo][word]
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      const uint32_t c[2][2] = {{l02[tau], l13[tau]}, {h02[tau], h13[tau]}};
+      const uint32_t sc[2] = {s02[tau], s13[tau]};
+#pragma unroll
+      for (int dh = 0; dh < 2; ++dh)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const half2v cv = as_h2(c[dh][k]), sv = as_h2(sc[k]);
+          const half2v hi = cv * sv;
+          const half2v lo = __builtin_elementwise_fma(cv, sv, -hi);
+          vh[dh][0][2 * tau + k] = as_u32(hi);
+          vh[dh][1][2 * tau + k] = as_u32(lo);
+        }
+    }
+#pragma unroll
+    for (int dh = 0; dh < 2; ++dh) {
+      const half8 vhi = __builtin_bit_cast(half8, u32x4{vh[dh][0][0], vh[dh][0][1], vh[dh][0][2], vh[dh][0][3]});
+      const half8 vlo = __builtin_bit_cast(half8, u32x4{vh[dh][1][0], vh[dh][1][1], vh[dh][1][2], vh[dh][1][3]});
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const half8 phi = __builtin_bit_cast(half8, u32x4{hw[nb][0], hw[nb][1], hw[nb][2], hw[nb][3]});
+        const half8 plo = __builtin_bit_cast(half8, u32x4{lw[nb][0], lw[nb][1], lw[nb][2], lw[nb][3]});
+        floatx4& c = acc[nb][2 * j + dh];
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(vhi, phi, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(vhi, plo, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(vlo, phi, c, 0, 0, 0);
+      }
+    }
+  }
+}
+
 template <int D, int NB, int VB, bool WIN, bool F8>
 __device__ __attribute__((always_inline)) inline void process_block(
     TileRaw<D, VB> (&raw)[2], int blk, bool masked, float e5, const i32x4 (&qd)[NB][3][D / 64],
@@ -576,7 +654,10 @@ __device__ __attribute__((always_inline)) inline void process_block(
   float pexp[NB][2][4];
   block_softmax<D, NB, VB, WIN, F8>(raw, blk, masked, e5, qd, qw, cz, first_tok, last_tok, g, acc, base, l_run,
                                     pexp);
-  block_pv_folded<D, NB, VB, F8>(raw, pexp, acc);
+  if constexpr (NB == 2)
+    block_pv_vhat_regs<D, NB, VB, F8>(raw, pexp, acc);
+  else
+    block_pv_folded<D, NB, VB, F8>(raw, pexp, acc);
 }
 
 // The query rows' B operands of Q K^T, from the raw fp16 words qw (lane: query row 16*nb + m16

@@ -325,9 +325,10 @@ __global__ __launch_bounds__(256) void decode_kernel(const int32_t* page_table, 
         }
       }
       // binary exponent of the block's largest V scale (positive fp16: bit order is value order);
-      // every scale is below 2^(e5 - 14)
-      float e5;
-      {
+      // every scale is below 2^(e5 - 14).  Two row blocks scale V on the V side and keep p below
+      // 2^13 instead (block_pv_vhat_regs).
+      float e5 = 14.0f;
+      if constexpr (NB == 1) {
         const uint32_t* vsw = (const uint32_t*)(src + Stage<D, VB>::kVs) + (lane & (D / 4 - 1));
         const uint32_t m = wave_max_u16x2(__builtin_bit_cast(uint32_t, __builtin_elementwise_max(
             __builtin_bit_cast(u16x2, vsw[0]), __builtin_bit_cast(u16x2, vsw[Stage<D, VB>::kTileBytes / 4]))));
