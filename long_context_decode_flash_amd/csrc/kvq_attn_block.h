@@ -71,26 +71,17 @@ __device__ inline void f8x8_to_h2x4(uint32_t lo_w, uint32_t hi_w, uint32_t& lo02
   hi13 = e4m3x2_to_h2<true>(h);
 }
 
-// p0 * s0 and p1 * s1 (p fp32, s an fp16 half of sw0 / sw1 selected by SH) as fp16 hi + lo pairs:
+// p0 * s0 and p1 * s1 (p fp32, s the low fp16 half of sw0 / sw1) as fp16 hi + lo pairs:
 // hi = rne(p * s) and lo = rne(p * s - hi) straight from the exact products (v_fma_mix*), so the
 // two halves always belong together and hi + lo = p * s to about 2^-22.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-template <int SH>
-__device__ inline void mix_hi_lo(float p0, uint32_t sw0, float p1, uint32_t sw1, uint32_t& hi,
-                                 uint32_t& lo) {
+__device__ inline void mix_hi_lo(float p0, uint32_t sw0, float p1, uint32_t sw1, uint32_t& hi, uint32_t& lo) {
   uint32_t h, l;  // the lo-half writes declare the whole register as output; the hi-half writes keep it
-  if constexpr (SH == 0) {
-    asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel:[0,0,0] op_sel_hi:[0,1,0]" : "=v"(h) : "v"(p0), "v"(sw0));
-    asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[0,0,0] op_sel_hi:[0,1,0]" : "+v"(h) : "v"(p1), "v"(sw1));
-    asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel:[0,0,0] op_sel_hi:[0,1,1]" : "=&v"(l) : "v"(p0), "v"(sw0), "v"(h));
-    asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,1,1]" : "+v"(l) : "v"(p1), "v"(sw1), "v"(h));
-  } else {
-    asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(h) : "v"(p0), "v"(sw0));
-    asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "+v"(h) : "v"(p1), "v"(sw1));
-    asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel:[0,1,0] op_sel_hi:[0,1,1]" : "=&v"(l) : "v"(p0), "v"(sw0), "v"(h));
-    asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,1,1] op_sel_hi:[0,1,1]" : "+v"(l) : "v"(p1), "v"(sw1), "v"(h));
-  }
+  asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel:[0,0,0] op_sel_hi:[0,1,0]" : "=v"(h) : "v"(p0), "v"(sw0));
+  asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[0,0,0] op_sel_hi:[0,1,0]" : "+v"(h) : "v"(p1), "v"(sw1));
+  asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel:[0,0,0] op_sel_hi:[0,1,1]" : "=&v"(l) : "v"(p0), "v"(sw0), "v"(h));
+  asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,1,1]" : "+v"(l) : "v"(p1), "v"(sw1), "v"(h));
   hi = h;
   lo = l;
 }
@@ -508,73 +499,17 @@ __device__ __attribute__((always_inline)) inline void block_softmax(
   block_softmax_scores<D, NB, WIN>(sc, ksw, blk, masked, e5, cz, first_tok, last_tok, g, acc, base, l_run, pexp);
 }
 
-// The second half: O^T += V^T P^T, one 32-dim scale group at a time, with the V scale folded
-// into P.
-template <int D, int NB, int VB, bool F8>
-__device__ __attribute__((always_inline)) inline void block_pv_folded(TileRaw<D, VB> (&raw)[2],
-                                                                      const float (&pexp)[NB][2][4],
-                                                                      floatx4 (&acc)[NB][D / 16]) {
-  constexpr int NG = D / 32;
-#pragma unroll
-  for (int j = 0; j < NG; ++j) {
-    uint32_t l02[2], l13[2], h02[2], h13[2];
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      if constexpr (F8)
-        f8x8_to_h2x4(raw[tau].v[2 * j], raw[tau].v[2 * j + 1], l02[tau], l13[tau], h02[tau], h13[tau]);
-      else if constexpr (VB == 8)
-        i8x8_to_h2x4(raw[tau].v[2 * j], raw[tau].v[2 * j + 1], l02[tau], l13[tau], h02[tau], h13[tau]);
-      else
-        i4x8_to_h2x4(raw[tau].v[j], l02[tau], l13[tau], h02[tau], h13[tau]);
-    }
-    const half8 vlo = __builtin_bit_cast(half8, u32x4{l02[0], l13[0], l02[1], l13[1]});
-    const half8 vhi = __builtin_bit_cast(half8, u32x4{h02[0], h13[0], h02[1], h13[1]});
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      // token order of the operand: (tau0: 0,2,1,3), (tau1: 0,2,1,3); the scale of token e, group
-      // j is fp16 half (j & 1) of word (e * NG + j) / 2
-      uint32_t hw[4], lw[4];
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau) {
-        const uint32_t* vs = raw[tau].vs;
-        if (j & 1) {  // resolved at compile time once the group loop is unrolled
-          mix_hi_lo<1>(pexp[nb][tau][0], vs[(0 * NG + j) / 2], pexp[nb][tau][2], vs[(2 * NG + j) / 2],
-                       hw[2 * tau], lw[2 * tau]);
-          mix_hi_lo<1>(pexp[nb][tau][1], vs[(1 * NG + j) / 2], pexp[nb][tau][3], vs[(3 * NG + j) / 2],
-                       hw[2 * tau + 1], lw[2 * tau + 1]);
-        } else {
-          mix_hi_lo<0>(pexp[nb][tau][0], vs[(0 * NG + j) / 2], pexp[nb][tau][2], vs[(2 * NG + j) / 2],
-                       hw[2 * tau], lw[2 * tau]);
-          mix_hi_lo<0>(pexp[nb][tau][1], vs[(1 * NG + j) / 2], pexp[nb][tau][3], vs[(3 * NG + j) / 2],
-                       hw[2 * tau + 1], lw[2 * tau + 1]);
-        }
-      }
-      // The halves come from inline asm, which the compiler's hazard tracking does not see, so
-      // it may issue an MFMA reading them one instruction after the last write (that read stale
-      // data).  This nop, ordered after every write and before every read of the eight
-      // registers, gives the matrix core the two wait states a VALU result needs before an MFMA
-      // reads it.  (The same values from plain fp16 code, which the compiler tracks, measured
-      // slower: it builds the upper-half products with two more instructions.)
-      asm("s_nop 1" : "+v"(hw[0]), "+v"(hw[1]), "+v"(hw[2]), "+v"(hw[3]), "+v"(lw[0]), "+v"(lw[1]),
-          "+v"(lw[2]), "+v"(lw[3]));
-      const half8 phi = __builtin_bit_cast(half8, u32x4{hw[0], hw[1], hw[2], hw[3]});
-      const half8 plo = __builtin_bit_cast(half8, u32x4{lw[0], lw[1], lw[2], lw[3]});
-      acc[nb][2 * j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vlo, phi, acc[nb][2 * j], 0, 0, 0);
-      acc[nb][2 * j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vlo, plo, acc[nb][2 * j], 0, 0, 0);
-      acc[nb][2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vhi, phi, acc[nb][2 * j + 1], 0, 0, 0);
-      acc[nb][2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vhi, plo, acc[nb][2 * j + 1], 0, 0, 0);
-    }
-  }
-}
-
-// The P V step for two row blocks: the V scale goes on the V side, once for both row blocks.
-// A code times its fp16 scale has at most 18 significant bits (an 8-bit integer code; 14 for
-// 4-bit codes, 15 for E4M3), so v = code * s_v splits exactly into fp16 hi = rne(v) (one packed
+// The second half of the block step: O^T += V^T P^T with the V scale on the V side.  A code
+// times its fp16 scale has at most 18 significant bits (an 8-bit integer code; 14 for 4-bit
+// codes, 15 for E4M3), so v = code * s_v splits exactly into fp16 hi = rne(v) (one packed
 // multiply) and lo = v - hi (one packed fma, exact).  P splits once per row into fp16 hi + lo,
 // and each operand pair takes three products (hi*hi, hi*lo, lo*hi; lo*lo is below 2^-22 of the
-// product).  Against folding the scale into P per 32-dim group, this trades 128 of the block's
-// VALU instructions per row block for a third matrix-core product; with two row blocks that is
-// the cheaper side.  p stays below 2^13 under the offsets (the caller passes e5 = 14).
+// product).  Folding the scale into P instead (hi and lo of p * s_v per 32-dim group and row)
+// needs two matrix-core products per pair but 128 more VALU instructions per row block, and its
+// P halves, written per group right before their products, put a wait in front of every
+// group's matrix-core instructions; on the 184K step this form measured 0.7 us faster in the
+// first milliseconds, and 10% faster on the two-row-block MTP step.  p stays below 2^13 under
+// the offsets (the caller passes e5 = 14: no V-scale exponent enters them).
 template <int D, int NB, int VB, bool F8>
 __device__ __attribute__((always_inline)) inline void block_pv_vhat_regs(TileRaw<D, VB> (&raw)[2],
                                                                          const float (&pexp)[NB][2][4],
@@ -586,15 +521,15 @@ __device__ __attribute__((always_inline)) inline void block_pv_vhat_regs(TileRaw
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
-      mix_hi_lo<0>(pexp[nb][tau][0], kOne, pexp[nb][tau][2], kOne, hw[nb][2 * tau], lw[nb][2 * tau]);
-      mix_hi_lo<0>(pexp[nb][tau][1], kOne, pexp[nb][tau][3], kOne, hw[nb][2 * tau + 1], lw[nb][2 * tau + 1]);
+      mix_hi_lo(pexp[nb][tau][0], kOne, pexp[nb][tau][2], kOne, hw[nb][2 * tau], lw[nb][2 * tau]);
+      mix_hi_lo(pexp[nb][tau][1], kOne, pexp[nb][tau][3], kOne, hw[nb][2 * tau + 1], lw[nb][2 * tau + 1]);
     }
-  static_assert(NB == 2, "the nop below ties the P words of two row blocks");
   // two wait states between the inline-asm writes of P and the matrix-core reads (the
   // compiler's hazard tracking does not see inline-asm results)
-  asm("s_nop 1" : "+v"(hw[0][0]), "+v"(hw[0][1]), "+v"(hw[0][2]), "+v"(hw[0][3]), "+v"(lw[0][0]),
-      "+v"(lw[0][1]), "+v"(lw[0][2]), "+v"(lw[0][3]), "+v"(hw[1][0]), "+v"(hw[1][1]), "+v"(hw[1][2]),
-      "+v"(hw[1][3]), "+v"(lw[1][0]), "+v"(lw[1][1]), "+v"(lw[1][2]), "+v"(lw[1][3]));
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+    asm("s_nop 1" : "+v"(hw[nb][0]), "+v"(hw[nb][1]), "+v"(hw[nb][2]), "+v"(hw[nb][3]), "+v"(lw[nb][0]),
+        "+v"(lw[nb][1]), "+v"(lw[nb][2]), "+v"(lw[nb][3]));
 #pragma unroll
   for (int j = 0; j < NG; ++j) {
     uint32_t l02[2], l13[2], h02[2], h13[2], s02[2], s13[2];
@@ -654,10 +589,7 @@ __device__ __attribute__((always_inline)) inline void process_block(
   float pexp[NB][2][4];
   block_softmax<D, NB, VB, WIN, F8>(raw, blk, masked, e5, qd, qw, cz, first_tok, last_tok, g, acc, base, l_run,
                                     pexp);
-  if constexpr (NB == 2)
-    block_pv_vhat_regs<D, NB, VB, F8>(raw, pexp, acc);
-  else
-    block_pv_folded<D, NB, VB, F8>(raw, pexp, acc);
+  block_pv_vhat_regs<D, NB, VB, F8>(raw, pexp, acc);
 }
 
 // The query rows' B operands of Q K^T, from the raw fp16 words qw (lane: query row 16*nb + m16

@@ -17,8 +17,8 @@
 //   * the 16x16 logit tile comes out with each lane holding one query row and four tokens, the
 //     B-operand layout of the P V product (tokens on K), so P never leaves the registers; V codes
 //     arrive pre-arranged as the A operand of v_mfma_f32_16x16x32_f16 and are widened with
-//     exact bit tricks; the V scale (per token and 32 dims) is folded into P, split into fp16
-//     high and low parts from one single-rounding multiply so the product keeps fp32 accuracy;
+//     exact bit tricks; the V scale (per token and 32 dims) multiplies the codes, and both that
+//     exact product and P split into fp16 high and low parts, so the product keeps fp32 accuracy;
 //   * online softmax in log2 units whose exponent offset only moves in powers of two when a
 //     block needs it, so most blocks rescale nothing;
 //   * the waves merge through LDS into one partial per workgroup (or straight into the output
@@ -324,17 +324,8 @@ __global__ __launch_bounds__(256) void decode_kernel(const int32_t* page_table, 
           clear_unseen_v<D, VB>(raw[1], blk * kBlock + kTile, g, t_lo, Lc);
         }
       }
-      // binary exponent of the block's largest V scale (positive fp16: bit order is value order);
-      // every scale is below 2^(e5 - 14).  Two row blocks scale V on the V side and keep p below
-      // 2^13 instead (block_pv_vhat_regs).
-      float e5 = 14.0f;
-      if constexpr (NB == 1) {
-        const uint32_t* vsw = (const uint32_t*)(src + Stage<D, VB>::kVs) + (lane & (D / 4 - 1));
-        const uint32_t m = wave_max_u16x2(__builtin_bit_cast(uint32_t, __builtin_elementwise_max(
-            __builtin_bit_cast(u16x2, vsw[0]), __builtin_bit_cast(u16x2, vsw[Stage<D, VB>::kTileBytes / 4]))));
-        e5 = (float)((m >> 10) & 31);
-      }
-      process_block<D, NB, VB, WIN, F8>(raw, blk, masked, e5, qd, qw, cz, first_tok, last_tok, g, acc, base,
+      // p stays below 2^13 (the V scale is applied on the V side: no V-scale exponent)
+      process_block<D, NB, VB, WIN, F8>(raw, blk, masked, 14.0f, qd, qw, cz, first_tok, last_tok, g, acc, base,
                                         l_run);
     }
     c0 += CHUNK;

@@ -185,8 +185,8 @@ __device__ __attribute__((always_inline)) inline void block_pv_vhat(const VHat<D
   for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
-      mix_hi_lo<0>(pexp[nb][tau][0] * pf, kOne, pexp[nb][tau][2] * pf, kOne, hw[nb][2 * tau], lw[nb][2 * tau]);
-      mix_hi_lo<0>(pexp[nb][tau][1] * pf, kOne, pexp[nb][tau][3] * pf, kOne, hw[nb][2 * tau + 1],
+      mix_hi_lo(pexp[nb][tau][0] * pf, kOne, pexp[nb][tau][2] * pf, kOne, hw[nb][2 * tau], lw[nb][2 * tau]);
+      mix_hi_lo(pexp[nb][tau][1] * pf, kOne, pexp[nb][tau][3] * pf, kOne, hw[nb][2 * tau + 1],
                    lw[nb][2 * tau + 1]);
     }
     // two wait states between the inline-asm writes of P and the matrix-core reads (the

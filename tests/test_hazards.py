@@ -172,10 +172,12 @@ def test_mfma_operands_have_their_wait_states(listings, src):
 
 
 def test_checker_sees_the_nop_taken_out(tmp_path):
-    """The same check on a copy of the sources with the hand-placed nops of the decode's two P V
-    steps removed (the scale folded into P for one row block, the scale on V for two; compiled
-    only, never run): every decode kernel then has MFMAs that read a P half one wait state after
-    its inline-asm write, which is the stale read the nops prevent."""
+    """The same check on a copy of the sources with the hand-placed nop of the decode's P V step
+    removed (compiled only, never run): the checker then finds MFMAs that read a P half one wait
+    state after its inline-asm v_fma_mix write, the stale read the nop prevents.  (Which kernels
+    depend on the nop is the schedule's business: with these sources 16 of the 18 one-row-block
+    kernels do; in the two-row-block kernels the second row block's P split and the V operands'
+    own work fall between the first P writes and the first product, and the nop is a guard.)"""
     if not os.path.exists(B.HIPCC) and not shutil.which(B.HIPCC):
         pytest.skip("hipcc not available")
     src = tmp_path / "csrc"
@@ -183,7 +185,7 @@ def test_checker_sees_the_nop_taken_out(tmp_path):
     hdr = src / "kvq_attn_block.h"
     text = hdr.read_text()
     text, n = re.subn(r'asm\("s_nop 1"[^;]*;', ";", text)
-    assert n == 2
+    assert n == 1
     hdr.write_text(text)
     flags = [f for f in B.FLAGS if f not in ("-fPIC", "-shared")]
     out = str(tmp_path / "dec.s")
@@ -191,12 +193,8 @@ def test_checker_sees_the_nop_taken_out(tmp_path):
                           "-I", str(src), "-o", out, str(src / "kvq_decode.hip")], capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-2000:]
     ks = kernels(open(out).read())
-    # one row block (template argument NB = 1): P V folds the scale into P, one scale group at a
-    # time, and each group's MFMAs follow its P writes closely; with two row blocks the P halves
-    # are written once per block, and the V operands' own work separates them from the first
-    # MFMA in the current schedule (the nop there is a guard against a later reschedule)
-    one_row_block = {k: v for k, v in ks.items() if re.search(r"decode_kernelILi\d+ELi1E", k)}
-    assert len(one_row_block) == 18
-    flagged = [k for k, v in one_row_block.items() if all_violations(v)]
-    assert len(flagged) == len(one_row_block), \
-        f"{len(one_row_block) - len(flagged)} one-row-block decode kernels show no hazard"
+    found = {k: all_violations(v) for k, v in ks.items() if "decode_kernel" in k}
+    flagged = {k: v for k, v in found.items() if v}
+    assert flagged, "no decode kernel reads a P half too early without the nop"
+    writers = {w.split()[0] for v in flagged.values() for w, _, _ in v}
+    assert writers <= {"v_fma_mixlo_f16", "v_fma_mixhi_f16"}, writers
