@@ -8,8 +8,8 @@
 // replies on 4-bit vs fp16 KV).  The split-KV scheme here is this library's MI355X design:
 //
 //   * one workgroup of 4 waves per piece of a (sequence, KV head) context; each wave streams
-//     32-token blocks through three LDS stage buffers with direct-to-LDS 16-byte loads, so two
-//     blocks are in flight while it computes one;
+//     32-token blocks through LDS stage buffers with direct-to-LDS 16-byte loads (two buffers
+//     at head dim 256, one block in flight while it computes one; three below);
 //   * Q K^T runs on the int8 matrix cores: the K codes of one 16-byte load per lane are the A
 //     operand of v_mfma_i32_16x16x64_i8 as they sit in the page, and each query row is split
 //     exactly into three int8 digits at a per-row power-of-two scale (B operands, query rows of
@@ -20,10 +20,10 @@
 //     exact bit tricks; the V scale (per token and 32 dims) multiplies the codes, and both that
 //     exact product and P split into fp16 high and low parts, so the product keeps fp32 accuracy;
 //   * online softmax in log2 units whose exponent offset only moves in powers of two when a
-//     block needs it, so most blocks rescale nothing;
+//     block needs it, so most blocks rescale nothing and form no cross-lane row maximum;
 //   * the waves merge through LDS into one partial per workgroup (or straight into the output
-//     when a context is one piece); a second, wide launch merges the pieces' partials, one
-//     lane per (sequence, KV head, query row, 4 dims).
+//     when a context is one piece); a second, wide launch merges the pieces' partials, eight
+//     lanes per (sequence, KV head, query row, 4 dims).
 #include "kvq_attn_block.h"
 
 namespace kvq {
