@@ -37,13 +37,13 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_hash() -> str:
-    """Hash of the HIP sources: counters taken on other code are not reported as traffic."""
+def library_hash() -> str:
+    """Hash of the built library the bench loads (the build is deterministic, so an edit that
+    changes no code keeps it): counters taken on other code are not reported as traffic."""
+    from long_context_decode_flash_amd import kvq
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "long_context_decode_flash_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+    with open(kvq.LIB_PATH, "rb") as f:
+        h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -335,7 +335,7 @@ def ingest_pmc(fetch_csv, write_csv, workload, probe_mib, commands):
     WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for a plain device
     copy of probe_mib MiB (the largest copyBuffer dispatches of the run)."""
     probe_kib = probe_mib * 1024.0
-    out = {"workload": workload, "source_hash": source_hash(), "copy_probe_mib": probe_mib,
+    out = {"workload": workload, "library_hash": library_hash(), "copy_probe_mib": probe_mib,
            "commands": commands}
     for key, path in (("fetch", fetch_csv), ("write", write_csv)):
         rows = _counter_rows(path)
@@ -733,7 +733,7 @@ def main(argv=None):
     if os.path.exists(pmc_file):
         with open(pmc_file) as f:
             pmc = json.load(f)
-        if (pmc.get("source_hash") == source_hash() and pmc.get("workload") == name and
+        if (pmc.get("library_hash") == library_hash() and pmc.get("workload") == name and
                 args.kv_format == "k8v4"):
             traffic = pmc.get("hbm_bytes_per_launch")
 
