@@ -352,10 +352,12 @@ __device__ __attribute__((always_inline)) inline void block_scores(TileRaw<D, VB
 #pragma unroll
       for (int pc = 0; pc < 3; ++pc) sd[tau][nb][pc] = i32x4{0, 0, 0, 0};
     }
+  // tile by tile: the first tile's scores are complete after half of the products, so their
+  // conversion and logits can go on beside the second tile's
 #pragma unroll
-  for (int jj = 0; jj < D / 64; ++jj)
+  for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
+    for (int jj = 0; jj < D / 64; ++jj) {
       if constexpr (F8) {
         // dword i of the lane's 16 codes holds dims 4i .. 4i+3: halves 0..7 and 8..15 pair with
         // the query's two fp16 words of the same 16 dims
